@@ -1,0 +1,163 @@
+"""Unpack, pack, block quantisation and dequantisation, by definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Inputs are the tensor specs, the plan (V, S, starts), the number R_mat of
+rank slices actually held in memory (ranks at or past R_mat hold only
+padding and are not materialised), and plain arrays. Each function recomputes
+the tensor intervals, padding and blocks itself from those inputs.
+
+Readings (listed in the design notes):
+  * Unpack ([walk], DBuffer paragraphs: a tensor *is* its planned slice of the
+    buffer): T_i[e] = G[s_i + e], bit for bit.
+  * Pack ([walk], DBuffer paragraph on fused add / scale / zero / copy before
+    a collective): with sigma = fl32(1/V) (or a caller's factor),
+    y = fl32(g * sigma) and out = fl32(prev + y) when accumulating, else y:
+    scale first, then add, two roundings, no fused multiply-add. Every
+    padding position is written as +0.0; padding of prev is never read.
+  * Quantisation blocks ([walk], "every quantization block should ideally
+    live entirely on one device"; the 8-bit Adam paragraph's 32x32 blocks at
+    32-row granularity): TILE tensors are cut into br x bc tiles of the
+    row-major tensor (partial at the right and bottom edges); FLAT tensors
+    into their b-element blocks. Other kinds are not quantised.
+  * Per block: amax = max |x| (exact). If amax > 0 the stored scale is
+    fl32(amax / Q) and values are multiplied by r = min(fl32(Q / amax),
+    FLT_MAX) before encoding (one correctly rounded division per block; the
+    clamp keeps r finite when amax is tiny). If amax == 0 the scale is 1.0 and
+    every code is 0. Q = 448 (E4M3), 127 (int8), 255 (uint8).
+  * Code bytes outside every quantisation block (padding, unquantised
+    tensors) are 0x00. Dequantised values there are +0.0.
+  * Scales are ordered by tensor (spec order), then tile row-major / flat
+    block index.
+"""
+from __future__ import annotations
+
+from typing import Iterator, List, Sequence, Tuple
+
+import numpy as np
+
+from . import codes
+from .plan import numel, padding_ranges
+
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+def f32(x) -> np.ndarray:
+    """Round float64 values to float32 (nearest, ties to even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def inv_v(V: int) -> np.float32:
+    """sigma = fl32(1/V), correctly rounded."""
+    return np.float32(np.float64(1.0) / np.float64(V))
+
+
+# ---------------------------------------------------------------- unpack
+
+def unpack(G: np.ndarray, specs, starts) -> List[np.ndarray]:
+    """Full tensors from the gathered flat buffer: T_i[e] = G[s_i + e] (any dtype, bitwise)."""
+    out = []
+    for spec, s in zip(specs, starts):
+        n = numel(spec)
+        out.append(np.array(G[int(s): int(s) + n]).reshape(spec.rows, spec.cols))
+    return out
+
+
+# ---------------------------------------------------------------- pack
+
+def pack_values(g: np.ndarray, prev, sigma, accumulate: bool) -> np.ndarray:
+    """fl32(g * sigma), then fl32(prev + that) when accumulating."""
+    y = f32(np.asarray(g, dtype=np.float32).astype(np.float64) * np.float64(np.float32(sigma)))
+    if accumulate:
+        y = f32(np.asarray(prev, dtype=np.float32).astype(np.float64) + y.astype(np.float64))
+    return y
+
+
+def pack(grads: Sequence[np.ndarray], prev, specs, starts, S: int, R_mat: int,
+         sigma, accumulate: bool) -> np.ndarray:
+    """Packed flat fp32 buffer of R_mat*S values; padding is +0.0."""
+    out = np.zeros(R_mat * S, dtype=np.float32)
+    for g, spec, s in zip(grads, specs, starts):
+        s, n = int(s), numel(spec)
+        p = prev[s: s + n] if accumulate else None
+        out[s: s + n] = pack_values(np.ravel(g), p, sigma, accumulate)
+    return out
+
+
+# ---------------------------------------------------------------- quant blocks
+
+def quant_blocks(specs, starts) -> Iterator[Tuple[int, int, np.ndarray]]:
+    """(tensor index, scale index, flat positions) of every quantisation block, in scale order."""
+    q = 0
+    for i, (spec, s) in enumerate(zip(specs, starts)):
+        s = int(s)
+        if spec.kind == "TILE":
+            br, bc = int(spec.p0), int(spec.p1)
+            r, c = int(spec.rows), int(spec.cols)
+            for r0 in range(0, r, br):
+                rows = np.arange(r0, min(r0 + br, r), dtype=np.int64)
+                for c0 in range(0, c, bc):
+                    cols = np.arange(c0, min(c0 + bc, c), dtype=np.int64)
+                    yield i, q, s + (rows[:, None] * c + cols[None, :]).ravel()
+                    q += 1
+        elif spec.kind == "FLAT":
+            b, n = int(spec.p0), numel(spec)
+            for e0 in range(0, n, b):
+                yield i, q, s + np.arange(e0, min(e0 + b, n), dtype=np.int64)
+                q += 1
+
+
+def count_quant_blocks(specs) -> int:
+    total = 0
+    for spec in specs:
+        if spec.kind == "TILE":
+            total += (-(-int(spec.rows) // int(spec.p0))) * (-(-int(spec.cols) // int(spec.p1)))
+        elif spec.kind == "FLAT":
+            total += -(-numel(spec) // int(spec.p0))
+    return total
+
+
+def quantize_block(x, fmt: str) -> Tuple[np.ndarray, np.float32]:
+    """Codes and scale of one block of fp32 values."""
+    x = np.asarray(x, dtype=np.float32)
+    Q = codes.FORMAT_QMAX[fmt]
+    amax = float(np.max(np.abs(x.astype(np.float64)))) if x.size else 0.0
+    if amax == 0.0:
+        return np.zeros(x.shape, dtype=np.uint8), np.float32(1.0)
+    scale = np.float32(amax / Q)
+    with np.errstate(over="ignore"):          # Q / amax may overflow fp32: clamp below
+        r = min(float(np.float32(Q / amax)), FLT_MAX)
+    y = f32(x.astype(np.float64) * r)
+    return codes.encode(y, fmt), scale
+
+
+def block_quant(src: np.ndarray, specs, starts, S: int, R_mat: int, fmt: str):
+    """Codes (R_mat*S bytes) and scales of every quantisation block of the flat buffer.
+
+    ``src`` holds fp32 values of the flat buffer (bf16 inputs widened exactly).
+    """
+    q = np.zeros(R_mat * S, dtype=np.uint8)
+    scales = np.zeros(count_quant_blocks(specs), dtype=np.float32)
+    for _, b, pos in quant_blocks(specs, starts):
+        c, sc = quantize_block(src[pos], fmt)
+        q[pos] = c
+        scales[b] = sc
+    return q, scales
+
+
+def dequant_values(c, scale, fmt: str) -> np.ndarray:
+    """fl32(decode(code) * scale)."""
+    return f32(codes.decode(c, fmt) * np.float64(np.float32(scale)))
+
+
+def block_dequant(q: np.ndarray, scales, specs, starts, S: int, R_mat: int, fmt: str) -> np.ndarray:
+    out = np.zeros(R_mat * S, dtype=np.float32)
+    for _, b, pos in quant_blocks(specs, starts):
+        out[pos] = dequant_values(q[pos], scales[b], fmt)
+    return out
+
+
+__all__ = [
+    "f32", "inv_v", "unpack", "pack_values", "pack", "quant_blocks", "count_quant_blocks",
+    "quantize_block", "block_quant", "dequant_values", "block_dequant", "padding_ranges",
+]

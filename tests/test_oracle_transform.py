@@ -1,0 +1,210 @@
+"""Pins of the oracle's unpack / pack / quant / dequant.
+
+  * fp32 arithmetic against exact rationals rounded by IEEE's definition
+    (tests/exact.py), for the 1/V factor, scale-then-add, the per-block scale
+    and reciprocal, the scaled values and their codes.
+  * closed forms: V a power of two makes g/V exact; the element attaining
+    amax maps to +-Q; an all-zero block has scale 1 and zero codes.
+  * invariants: padding comes out +0.0 without reading prev's padding;
+    unpack(pack(x, 1, no accumulate)) == x bit for bit; every quantisation
+    block position is covered exactly once and never crosses a rank; the
+    dequantised values stay within the rounding bound of the code grid.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import codes, plan as P, transform as T
+from tests import exact
+from workloads import TensorSpec, workload
+import workloads as W
+
+
+def _bits(x):
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 6, 7, 64, 100, 1024, 4097])
+def test_inv_v_is_correctly_rounded(V):
+    assert T.inv_v(V) == np.float32(exact.round_f32(Fraction(1, V)))
+
+
+@pytest.mark.parametrize("V,acc", [(3, True), (7, False), (64, True), (5, True), (1024, True)])
+def test_pack_values_exact(V, acc):
+    rng = np.random.default_rng(V)
+    g = (rng.standard_normal(400) * 10.0 ** rng.integers(-6, 3, 400)).astype(np.float32)
+    prev = (rng.standard_normal(400) * 10.0 ** rng.integers(-6, 3, 400)).astype(np.float32)
+    g[:4] = np.float32([0.0, -0.0, 1e-41, -3e-39])     # signed zero and subnormals
+    sigma = T.inv_v(V)
+    got = T.pack_values(g, prev, sigma, acc)
+    for k in range(g.size):
+        y = exact.round_f32(Fraction(float(g[k])) * Fraction(float(sigma)),
+                            negative_zero=bool(np.signbit(g[k])))
+        if acc:
+            y = exact.round_f32(Fraction(float(prev[k])) + Fraction(y),
+                                negative_zero=bool(np.signbit(prev[k]) and np.signbit(y)))
+        assert _bits(got[k]) == exact.f32_bits(y), (k, g[k], prev[k])
+
+
+def test_pack_power_of_two_V_is_exact_scaling():
+    rng = np.random.default_rng(1)
+    g = rng.standard_normal(1000).astype(np.float32)
+    y = T.pack_values(g, None, T.inv_v(64), False)
+    e_g = (_bits(g) >> 23) & 0xFF
+    assert np.array_equal((_bits(y) >> 23) & 0xFF, e_g - 6)          # exponent drops by 6
+    assert np.array_equal(_bits(y) & 0x807FFFFF, _bits(g) & 0x807FFFFF)  # sign, mantissa kept
+
+
+def _tiny_plan():
+    w = workload(0)
+    p = P.plan(w.specs, w.V)
+    return w, p
+
+
+def test_pack_zeroes_padding_and_ignores_prev_padding():
+    w, p = _tiny_plan()
+    S, R = p.S, w.V
+    grads = [W.tensor_values(w, i, W.Role.GRAD) for i in range(3)]
+    prev = np.concatenate([W.prev_slice(w, k, S) for k in range(R)])
+    pads = P.padding_ranges(w.specs, p.starts, S, R)
+    assert pads
+    poisoned = prev.copy()
+    for b, e in pads:
+        poisoned[b:e] = np.nan
+    out = T.pack(grads, poisoned, w.specs, p.starts, S, R, T.inv_v(w.V), True)
+    ref = T.pack(grads, prev, w.specs, p.starts, S, R, T.inv_v(w.V), True)
+    assert np.array_equal(_bits(out), _bits(ref))
+    for b, e in pads:
+        assert np.all(_bits(out[b:e]) == 0)
+    covered = sum(e - b for b, e in pads) + sum(s.numel for s in w.specs)
+    assert covered == R * S
+
+
+def test_unpack_of_pack_is_identity():
+    w, p = _tiny_plan()
+    x = [W.tensor_values(w, i, W.Role.WEIGHT) for i in range(3)]
+    flat = T.pack(x, None, w.specs, p.starts, p.S, w.V, np.float32(1.0), False)
+    back = T.unpack(flat, w.specs, p.starts)
+    for a, b in zip(x, back):
+        assert np.array_equal(_bits(a), _bits(b))
+        assert b.shape == a.shape
+
+
+def _exact_quant(x, fmt):
+    """Codes and scale of one block by exact arithmetic and exhaustive nearest-code search."""
+    Q = {"e4m3": 448, "i8": 127, "u8": 255}[fmt]
+    amax = max(abs(Fraction(float(v))) for v in x)
+    if amax == 0:
+        return [0] * len(x), 1.0
+    scale = exact.round_f32(amax / Q)
+    r = exact.round_f32(Fraction(Q) / amax)
+    r = min(r, float(np.finfo(np.float32).max))
+    out = []
+    for v in x:
+        y = exact.round_f32(Fraction(float(v)) * Fraction(r), negative_zero=bool(np.signbit(v)))
+        if fmt == "e4m3":
+            out.append(exact.e4m3_nearest(y))
+        elif fmt == "i8":
+            out.append(exact.int_nearest(y, -127, 127) & 0xFF)
+        else:
+            out.append(exact.int_nearest(y, 0, 255))
+    return out, scale
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8", "u8"])
+@pytest.mark.parametrize("seed", range(6))
+def test_quantize_block_exact(fmt, seed):
+    rng = np.random.default_rng(seed)
+    mag = 10.0 ** rng.integers(-30, 4)
+    x = (rng.standard_normal(96) * mag).astype(np.float32)
+    if fmt == "u8":
+        x = np.abs(x)
+    if seed == 0:
+        x[5] = -0.0
+    c, sc = T.quantize_block(x, fmt)
+    want_c, want_s = _exact_quant(x, fmt)
+    assert list(c) == want_c
+    assert _bits(sc) == exact.f32_bits(want_s)
+
+
+@pytest.mark.parametrize("fmt,Q,code", [("e4m3", 448, 0x7E), ("i8", 127, 127), ("u8", 255, 255)])
+def test_amax_element_maps_to_Q(fmt, Q, code):
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        x = np.abs(rng.standard_normal(64).astype(np.float32)) * np.float32(10.0 ** rng.integers(-20, 20))
+        k = int(np.argmax(x))
+        c, _ = T.quantize_block(x, fmt)
+        assert c[k] == code
+        if fmt != "u8":
+            c2, _ = T.quantize_block(-x, fmt)
+            assert c2[k] == ((code | 0x80) if fmt == "e4m3" else (-Q) & 0xFF)
+
+
+def test_zero_block_and_tiny_block():
+    c, s = T.quantize_block(np.zeros(40, np.float32), "e4m3")
+    assert s == np.float32(1.0) and not c.any()
+    # amax so small that Q/amax overflows fp32: r is clamped to FLT_MAX, zeros stay zero
+    x = np.float32([1e-41, 0.0, -5e-42, -0.0])
+    c, s = T.quantize_block(x, "e4m3")
+    want_c, want_s = _exact_quant(x, "e4m3")
+    assert list(c) == want_c and _bits(s) == exact.f32_bits(want_s)
+    assert c[1] == 0x00 and c[3] == 0x80
+
+
+def test_quant_blocks_cover_each_position_once_and_stay_on_one_rank():
+    specs = [TensorSpec("a", 37, 20, "TILE", 8, 6), TensorSpec("b", 3, 5, "ELEM"),
+             TensorSpec("c", 1, 4099, "FLAT", 256)]
+    V = 6
+    p = P.plan(specs, V)
+    seen = np.zeros(V * p.S, dtype=np.int64)
+    nblk = 0
+    for i, b, pos in T.quant_blocks(specs, p.starts):
+        assert b == nblk
+        nblk += 1
+        seen[pos] += 1
+        assert np.unique(pos // p.S).size == 1
+    assert nblk == T.count_quant_blocks(specs) == 5 * 4 + 17
+    s_a, s_c = int(p.starts[0]), int(p.starts[2])
+    assert np.all(seen[s_a: s_a + 740] == 1) and np.all(seen[s_c: s_c + 4099] == 1)
+    assert seen.sum() == 740 + 4099
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8", "u8"])
+def test_dequant_roundtrip_bounds(fmt):
+    rng = np.random.default_rng(9)
+    specs = [TensorSpec("a", 64, 40, "TILE", 16, 8), TensorSpec("b", 1, 5000, "FLAT", 512)]
+    V = 4
+    p = P.plan(specs, V)
+    src = rng.standard_normal(V * p.S).astype(np.float32)
+    if fmt == "u8":
+        src = np.abs(src)
+    q, sc = T.block_quant(src, specs, p.starts, p.S, V, fmt)
+    out = T.block_dequant(q, sc, specs, p.starts, p.S, V, fmt)
+    Q = codes.FORMAT_QMAX[fmt]
+    for _, b, pos in T.quant_blocks(specs, p.starts):
+        x, xr, s = src[pos].astype(np.float64), out[pos].astype(np.float64), float(sc[b])
+        amax = np.max(np.abs(x))
+        if fmt == "e4m3":
+            # relative half-ulp of a 3-bit mantissa, or half the subnormal step, times the scale
+            bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s) * (1 + 1e-6)
+        else:
+            bound = 0.5 * s * (1 + 1e-5) + np.abs(x) * 2.0 ** -20
+        assert np.all(np.abs(x - xr) <= bound)
+        k = int(np.argmax(np.abs(x)))
+        assert abs(abs(xr[k]) - amax) <= amax * 2.0 ** -20
+    for b, e in P.padding_ranges(specs, p.starts, p.S, V):
+        assert not q[b:e].any() and not out[b:e].any()
+
+
+def test_pack_pin_catches_add_before_scale(monkeypatch):
+    """Planted mistake: (prev + g) * sigma instead of prev + g * sigma fails the exact pin."""
+    def wrong(g, prev, sigma, accumulate):
+        s = np.asarray(g, np.float32).astype(np.float64)
+        if accumulate:
+            s = T.f32(s + np.asarray(prev, np.float32).astype(np.float64)).astype(np.float64)
+        return T.f32(s * np.float64(sigma))
+
+    monkeypatch.setattr(T, "pack_values", wrong)
+    with pytest.raises(AssertionError):
+        test_pack_values_exact(3, True)
