@@ -1,0 +1,213 @@
+/*
+ * rs.h — RaggedShard / DBuffer layout transforms on one MI355X (gfx950).
+ *
+ * A group of N tensors shares one flat buffer of V*S elements; logical rank k
+ * owns the slice [k*S, (k+1)*S). Tensor i occupies the contiguous interval
+ * [s_i, s_i + n_i); intervals are disjoint and padding lives only between
+ * them; a rank boundary that falls inside a tensor falls between two of its
+ * atomic blocks ("veScale-FSDP: flexible, structure-aware sharding at
+ * 10K-GPU scale", feynmanwiki walkthrough: the paragraphs on RaggedShard's
+ * forbidden cut and on the planner as a packing problem). The V ranks are
+ * slices of one GPU buffer: nothing here runs a collective.
+ *
+ * Calls (all extern "C", all return rs_status unless noted):
+ *   rs_plan_build       host planner: S and the starts s_i
+ *   rs_plan_load        validate a plan and lower it to device work lists
+ *   rs_plan_info / rs_plan_free
+ *   rs_unpack_gathered  gathered flat buffer -> N full tensors
+ *   rs_pack_scatter     N full gradients -> flat buffer, fused scale/add/zero
+ *   rs_block_quant      per-block absmax 8-bit quantisation of the flat buffer
+ *   rs_block_dequant    the inverse of rs_block_quant
+ *   rs_last_error       text of the calling thread's last error
+ *
+ * Conventions
+ *   - Sizes and offsets are in elements unless a name says bytes; all int64.
+ *   - Device pointers come from the caller (e.g. torch tensors' data_ptr())
+ *     and stay owned by the caller. The library owns rs_plan and the device
+ *     tables it allocates once in rs_plan_load; no transform call allocates.
+ *   - `stream` is a hipStream_t passed as void* (torch's current stream on
+ *     ROCm). Transform calls are asynchronous and ordered on that stream.
+ *   - Every check happens before any launch: on error nothing is enqueued,
+ *     the status is returned and rs_last_error() says why. No C++ exception
+ *     crosses this boundary.
+ *   - A plan caches the per-tensor pointer tables it last saw and uploads a
+ *     new table on `stream` only when they change. A plan is therefore not
+ *     safe to use from two threads, or from two streams with different
+ *     tensor pointers, at the same time.
+ *   - Floating-point inputs must be finite; NaN or Inf inside a quantisation
+ *     block gives unspecified codes (padding is never read, so it may hold
+ *     anything).
+ */
+#ifndef RS_H
+#define RS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rs_status {
+  RS_OK = 0,
+  RS_EINVAL = -1,   /* bad argument: null pointer, n < 1, V < 1, unknown enum ... */
+  RS_EPLAN = -2,    /* the plan breaks a constraint, or no plan exists */
+  RS_EALIGN = -3,   /* a pointer is not 16-byte aligned, or S / a start not a multiple of 16 */
+  RS_EDTYPE = -4,   /* dtype or code format not supported by this call */
+  RS_ENOMEM = -5,   /* host or device allocation failed (rs_plan_load only) */
+  RS_EHIP = -6,     /* a HIP runtime call or a kernel launch failed */
+  RS_ERANGE = -7    /* int64 overflow, or R_mat outside [R_used, V] */
+} rs_status;
+
+typedef enum rs_dtype {
+  RS_F32 = 0,
+  RS_BF16 = 1,
+  RS_E4M3 = 2,      /* OCP FP8 E4M3 (largest finite 448, no infinities) */
+  RS_I8 = 3,        /* signed, symmetric [-127, 127] */
+  RS_U8 = 4         /* unsigned [0, 255] */
+} rs_dtype;
+
+/* Atomic block of a tensor: the unit a rank boundary may never cut
+ * (feynmanwiki walkthrough, RaggedShard paragraphs: one element, rows, or a
+ * larger custom block). The flat block size g follows from the kind:
+ *   RS_ELEM        one element                        g = 1
+ *   RS_ROWS(k)     k whole rows                       g = k * cols
+ *   RS_TILE(br,bc) br x bc tiles of the row-major tensor; a rank boundary may
+ *                  only fall between br-row bands (the walkthrough's 8-bit
+ *                  Adam: 32x32 blocks at 32-row granularity)   g = br * cols
+ *   RS_FLAT(b)     b consecutive elements             g = b
+ *   RS_WHOLE       the whole tensor (one matrix per rank, as Muon wants)
+ *                                                     g = rows * cols
+ * The last block of a tensor may be partial. TILE and FLAT tensors are the
+ * ones rs_block_quant quantises (tiles / flat blocks); the others are not. */
+typedef enum rs_block_kind {
+  RS_ELEM = 0, RS_ROWS = 1, RS_TILE = 2, RS_FLAT = 3, RS_WHOLE = 4
+} rs_block_kind;
+
+/* One tensor of the group. A 1-D tensor of n elements is rows = n, cols = 1.
+ * p0: ROWS k, TILE br, FLAT b; p1: TILE bc; unused fields must be 0. */
+typedef struct rs_tensor_spec {
+  int64_t rows;
+  int64_t cols;
+  int32_t kind;      /* rs_block_kind */
+  int32_t reserved;  /* must be 0 */
+  int64_t p0;
+  int64_t p1;
+} rs_tensor_spec;
+
+typedef struct rs_plan rs_plan;   /* opaque, owned by the library */
+
+enum { RS_ORDER_BEST = 0, RS_ORDER_DEFAULT = 1 };
+enum { RS_ORDER_KIND_DEFAULT = 0, RS_ORDER_KIND_BLOCK = 1, RS_ORDER_KIND_SHAPE = 2 };
+
+/* Host planner (feynmanwiki walkthrough: "the planner first fixes a tensor
+ * order", "for a candidate per-device size", "the outer search"; bud-325
+ * summary, Method (2)).
+ * For each tensor order tried — the caller's order, block size descending,
+ * shape descending (element count, then rows), all stable — find the
+ * smallest S that is a multiple of `align` and at least
+ *   LB = align_up(max(ceil(sum n_i / V), max_i min(g_i, n_i)), align)
+ * for which placing each tensor at its earliest valid start after the
+ * previous tensor's end fits inside V*S. Keep the order with the smallest S,
+ * then the smallest end max(s_i + n_i), then the one listed first.
+ * policy: RS_ORDER_BEST tries the three orders, RS_ORDER_DEFAULT only the
+ * caller's. align >= 1 (16 for plans that rs_plan_load accepts).
+ * Outputs (caller-owned host arrays): *S_out; starts_out[n] in the caller's
+ * tensor order; order_out[n] the placement order (a permutation of 0..n-1);
+ * *order_kind_out one of RS_ORDER_KIND_*. order_out / order_kind_out may be
+ * NULL. Host only: touches no GPU.
+ * Errors: RS_EINVAL (null, n < 1, V < 1, align < 1, bad spec), RS_ERANGE
+ * (int64 overflow). */
+int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t align,
+                  int32_t policy, int64_t* S_out, int64_t* starts_out,
+                  int64_t* order_out, int32_t* order_kind_out);
+
+/* Validate a plan and build its device work lists on `device` (the pages'
+ * persistent per-tensor address mapping, made once).
+ * R_mat: number of rank slices actually allocated by the caller, with
+ * R_used = ceil(max(s_i + n_i) / S) <= R_mat <= V; ranks at or past R_mat
+ * hold only padding and are never touched.
+ * Checks (RS_EPLAN unless noted): S > 0 and S % 16 == 0 and every
+ * s_i % 16 == 0 (RS_EALIGN); intervals disjoint and inside [0, V*S); no
+ * rank boundary inside a tensor except at a multiple of g_i from s_i;
+ * R_mat in [R_used, V] (RS_ERANGE); V*S fits int64 (RS_ERANGE).
+ * On success *out owns host memory and one device allocation, released by
+ * rs_plan_free. Errors: the above, RS_ENOMEM, RS_EHIP. */
+int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,
+                 const int64_t* starts, int64_t R_mat, int32_t device, rs_plan** out);
+
+/* Plan facts; any output pointer may be NULL. n_qblocks is the number of
+ * quantisation blocks, i.e. the length of rs_block_quant's scale array:
+ * tensors in the caller's order; within a TILE tensor its tiles row-major,
+ * within a FLAT tensor its blocks in order. padding_elems counts the
+ * positions of [0, R_mat*S) that belong to no tensor. */
+int rs_plan_info(const rs_plan* plan, int64_t* R_used, int64_t* n_qblocks,
+                 int64_t* padding_elems);
+
+void rs_plan_free(rs_plan* plan);   /* NULL is a no-op; waits for the device */
+
+/* Unpack after the (simulated) AllGather: T_i[e] = gathered[s_i + e] for
+ * every tensor i and 0 <= e < n_i, bit for bit (feynmanwiki walkthrough,
+ * DBuffer paragraphs: a tensor is its planned slice; this call does the
+ * Copy-Out of FSDP2's Copy-Out / Copy-In paragraph in one launch).
+ * gathered: device, R_mat*S elements of `dt`, 16-byte aligned.
+ * dst: HOST array of n device pointers, each a contiguous row-major tensor of
+ * n_i elements of `dt`, 16-byte aligned. dt: RS_F32, RS_BF16 or any 1-byte
+ * dtype (RS_E4M3 / RS_I8 / RS_U8). Padding of `gathered` is never read.
+ * Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */
+int rs_unpack_gathered(rs_plan* plan, const void* gathered, int32_t dt,
+                       void* const* dst, void* stream);
+
+enum { RS_SCALE_INV_V = 0, RS_SCALE_GIVEN = 1 };
+
+/* Pack before the (simulated) ReduceScatter, with the group-fused pre-
+ * communication ops (feynmanwiki walkthrough, DBuffer paragraph on add,
+ * scale, zero and copy fused at group level):
+ *   sigma = fl32(1/V) for RS_SCALE_INV_V, else `scale`;
+ *   y = fl32(src_i[e] * sigma);
+ *   packed[s_i + e] = prev ? fl32(prev[s_i + e] + y) : y
+ * (scale first, then add: two IEEE round-to-nearest-even operations, never a
+ * fused multiply-add), and packed[p] = +0.0 at every padding position p in
+ * [0, R_mat*S). Padding of `prev` is never read.
+ * src: HOST array of n device pointers to contiguous gradients (src_dt
+ * RS_F32 or RS_BF16, 16-byte aligned). prev: device fp32 R_mat*S or NULL (no
+ * accumulation); it may equal `packed` (in-place accumulation). packed:
+ * device fp32 R_mat*S, 16-byte aligned.
+ * Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */
+int rs_pack_scatter(rs_plan* plan, const void* const* src, int32_t src_dt,
+                    const float* prev, float* packed, int32_t scale_mode, float scale,
+                    void* stream);
+
+/* Block-wise quantisation of every locally whole block (feynmanwiki
+ * walkthrough: a quantisation block should live on one device because its
+ * values share scale metadata; the 8-bit Adam paragraph). For each block B
+ * (a br x bc tile of a TILE tensor, partial at the edges, or a b-element
+ * block of a FLAT tensor):
+ *   amax = max |x| over B;  Q = 448 (RS_E4M3), 127 (RS_I8), 255 (RS_U8);
+ *   amax == 0: scale[B] = 1.0 and every code is 0;
+ *   otherwise scale[B] = fl32(amax / Q), r = min(fl32(Q / amax), FLT_MAX),
+ *   code = enc(fl32(x * r)), enc being round-to-nearest-even with saturation
+ *   (E4M3: to +-448, sign kept, -0 -> 0x80; I8: to [-127,127]; U8: [0,255]).
+ * Every byte of q outside all blocks (padding, untiled tensors) is 0x00.
+ * src: device, R_mat*S elements of src_dt (RS_F32 or RS_BF16), 16-byte
+ * aligned. q: device, R_mat*S bytes, 16-byte aligned. scales: device fp32
+ * [n_qblocks] (rs_plan_info), ordered by tensor, then tile row-major or flat
+ * block index.
+ * Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */
+int rs_block_quant(rs_plan* plan, const void* src, int32_t src_dt, void* q, int32_t q_dt,
+                   float* scales, void* stream);
+
+/* Inverse of rs_block_quant: out[p] = fl32(dec(q[p]) * scale[B]) inside
+ * block B, +0.0 everywhere else in [0, R_mat*S). Arguments as in
+ * rs_block_quant; out: device fp32 R_mat*S, 16-byte aligned. */
+int rs_block_dequant(rs_plan* plan, const void* q, int32_t q_dt, const float* scales,
+                     float* out, void* stream);
+
+/* Message for the calling thread's last failed call ("" if none). The
+ * pointer stays valid until the thread's next rs_* call. */
+const char* rs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RS_H */

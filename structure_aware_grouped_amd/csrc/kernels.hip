@@ -1,0 +1,685 @@
+// HIP kernels for gfx950 (CDNA4) and the transform entry points of the
+// RaggedShard / DBuffer layout library.
+//
+// Every kernel is HBM-bound streaming work over plan-indexed work lists made
+// once by rs_plan_load: 16-byte vector loads and stores, one 256-thread
+// workgroup per work item, several independent vectors in flight per thread.
+// Quantisation keeps a whole tile (or, one wave per block, a whole flat
+// block) in registers, so each input byte is read from HBM once; the block
+// absmax is a wave shuffle reduction plus, for tiles, a 4-entry LDS combine.
+// No MFMA: nothing here is a dense contraction.
+//
+// Arithmetic follows "veScale-FSDP: flexible, structure-aware sharding at
+// 10K-GPU scale" (feynmanwiki walkthrough, DBuffer paragraph on fused add /
+// scale / zero / copy; the block-wise quantisation and 8-bit Adam
+// paragraphs) with IEEE fp32 round-to-nearest-even operations written out
+// (__fmul_rn, __fadd_rn, __fdiv_rn) and no contraction into FMA.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "rs_internal.h"
+
+namespace rs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum Fmt { FMT_E4M3 = 0, FMT_I8 = 1, FMT_U8 = 2 };
+
+template <int FMT>
+struct QMax;
+template <> struct QMax<FMT_E4M3> { static constexpr float v = 448.0f; };
+template <> struct QMax<FMT_I8> { static constexpr float v = 127.0f; };
+template <> struct QMax<FMT_U8> { static constexpr float v = 255.0f; };
+
+// ------------------------------------------------------------------ codes
+
+// OCP E4M3, saturating, round to nearest even, sign kept. In the normal range
+// the fp32 significand is rounded to 3 bits by adding 0x7ffff plus the kept
+// lsb at bit 20, and the exponent rebiased from 127 to 7 (120 << 3 in code
+// units); below 2^-6 the code is the number of 2^-9 steps, rounded to even.
+__device__ __forceinline__ uint32_t e4m3_sw(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t a = u & 0x7fffffffu;
+  const uint32_t normal = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+  uint32_t c = a < 0x3c800000u ? sub : normal;
+  c = c < 0x7eu ? c : 0x7eu;
+  return c | ((u >> 24) & 0x80u);
+}
+
+__device__ __forceinline__ uint32_t i8_code(float y) {
+  float r = __builtin_rintf(y);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t u8_code(float y) {
+  float r = __builtin_rintf(y);
+  r = fminf(fmaxf(r, 0.0f), 255.0f);
+  return static_cast<uint32_t>(r);
+}
+
+// Four values -> four code bytes in one word (value k in byte k).
+template <int FMT, bool HW>
+__device__ __forceinline__ uint32_t encode4(float y0, float y1, float y2, float y3) {
+  if constexpr (FMT == FMT_E4M3 && HW) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+    return static_cast<uint32_t>(w);
+  } else if constexpr (FMT == FMT_E4M3) {
+    return e4m3_sw(y0) | (e4m3_sw(y1) << 8) | (e4m3_sw(y2) << 16) | (e4m3_sw(y3) << 24);
+  } else if constexpr (FMT == FMT_I8) {
+    return i8_code(y0) | (i8_code(y1) << 8) | (i8_code(y2) << 16) | (i8_code(y3) << 24);
+  } else {
+    return u8_code(y0) | (u8_code(y1) << 8) | (u8_code(y2) << 16) | (u8_code(y3) << 24);
+  }
+}
+
+template <int FMT, bool HW>
+__device__ __forceinline__ uint32_t encode1(float y) {
+  return encode4<FMT, HW>(y, 0.0f, 0.0f, 0.0f) & 0xffu;
+}
+
+__device__ __forceinline__ float e4m3_value_sw(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                : static_cast<float>(m) * 0.001953125f;  // m * 2^-9
+  if ((c & 0x7fu) == 0x7fu) mag = __uint_as_float(0x7fc00000u);
+  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+}
+
+template <int FMT>
+__device__ __forceinline__ float decode_sw(uint32_t c) {
+  if constexpr (FMT == FMT_E4M3) {
+    return e4m3_value_sw(c);
+  } else if constexpr (FMT == FMT_I8) {
+    return static_cast<float>(static_cast<int8_t>(c));
+  } else {
+    return static_cast<float>(c);
+  }
+}
+
+// Four code bytes of a word -> their exact values.
+template <int FMT, bool HW>
+__device__ __forceinline__ f32x4 decode4(uint32_t word) {
+  if constexpr (FMT == FMT_E4M3 && HW) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(word), true);
+    return f32x4{lo.x, lo.y, hi.x, hi.y};
+  } else {
+    return f32x4{decode_sw<FMT>(word & 0xffu), decode_sw<FMT>((word >> 8) & 0xffu),
+                 decode_sw<FMT>((word >> 16) & 0xffu), decode_sw<FMT>(word >> 24)};
+  }
+}
+
+template <int FMT, bool HW>
+__device__ __forceinline__ float decode1(uint32_t c) {
+  return decode4<FMT, HW>(c & 0xffu).x;
+}
+
+// ------------------------------------------------------------------ input types
+
+// fp32 or bf16 input: elements per 16-byte vector, widening, |x| bits.
+template <bool BF16>
+struct In;
+
+template <>
+struct In<false> {
+  static constexpr int VE = 4;
+  static constexpr int EB = 4;
+  __device__ static float elem(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  __device__ static uint32_t absmax(const u32x4& r) {
+    const uint32_t a = max(r.x & 0x7fffffffu, r.y & 0x7fffffffu);
+    const uint32_t b = max(r.z & 0x7fffffffu, r.w & 0x7fffffffu);
+    return max(a, b);
+  }
+  __device__ static void widen(const u32x4& r, float (&x)[4]) {
+    x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
+    x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
+  }
+};
+
+template <>
+struct In<true> {
+  static constexpr int VE = 8;
+  static constexpr int EB = 2;
+  __device__ static float elem(const void* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+  // max |x| as fp32 bits: low halves compared before the shift, high halves in place
+  __device__ static uint32_t absmax(const u32x4& r) {
+    const uint32_t lo = max(max(r.x & 0x7fffu, r.y & 0x7fffu), max(r.z & 0x7fffu, r.w & 0x7fffu));
+    const uint32_t hi = max(max(r.x & 0x7fff0000u, r.y & 0x7fff0000u),
+                            max(r.z & 0x7fff0000u, r.w & 0x7fff0000u));
+    return max(lo << 16, hi);
+  }
+  __device__ static void widen(const u32x4& r, float (&x)[8]) {
+    x[0] = __uint_as_float(r.x << 16); x[1] = __uint_as_float(r.x & 0xffff0000u);
+    x[2] = __uint_as_float(r.y << 16); x[3] = __uint_as_float(r.y & 0xffff0000u);
+    x[4] = __uint_as_float(r.z << 16); x[5] = __uint_as_float(r.z & 0xffff0000u);
+    x[6] = __uint_as_float(r.w << 16); x[7] = __uint_as_float(r.w & 0xffff0000u);
+  }
+};
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, kWave)));
+  return v;
+}
+
+// Max over a group of NT threads (a wave, or a 256-thread workgroup via LDS).
+template <int NT>
+__device__ __forceinline__ uint32_t group_max(uint32_t v, int tid, uint32_t* red) {
+  v = wave_max(v);
+  if constexpr (NT > kWave) {
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w) v = max(v, red[w]);
+  }
+  return v;
+}
+
+// Walks vector indices tid, tid + NT, ... of a rows x vpr grid without a
+// division per step: (row, col) advance by (NT / vpr, NT % vpr) with a carry.
+struct GridWalk {
+  int row, col, drow, dcol, vpr;
+  __device__ GridWalk(int tid, int vpr_, int nt) : vpr(vpr_) {
+    row = tid / vpr; col = tid - row * vpr;
+    drow = nt / vpr; dcol = nt - drow * vpr;
+  }
+  __device__ void next() {
+    row += drow; col += dcol;
+    if (col >= vpr) { col -= vpr; row += 1; }
+  }
+};
+
+// ------------------------------------------------------------------ quant
+
+// One quantisation block: element (r, c) at base + r*stride + c, r < rows,
+// c < cols, handled by NT threads (tid in [0, NT)). Fast path: every vector
+// of the block stays in registers (at most NT*MAXV 16-byte vectors, rows and
+// base aligned to a vector). Otherwise: two passes over memory, element by
+// element.
+template <bool BF16, int FMT, bool HW, int NT, int MAXV>
+__device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ q,
+                            float* __restrict__ scales, int64_t base, int64_t stride, int rows,
+                            int cols, int64_t sidx, int tid, uint32_t* red) {
+  using I = In<BF16>;
+  constexpr int VE = I::VE;
+  constexpr float Q = QMax<FMT>::v;
+  const int vpr = cols / VE;
+  const int nvec = rows * vpr;
+  const bool fast = (base % VE == 0) && (stride % VE == 0) && (cols % VE == 0) && nvec <= NT * MAXV;
+  const char* sb = static_cast<const char*>(src);
+
+  if (fast) {
+    u32x4 raw[MAXV];
+    uint32_t m = 0;
+    {
+      GridWalk w(tid, vpr, NT);
+#pragma unroll
+      for (int k = 0; k < MAXV; ++k) {
+        if (tid + k * NT < nvec) {
+          const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * VE;
+          raw[k] = *reinterpret_cast<const u32x4*>(sb + e * I::EB);
+          m = max(m, I::absmax(raw[k]));
+        }
+        w.next();
+      }
+    }
+    const float amax = __uint_as_float(group_max<NT>(m, tid, red));
+    const bool zero = amax == 0.0f;
+    const float r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
+    if (tid == 0) scales[sidx] = zero ? 1.0f : __fdiv_rn(amax, Q);
+    GridWalk w(tid, vpr, NT);
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      if (tid + k * NT < nvec) {
+        const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * VE;
+        float x[VE];
+        I::widen(raw[k], x);
+        uint32_t words[VE / 4];
+#pragma unroll
+        for (int h = 0; h < VE / 4; ++h) {
+          words[h] = zero ? 0u
+                          : encode4<FMT, HW>(__fmul_rn(x[4 * h], r), __fmul_rn(x[4 * h + 1], r),
+                                             __fmul_rn(x[4 * h + 2], r), __fmul_rn(x[4 * h + 3], r));
+        }
+        if constexpr (VE == 8) {
+          *reinterpret_cast<u32x2*>(q + e) = u32x2{words[0], words[1]};
+        } else {
+          *reinterpret_cast<uint32_t*>(q + e) = words[0];
+        }
+      }
+      w.next();
+    }
+    return;
+  }
+
+  // general path: any alignment, any block size
+  const int64_t total = static_cast<int64_t>(rows) * cols;
+  uint32_t m = 0;
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    m = max(m, __float_as_uint(I::elem(src, base + rr * stride + cc)) & 0x7fffffffu);
+  }
+  const float amax = __uint_as_float(group_max<NT>(m, tid, red));
+  const bool zero = amax == 0.0f;
+  const float r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
+  if (tid == 0) scales[sidx] = zero ? 1.0f : __fdiv_rn(amax, Q);
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    const int64_t e = base + rr * stride + cc;
+    q[e] = zero ? 0 : static_cast<uint8_t>(encode1<FMT, HW>(__fmul_rn(I::elem(src, e), r)));
+  }
+}
+
+// Zero [base, base + len) of a byte array (codes) with 16-byte stores in the middle.
+__device__ void zero_bytes(uint8_t* q, int64_t base, int64_t len, int tid) {
+  const int64_t end = base + len;
+  const int64_t a0 = (base + 15) & ~int64_t(15);
+  const int64_t a1 = end & ~int64_t(15);
+  if (a0 >= a1) {
+    for (int64_t i = base + tid; i < end; i += kThreads) q[i] = 0;
+    return;
+  }
+  for (int64_t i = base + tid; i < a0; i += kThreads) q[i] = 0;
+  for (int64_t i = a1 + tid; i < end; i += kThreads) q[i] = 0;
+  u32x4* v = reinterpret_cast<u32x4*>(q + a0);
+  const int64_t nv = (a1 - a0) >> 4;
+  for (int64_t i = tid; i < nv; i += kThreads) v[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Zero [base, base + len) of an fp32 array with 16-byte stores in the middle.
+__device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
+  const int64_t end = base + len;
+  const int64_t a0 = (base + 3) & ~int64_t(3);
+  const int64_t a1 = end & ~int64_t(3);
+  if (a0 >= a1) {
+    for (int64_t i = base + tid; i < end; i += kThreads) o[i] = 0.0f;
+    return;
+  }
+  for (int64_t i = base + tid; i < a0; i += kThreads) o[i] = 0.0f;
+  for (int64_t i = a1 + tid; i < end; i += kThreads) o[i] = 0.0f;
+  f32x4* v = reinterpret_cast<f32x4*>(o + a0);
+  const int64_t nv = (a1 - a0) >> 2;
+  for (int64_t i = tid; i < nv; i += kThreads) v[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+template <bool BF16, int FMT, bool HW>
+__global__ __launch_bounds__(kThreads) void quant_kernel(const QJob* __restrict__ jobs,
+                                                         const void* __restrict__ src,
+                                                         uint8_t* __restrict__ q,
+                                                         float* __restrict__ scales) {
+  __shared__ uint32_t red[kThreads / kWave];
+  const QJob j = jobs[blockIdx.x];
+  const int tid = threadIdx.x;
+  if (j.kind == QJOB_ZERO) {
+    zero_bytes(q, j.base, j.stride, tid);
+  } else if (j.kind == QJOB_TILE) {
+    quant_block<BF16, FMT, HW, kThreads, BF16 ? 8 : 16>(src, q, scales, j.base, j.stride, j.rows,
+                                                         j.cols, j.scale, tid, red);
+  } else {
+    const int wave = tid / kWave;
+    if (wave < j.rows) {
+      const int len = wave == j.rows - 1 ? j.last : j.cols;
+      quant_block<BF16, FMT, HW, kWave, 8>(src, q, scales, j.base + static_cast<int64_t>(wave) * j.cols,
+                                           len, 1, len, j.scale + wave, tid & (kWave - 1), nullptr);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dequant
+
+template <int FMT, bool HW, int NT>
+__device__ void dequant_block(const uint8_t* __restrict__ q, float* __restrict__ out, float s,
+                              int64_t base, int64_t stride, int rows, int cols, int tid) {
+  if ((base % 4 == 0) && (stride % 4 == 0) && (cols % 4 == 0)) {
+    const int vpr = cols / 4;
+    const int nvec = rows * vpr;
+    GridWalk w(tid, vpr, NT);
+    for (int i = tid; i < nvec; i += NT) {
+      const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 4;
+      const f32x4 d = decode4<FMT, HW>(*reinterpret_cast<const uint32_t*>(q + e));
+      *reinterpret_cast<f32x4*>(out + e) =
+          f32x4{__fmul_rn(d.x, s), __fmul_rn(d.y, s), __fmul_rn(d.z, s), __fmul_rn(d.w, s)};
+      w.next();
+    }
+    return;
+  }
+  const int64_t total = static_cast<int64_t>(rows) * cols;
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    const int64_t e = base + rr * stride + cc;
+    out[e] = __fmul_rn(decode1<FMT, HW>(q[e]), s);
+  }
+}
+
+template <int FMT, bool HW>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const QJob* __restrict__ jobs,
+                                                           const uint8_t* __restrict__ q,
+                                                           const float* __restrict__ scales,
+                                                           float* __restrict__ out) {
+  const QJob j = jobs[blockIdx.x];
+  const int tid = threadIdx.x;
+  if (j.kind == QJOB_ZERO) {
+    zero_f32(out, j.base, j.stride, tid);
+  } else if (j.kind == QJOB_TILE) {
+    dequant_block<FMT, HW, kThreads>(q, out, scales[j.scale], j.base, j.stride, j.rows, j.cols, tid);
+  } else {
+    const int wave = tid / kWave;
+    if (wave < j.rows) {
+      const int len = wave == j.rows - 1 ? j.last : j.cols;
+      dequant_block<FMT, HW, kWave>(q, out, scales[j.scale + wave],
+                                    j.base + static_cast<int64_t>(wave) * j.cols, len, 1, len,
+                                    tid & (kWave - 1));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ unpack
+
+template <int U>
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const CopyChunk* __restrict__ chunks,
+                                                          const uint8_t* __restrict__ gathered,
+                                                          void* const* __restrict__ dst, int eb) {
+  const CopyChunk c = chunks[blockIdx.x];
+  const uint8_t* s = gathered + c.src * eb;
+  uint8_t* d = static_cast<uint8_t*>(dst[c.tensor]) + c.off * eb;
+  const int nbytes = c.len * eb;
+  const int nvec = nbytes >> 4;
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(s);
+  u32x4* d4 = reinterpret_cast<u32x4*>(d);
+  for (int b = threadIdx.x; b < nvec; b += kThreads * U) {
+    u32x4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (b + u * kThreads < nvec) r[u] = s4[b + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (b + u * kThreads < nvec) d4[b + u * kThreads] = r[u];
+  }
+  const int tail = nbytes & 15;
+  if (static_cast<int>(threadIdx.x) < tail) d[(nvec << 4) + threadIdx.x] = s[(nvec << 4) + threadIdx.x];
+}
+
+// ------------------------------------------------------------------ pack
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 load4(const void* p, int64_t e) {
+  if constexpr (BF16) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + e);
+    return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + e);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* p, int64_t e) {
+  if constexpr (BF16)
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[e]) << 16);
+  else
+    return static_cast<const float*>(p)[e];
+}
+
+// packed = acc ? prev + src*sigma : src*sigma on tensor data, +0.0 on padding.
+// `prev` may alias `out`: every element is read before it is written, by the
+// same thread.
+template <bool BF16, bool ACC, int U>
+__global__ __launch_bounds__(kThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
+                                                        const void* const* __restrict__ src,
+                                                        const float* prev, float* out, float sigma) {
+  const PackChunk c = chunks[blockIdx.x];
+  f32x4* o4 = reinterpret_cast<f32x4*>(out + c.out);
+  const int nv = c.n_total >> 2;
+  if (c.tensor < 0) {
+    for (int i = threadIdx.x; i < nv; i += kThreads) o4[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    return;
+  }
+  const void* g = src[c.tensor];
+  const int nd = c.n_data;
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(prev + c.out);
+  for (int b = threadIdx.x; b < nv; b += kThreads * U) {
+    f32x4 gv[U], pv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = b + u * kThreads;
+      if (i < nv && 4 * i + 4 <= nd) {
+        gv[u] = load4<BF16>(g, c.off + 4 * i);
+        if constexpr (ACC) pv[u] = p4[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = b + u * kThreads;
+      if (i >= nv) continue;
+      f32x4 y;
+      if (4 * i + 4 <= nd) {
+        y.x = __fmul_rn(gv[u].x, sigma);
+        y.y = __fmul_rn(gv[u].y, sigma);
+        y.z = __fmul_rn(gv[u].z, sigma);
+        y.w = __fmul_rn(gv[u].w, sigma);
+        if constexpr (ACC) {
+          y.x = __fadd_rn(pv[u].x, y.x);
+          y.y = __fadd_rn(pv[u].y, y.y);
+          y.z = __fadd_rn(pv[u].z, y.z);
+          y.w = __fadd_rn(pv[u].w, y.w);
+        }
+      } else {
+        float t[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = 4 * i + k;
+          if (e < nd) {
+            float v = __fmul_rn(load1<BF16>(g, c.off + e), sigma);
+            if constexpr (ACC) v = __fadd_rn(prev[c.out + e], v);
+            t[k] = v;
+          } else {
+            t[k] = 0.0f;
+          }
+        }
+        y = f32x4{t[0], t[1], t[2], t[3]};
+      }
+      o4[i] = y;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_call(const rs_plan* p, const char* who) {
+  if (!p) return fail(RS_EINVAL, std::string(who) + ": null plan");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(RS_EHIP, std::string(who) + ": hipGetDevice failed");
+  if (cur != p->device)
+    return fail(RS_EINVAL, std::string(who) + ": current device " + std::to_string(cur) +
+                               " differs from the plan's device " + std::to_string(p->device));
+  return RS_OK;
+}
+
+int launched(const char* who) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RS_EHIP, std::string(who) + ": launch failed: " + hipGetErrorString(e));
+  return RS_OK;
+}
+
+// Upload a per-tensor pointer table on `stream` if it differs from the last one.
+int sync_table(rs_plan* p, PtrTable* tab, const void* const* ptrs, hipStream_t stream, const char* who) {
+  const size_t bytes = sizeof(void*) * static_cast<size_t>(p->n);
+  if (tab->valid && std::memcmp(tab->seen.data(), ptrs, bytes) == 0) return RS_OK;
+  if (tab->pending && hipEventSynchronize(tab->done) != hipSuccess)
+    return fail(RS_EHIP, std::string(who) + ": waiting for the previous table upload failed");
+  std::memcpy(tab->stage, ptrs, bytes);
+  if (hipMemcpyAsync(tab->dev, tab->stage, bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipEventRecord(tab->done, stream) != hipSuccess) {
+    tab->valid = false;
+    return fail(RS_EHIP, std::string(who) + ": pointer table upload failed");
+  }
+  tab->pending = true;
+  std::memcpy(tab->seen.data(), ptrs, bytes);
+  tab->valid = true;
+  return RS_OK;
+}
+
+int elem_bytes(int32_t dt) {
+  switch (dt) {
+    case RS_F32: return 4;
+    case RS_BF16: return 2;
+    case RS_E4M3: case RS_I8: case RS_U8: return 1;
+    default: return 0;
+  }
+}
+
+}  // namespace
+}  // namespace rs
+
+using namespace rs;
+
+extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, void* const* dst,
+                                  void* stream) {
+  const char* who = "rs_unpack_gathered";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  const int eb = elem_bytes(dt);
+  if (eb == 0) return fail(RS_EDTYPE, std::string(who) + ": unknown dtype");
+  if (!gathered || !dst) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (!aligned16(gathered)) return fail(RS_EALIGN, std::string(who) + ": gathered buffer not 16-byte aligned");
+  for (int64_t i = 0; i < p->n; ++i) {
+    if (!dst[i]) return fail(RS_EINVAL, std::string(who) + ": null destination " + std::to_string(i));
+    if (!aligned16(dst[i])) return fail(RS_EALIGN, std::string(who) + ": destination " + std::to_string(i) + " not 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sync_table(p, &p->dst, dst, s, who);
+  if (st != RS_OK) return st;
+  hipLaunchKernelGGL(unpack_kernel<4>, dim3(static_cast<unsigned>(p->n_unpack)), dim3(kThreads), 0, s,
+                     p->unpack, static_cast<const uint8_t*>(gathered), p->dst.dev, eb);
+  return launched(who);
+}
+
+extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_dt, const float* prev,
+                               float* packed, int32_t scale_mode, float scale, void* stream) {
+  const char* who = "rs_pack_scatter";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  if (src_dt != RS_F32 && src_dt != RS_BF16) return fail(RS_EDTYPE, std::string(who) + ": src must be fp32 or bf16");
+  if (!src || !packed) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (!aligned16(packed) || (prev && !aligned16(prev)))
+    return fail(RS_EALIGN, std::string(who) + ": packed / prev not 16-byte aligned");
+  for (int64_t i = 0; i < p->n; ++i) {
+    if (!src[i]) return fail(RS_EINVAL, std::string(who) + ": null source " + std::to_string(i));
+    if (!aligned16(src[i])) return fail(RS_EALIGN, std::string(who) + ": source " + std::to_string(i) + " not 16-byte aligned");
+  }
+  float sigma;
+  if (scale_mode == RS_SCALE_INV_V)
+    sigma = 1.0f / static_cast<float>(p->V);   // IEEE fp32 division on the host: fl32(1/V) for V < 2^24
+  else if (scale_mode == RS_SCALE_GIVEN)
+    sigma = scale;
+  else
+    return fail(RS_EINVAL, std::string(who) + ": unknown scale mode");
+  if (scale_mode == RS_SCALE_INV_V && p->V >= (int64_t(1) << 24))
+    return fail(RS_ERANGE, std::string(who) + ": V too large for an exact fp32 1/V");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sync_table(p, &p->src, src, s, who);
+  if (st != RS_OK) return st;
+  const dim3 grid(static_cast<unsigned>(p->n_pack)), block(kThreads);
+  void** tab = p->src.dev;
+  if (src_dt == RS_F32) {
+    if (prev) hipLaunchKernelGGL((pack_kernel<false, true, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    else hipLaunchKernelGGL((pack_kernel<false, false, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+  } else {
+    if (prev) hipLaunchKernelGGL((pack_kernel<true, true, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    else hipLaunchKernelGGL((pack_kernel<true, false, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+  }
+  return launched(who);
+}
+
+namespace {
+
+template <bool BF16>
+void launch_quant(const rs_plan* p, const void* src, int fmt, bool hw, uint8_t* q, float* scales,
+                  hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p->n_qjobs)), block(kThreads);
+  if (fmt == FMT_E4M3 && hw)
+    hipLaunchKernelGGL((quant_kernel<BF16, FMT_E4M3, true>), grid, block, 0, s, p->qjobs, src, q, scales);
+  else if (fmt == FMT_E4M3)
+    hipLaunchKernelGGL((quant_kernel<BF16, FMT_E4M3, false>), grid, block, 0, s, p->qjobs, src, q, scales);
+  else if (fmt == FMT_I8)
+    hipLaunchKernelGGL((quant_kernel<BF16, FMT_I8, false>), grid, block, 0, s, p->qjobs, src, q, scales);
+  else
+    hipLaunchKernelGGL((quant_kernel<BF16, FMT_U8, false>), grid, block, 0, s, p->qjobs, src, q, scales);
+}
+
+int fmt_of(int32_t q_dt) {
+  switch (q_dt) {
+    case RS_E4M3: return FMT_E4M3;
+    case RS_I8: return FMT_I8;
+    case RS_U8: return FMT_U8;
+    default: return -1;
+  }
+}
+
+}  // namespace
+
+extern "C" int rs_block_quant(rs_plan* p, const void* src, int32_t src_dt, void* q, int32_t q_dt,
+                              float* scales, void* stream) {
+  const char* who = "rs_block_quant";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  if (src_dt != RS_F32 && src_dt != RS_BF16) return fail(RS_EDTYPE, std::string(who) + ": src must be fp32 or bf16");
+  const int fmt = fmt_of(q_dt);
+  if (fmt < 0) return fail(RS_EDTYPE, std::string(who) + ": code format must be E4M3, I8 or U8");
+  if (!src || !q || (!scales && p->n_qblocks > 0)) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (!aligned16(src) || !aligned16(q)) return fail(RS_EALIGN, std::string(who) + ": src / q not 16-byte aligned");
+  if (p->n_qjobs == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (src_dt == RS_BF16)
+    launch_quant<true>(p, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
+  else
+    launch_quant<false>(p, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
+  return launched(who);
+}
+
+extern "C" int rs_block_dequant(rs_plan* p, const void* q, int32_t q_dt, const float* scales,
+                                float* out, void* stream) {
+  const char* who = "rs_block_dequant";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  const int fmt = fmt_of(q_dt);
+  if (fmt < 0) return fail(RS_EDTYPE, std::string(who) + ": code format must be E4M3, I8 or U8");
+  if (!q || !out || (!scales && p->n_qblocks > 0)) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (!aligned16(q) || !aligned16(out)) return fail(RS_EALIGN, std::string(who) + ": q / out not 16-byte aligned");
+  if (p->n_qjobs == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(p->n_qjobs)), block(kThreads);
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  if (fmt == FMT_E4M3 && p->e4m3_hw)
+    hipLaunchKernelGGL((dequant_kernel<FMT_E4M3, true>), grid, block, 0, s, p->qjobs, qb, scales, out);
+  else if (fmt == FMT_E4M3)
+    hipLaunchKernelGGL((dequant_kernel<FMT_E4M3, false>), grid, block, 0, s, p->qjobs, qb, scales, out);
+  else if (fmt == FMT_I8)
+    hipLaunchKernelGGL((dequant_kernel<FMT_I8, false>), grid, block, 0, s, p->qjobs, qb, scales, out);
+  else
+    hipLaunchKernelGGL((dequant_kernel<FMT_U8, false>), grid, block, 0, s, p->qjobs, qb, scales, out);
+  return launched(who);
+}

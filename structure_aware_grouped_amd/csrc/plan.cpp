@@ -1,0 +1,314 @@
+// Plan validation and lowering: a plan (specs, V, S, starts, R_mat) becomes
+// device work lists for unpack, pack and block quant / dequant, built once
+// and kept for the plan's lifetime (the DBuffer's persistent per-tensor
+// address mapping: "veScale-FSDP: flexible, structure-aware sharding at
+// 10K-GPU scale", feynmanwiki walkthrough, DBuffer paragraphs).
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "rs_internal.h"
+
+namespace rs {
+
+namespace {
+thread_local std::string g_error;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Checks a plan against the constraints; fills the tensor table.
+int validate(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S, const int64_t* starts,
+             int64_t R_mat, std::vector<Tensor>* out, int64_t* R_used) {
+  if (!specs || !starts) return fail(RS_EINVAL, "rs_plan_load: null specs or starts");
+  if (n < 1 || n > (int64_t(1) << 31)) return fail(RS_EINVAL, "rs_plan_load: bad tensor count");
+  if (V < 1) return fail(RS_EINVAL, "rs_plan_load: V must be >= 1");
+  if (S <= 0) return fail(RS_EINVAL, "rs_plan_load: S must be > 0");
+  if (S % 16 != 0) return fail(RS_EALIGN, "rs_plan_load: S must be a multiple of 16");
+  const int64_t kLimit = int64_t(1) << 62;
+  if (V > kLimit / S) return fail(RS_ERANGE, "rs_plan_load: V * S overflows");
+  const int64_t total = V * S;
+
+  out->resize(n);
+  std::vector<std::pair<int64_t, int64_t>> iv(n);
+  int64_t max_end = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    std::string why;
+    if (!spec_ok(specs[i], &why))
+      return fail(RS_EINVAL, "rs_plan_load: tensor " + std::to_string(i) + ": " + why);
+    Tensor& t = (*out)[i];
+    t.rows = specs[i].rows;
+    t.cols = specs[i].cols;
+    t.n = t.rows * t.cols;
+    t.g = granularity(specs[i]);
+    t.kind = specs[i].kind;
+    t.p0 = specs[i].p0;
+    t.p1 = specs[i].p1;
+    t.start = starts[i];
+    const std::string tag = "rs_plan_load: tensor " + std::to_string(i);
+    if (t.start % 16 != 0) return fail(RS_EALIGN, tag + ": start not a multiple of 16");
+    if (t.start < 0 || t.start > total - t.n)
+      return fail(RS_EPLAN, tag + ": interval outside [0, V*S)");
+    // rank boundaries strictly inside the tensor: the first one at b, then every S
+    const int64_t b = (t.start / S + 1) * S;
+    if (b < t.start + t.n) {
+      if ((b - t.start) % t.g != 0) return fail(RS_EPLAN, tag + ": a rank boundary cuts an atomic block");
+      if (b + S < t.start + t.n && S % t.g != 0)
+        return fail(RS_EPLAN, tag + ": a rank boundary cuts an atomic block");
+    }
+    iv[i] = {t.start, t.start + t.n};
+    max_end = std::max(max_end, t.start + t.n);
+  }
+  std::sort(iv.begin(), iv.end());
+  for (int64_t i = 1; i < n; ++i)
+    if (iv[i].first < iv[i - 1].second) return fail(RS_EPLAN, "rs_plan_load: tensors overlap");
+  *R_used = (max_end + S - 1) / S;
+  if (R_mat < *R_used || R_mat > V)
+    return fail(RS_ERANGE, "rs_plan_load: R_mat must lie in [R_used, V] (R_used = " +
+                               std::to_string(*R_used) + ")");
+  return RS_OK;
+}
+
+struct Tables {
+  std::vector<CopyChunk> unpack;
+  std::vector<PackChunk> pack;
+  std::vector<QJob> qjobs;
+  int64_t n_qblocks = 0;
+  int64_t padding = 0;
+  int32_t max_tile_vec16 = 0;
+};
+
+void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
+  const int64_t top = R_mat * S;
+  const int64_t n = static_cast<int64_t>(t.size());
+
+  // unpack: every tensor in chunks
+  for (int64_t i = 0; i < n; ++i)
+    for (int64_t off = 0; off < t[i].n; off += kUnpackChunk)
+      tb->unpack.push_back({t[i].start + off, off,
+                            static_cast<int32_t>(std::min(kUnpackChunk, t[i].n - off)),
+                            static_cast<int32_t>(i)});
+
+  // pack: walk the buffer in address order; data chunks own the padding up
+  // to the next 16-element boundary after their tensor ends
+  std::vector<int64_t> by_start(n);
+  for (int64_t i = 0; i < n; ++i) by_start[i] = i;
+  std::sort(by_start.begin(), by_start.end(), [&](int64_t a, int64_t b) { return t[a].start < t[b].start; });
+  auto pad = [&](int64_t from, int64_t to) {
+    for (int64_t p = from; p < to; p += kPackChunk)
+      tb->pack.push_back({p, 0, static_cast<int32_t>(std::min(kPackChunk, to - p)), 0, -1, 0});
+  };
+  int64_t pos = 0;
+  for (int64_t k : by_start) {
+    const Tensor& x = t[k];
+    pad(pos, x.start);
+    const int64_t end16 = align_up(x.start + x.n, 16);
+    for (int64_t off = 0; off < x.n; off += kPackChunk) {
+      const int64_t n_data = std::min(kPackChunk, x.n - off);
+      const int64_t n_total = (off + kPackChunk >= x.n) ? end16 - (x.start + off) : n_data;
+      tb->pack.push_back({x.start + off, off, static_cast<int32_t>(n_total),
+                          static_cast<int32_t>(n_data), static_cast<int32_t>(k), 0});
+    }
+    pos = end16;
+  }
+  pad(pos, top);
+
+  int64_t covered = 0;
+  for (const Tensor& x : t) covered += x.n;
+  tb->padding = top - covered;
+
+  // quant / dequant: tiles and flat blocks in scale order, then zero ranges
+  int64_t q = 0;
+  for (const Tensor& x : t) {
+    if (x.kind == RS_TILE) {
+      for (int64_t r0 = 0; r0 < x.rows; r0 += x.p0) {
+        for (int64_t c0 = 0; c0 < x.cols; c0 += x.p1) {
+          QJob j{};
+          j.base = x.start + r0 * x.cols + c0;
+          j.stride = x.cols;
+          j.scale = q++;
+          j.rows = static_cast<int32_t>(std::min(x.p0, x.rows - r0));
+          j.cols = static_cast<int32_t>(std::min(x.p1, x.cols - c0));
+          j.kind = QJOB_TILE;
+          j.last = 0;
+          tb->qjobs.push_back(j);
+          const int64_t v16 = int64_t(j.rows) * ((int64_t(j.cols) * 4 + 15) / 16);
+          tb->max_tile_vec16 = static_cast<int32_t>(std::max<int64_t>(tb->max_tile_vec16, std::min<int64_t>(v16, 1 << 30)));
+        }
+      }
+    } else if (x.kind == RS_FLAT) {
+      const int64_t nblk = (x.n + x.p0 - 1) / x.p0;
+      for (int64_t b0 = 0; b0 < nblk; b0 += kFlatPerGroup) {
+        const int64_t cnt = std::min<int64_t>(kFlatPerGroup, nblk - b0);
+        QJob j{};
+        j.base = x.start + b0 * x.p0;
+        j.stride = x.p0;
+        j.scale = q;
+        j.rows = static_cast<int32_t>(cnt);
+        j.cols = static_cast<int32_t>(x.p0);
+        j.kind = QJOB_FLAT;
+        j.last = static_cast<int32_t>(std::min(x.p0, x.n - (b0 + cnt - 1) * x.p0));
+        tb->qjobs.push_back(j);
+        q += cnt;
+      }
+    }
+  }
+  tb->n_qblocks = q;
+  std::vector<std::pair<int64_t, int64_t>> qiv;
+  for (const Tensor& x : t)
+    if (x.kind == RS_TILE || x.kind == RS_FLAT) qiv.push_back({x.start, x.start + x.n});
+  std::sort(qiv.begin(), qiv.end());
+  auto zero = [&](int64_t from, int64_t to) {
+    for (int64_t p = from; p < to; p += kZeroChunk) {
+      QJob j{};
+      j.base = p;
+      j.stride = std::min(kZeroChunk, to - p);
+      j.kind = QJOB_ZERO;
+      tb->qjobs.push_back(j);
+    }
+  };
+  pos = 0;
+  for (auto& r : qiv) {
+    zero(pos, r.first);
+    pos = r.second;
+  }
+  zero(pos, top);
+}
+
+template <typename T>
+T* carve(char*& p, int64_t count) {
+  T* out = reinterpret_cast<T*>(p);
+  p += align_up(static_cast<int64_t>(sizeof(T)) * std::max<int64_t>(count, 1), 256);
+  return out;
+}
+
+}  // namespace
+
+int fail(int status, const std::string& msg) {
+  g_error = msg;
+  return status;
+}
+
+void clear_error() { g_error.clear(); }
+
+}  // namespace rs
+
+using namespace rs;
+
+static void release(rs_plan* p) {
+  if (!p) return;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(p->device);
+  (void)hipDeviceSynchronize();
+  for (PtrTable* tab : {&p->dst, &p->src}) {
+    if (tab->done) (void)hipEventDestroy(tab->done);
+    if (tab->stage) (void)hipHostFree(tab->stage);
+  }
+  if (p->dmem) (void)hipFree(p->dmem);
+  (void)hipSetDevice(prev);
+  delete p;
+}
+
+static int init_table(PtrTable* tab, void** dev, int64_t n) {
+  tab->dev = dev;
+  tab->seen.assign(n, nullptr);
+  if (hipHostMalloc(reinterpret_cast<void**>(&tab->stage), sizeof(void*) * n, hipHostMallocDefault) != hipSuccess)
+    return fail(RS_ENOMEM, "rs_plan_load: pinned staging allocation failed");
+  if (hipEventCreateWithFlags(&tab->done, hipEventDisableTiming) != hipSuccess)
+    return fail(RS_EHIP, "rs_plan_load: hipEventCreate failed");
+  return RS_OK;
+}
+
+extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,
+                            const int64_t* starts, int64_t R_mat, int32_t device, rs_plan** out) {
+  try {
+    clear_error();
+    if (!out) return fail(RS_EINVAL, "rs_plan_load: null output");
+    *out = nullptr;
+    if (device < 0) return fail(RS_EINVAL, "rs_plan_load: bad device");
+    std::vector<Tensor> t;
+    int64_t R_used = 0;
+    int st = validate(specs, n, V, S, starts, R_mat, &t, &R_used);
+    if (st != RS_OK) return st;
+
+    Tables tb;
+    lower(t, S, R_mat, &tb);
+
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return fail(RS_EHIP, "rs_plan_load: no HIP device");
+    if (hipSetDevice(device) != hipSuccess) return fail(RS_EHIP, "rs_plan_load: hipSetDevice failed");
+
+    rs_plan* p = new rs_plan();
+    p->device = device;
+    p->V = V;
+    p->S = S;
+    p->R_mat = R_mat;
+    p->R_used = R_used;
+    p->n = n;
+    p->padding = tb.padding;
+    p->t = t;
+    p->n_unpack = static_cast<int64_t>(tb.unpack.size());
+    p->n_pack = static_cast<int64_t>(tb.pack.size());
+    p->n_qjobs = static_cast<int64_t>(tb.qjobs.size());
+    p->n_qblocks = tb.n_qblocks;
+    p->max_tile_vec16 = tb.max_tile_vec16;
+    const char* enc = std::getenv("RS_E4M3_ENCODER");
+    p->e4m3_hw = enc && std::strcmp(enc, "hw") == 0;
+
+    const int64_t bytes = align_up(sizeof(CopyChunk) * std::max<int64_t>(p->n_unpack, 1), 256) +
+                          align_up(sizeof(PackChunk) * std::max<int64_t>(p->n_pack, 1), 256) +
+                          align_up(sizeof(QJob) * std::max<int64_t>(p->n_qjobs, 1), 256) +
+                          2 * align_up(sizeof(void*) * n, 256);
+    if (hipMalloc(&p->dmem, bytes) != hipSuccess) {
+      p->dmem = nullptr;
+      release(p);
+      (void)hipSetDevice(prev);
+      return fail(RS_ENOMEM, "rs_plan_load: device allocation of the work lists failed");
+    }
+    char* cur = static_cast<char*>(p->dmem);
+    p->unpack = carve<CopyChunk>(cur, p->n_unpack);
+    p->pack = carve<PackChunk>(cur, p->n_pack);
+    p->qjobs = carve<QJob>(cur, p->n_qjobs);
+    void** dst_dev = carve<void*>(cur, n);
+    void** src_dev = carve<void*>(cur, n);
+
+    bool ok = hipMemcpy(p->unpack, tb.unpack.data(), sizeof(CopyChunk) * p->n_unpack, hipMemcpyHostToDevice) == hipSuccess &&
+              hipMemcpy(p->pack, tb.pack.data(), sizeof(PackChunk) * p->n_pack, hipMemcpyHostToDevice) == hipSuccess &&
+              (p->n_qjobs == 0 || hipMemcpy(p->qjobs, tb.qjobs.data(), sizeof(QJob) * p->n_qjobs, hipMemcpyHostToDevice) == hipSuccess);
+    if (!ok) {
+      release(p);
+      (void)hipSetDevice(prev);
+      return fail(RS_EHIP, "rs_plan_load: upload of the work lists failed");
+    }
+    st = init_table(&p->dst, dst_dev, n);
+    if (st == RS_OK) st = init_table(&p->src, src_dev, n);
+    if (st != RS_OK) {
+      std::string msg = rs_last_error();
+      release(p);
+      (void)hipSetDevice(prev);
+      return fail(st, msg);
+    }
+    (void)hipSetDevice(prev);
+    *out = p;
+    return RS_OK;
+  } catch (const std::exception& ex) {
+    return fail(RS_ENOMEM, std::string("rs_plan_load: ") + ex.what());
+  }
+}
+
+extern "C" int rs_plan_info(const rs_plan* p, int64_t* R_used, int64_t* n_qblocks, int64_t* padding) {
+  clear_error();
+  if (!p) return fail(RS_EINVAL, "rs_plan_info: null plan");
+  if (R_used) *R_used = p->R_used;
+  if (n_qblocks) *n_qblocks = p->n_qblocks;
+  if (padding) *padding = p->padding;
+  return RS_OK;
+}
+
+extern "C" void rs_plan_free(rs_plan* p) { release(p); }
+
+extern "C" const char* rs_last_error(void) { return rs::g_error.c_str(); }

@@ -1,0 +1,105 @@
+// Internal types shared by the host planner, the plan lowering and the HIP
+// kernels of the RaggedShard / DBuffer layout library.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "rs.h"
+
+namespace rs {
+
+// Elements per work item (tuned on gfx950; all multiples of 16 so every item
+// starts 16-element aligned when its tensor does).
+constexpr int64_t kUnpackChunk = 16384;   // elements per unpack work item
+constexpr int64_t kPackChunk = 8192;      // output elements per pack work item
+constexpr int64_t kZeroChunk = 65536;     // elements per zero-fill work item
+constexpr int kFlatPerGroup = 4;          // flat quant blocks per 256-thread group (one per wave)
+
+// One tensor of a loaded plan.
+struct Tensor {
+  int64_t rows, cols, n, g, start;
+  int64_t p0, p1;
+  int32_t kind;
+};
+
+// Unpack work item: `len` consecutive elements of one tensor.
+struct CopyChunk {
+  int64_t src;      // element offset in the flat buffer
+  int64_t off;      // element offset inside the tensor
+  int32_t len;      // elements
+  int32_t tensor;
+};
+
+// Pack work item: an aligned run of the flat output. The first n_data
+// elements come from tensor `tensor` (starting at its element `off`); the
+// remaining n_total - n_data elements are padding. tensor < 0: all padding.
+struct PackChunk {
+  int64_t out;      // element offset in the flat buffer (multiple of 16)
+  int64_t off;
+  int32_t n_total;  // multiple of 16
+  int32_t n_data;
+  int32_t tensor;
+  int32_t unused;
+};
+
+enum QJobKind : int32_t { QJOB_TILE = 0, QJOB_FLAT = 1, QJOB_ZERO = 2 };
+
+// Quant / dequant work item.
+//   TILE: one tile: element (r, c) sits at base + r*stride + c, r < rows, c < cols.
+//   FLAT: `rows` (1..kFlatPerGroup) consecutive flat blocks of `cols` elements
+//         from base; the last one has `last` elements. Scales scale..scale+rows-1.
+//   ZERO: elements [base, base + stride) lie in no block (codes 0, values +0.0).
+struct QJob {
+  int64_t base;
+  int64_t stride;
+  int64_t scale;
+  int32_t rows;
+  int32_t cols;
+  int32_t kind;
+  int32_t last;
+};
+
+// Device copy of a per-tensor pointer table plus the host state that decides
+// when it must be uploaded again.
+struct PtrTable {
+  void** dev = nullptr;          // n device-side pointers (inside the plan's allocation)
+  void** stage = nullptr;        // pinned host staging for the upload
+  hipEvent_t done = nullptr;     // recorded after the last upload from `stage`
+  std::vector<const void*> seen; // pointers of the last upload
+  bool valid = false;
+  bool pending = false;
+};
+
+// Granularity and spec checks shared by the planner and the loader.
+int64_t granularity(const rs_tensor_spec& s);
+bool spec_ok(const rs_tensor_spec& s, std::string* why);
+
+// Thread-local error reporting: record a message, return the status.
+int fail(int status, const std::string& msg);
+void clear_error();
+
+}  // namespace rs
+
+struct rs_plan {
+  int device = 0;
+  int64_t V = 0, S = 0, R_mat = 0, R_used = 0, n = 0, padding = 0;
+  std::vector<rs::Tensor> t;
+
+  void* dmem = nullptr;  // one device allocation holding every table below
+  rs::CopyChunk* unpack = nullptr;
+  int64_t n_unpack = 0;
+  rs::PackChunk* pack = nullptr;
+  int64_t n_pack = 0;
+  rs::QJob* qjobs = nullptr;
+  int64_t n_qjobs = 0;
+  int64_t n_qblocks = 0;
+  int32_t max_tile_vec16 = 0;  // largest tile, in 16-byte vectors of 4-byte input
+
+  rs::PtrTable dst;  // unpack destinations
+  rs::PtrTable src;  // pack sources
+  bool e4m3_hw = false;  // use gfx950's FP8 conversion instructions
+};

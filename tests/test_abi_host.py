@@ -1,0 +1,127 @@
+"""The C-ABI library on the host: it loads, exports every declared call, its
+planner reproduces the oracle's plan exactly, and invalid plans or arguments
+are rejected with the documented status before anything touches a GPU."""
+import os
+import random
+import re
+import time
+
+import pytest
+
+from oracle import plan as OP
+from tests.test_oracle_plan import random_instance
+from workloads import TensorSpec, workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def rs():
+    import structure_aware_grouped_amd as pkg
+    from structure_aware_grouped_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("librs_hip.so is not built: run __graft_entry__.build()")
+    binding.load()
+    return pkg
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "rs.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(rs_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_call(rs):
+    from structure_aware_grouped_amd import binding
+    names = _declared()
+    assert set(names) == set(binding.EXPORTS)
+    lib = binding.load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_host_planner_matches_oracle_on_workloads(rs, idx):
+    w = workload(idx)
+    t0 = time.perf_counter()
+    S, starts, order, name = rs.rs_plan_build(list(w.specs), w.V)
+    dt = time.perf_counter() - t0
+    ref = OP.plan(w.specs, w.V)
+    assert S == ref.S
+    assert starts == [int(s) for s in ref.starts]
+    assert order == ref.order and name == ref.order_name
+    assert dt < 0.3   # the pages report planning under 0.3 s
+
+
+@pytest.mark.parametrize("seed", range(150))
+def test_host_planner_matches_oracle_on_random_instances(rs, seed):
+    specs, V, a = random_instance(10_000 + seed)
+    for policy in ("best", "default"):
+        S, starts, order, name = rs.rs_plan_build(specs, V, a, policy)
+        ref = OP.plan(specs, V, a, policy)
+        assert (S, starts, order, name) == (ref.S, [int(s) for s in ref.starts], ref.order,
+                                             ref.order_name)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_host_planner_matches_oracle_on_larger_random_groups(rs, seed):
+    rng = random.Random(77 + seed)
+    specs = []
+    for i in range(rng.randint(2, 12)):
+        kind = rng.choice(["ROWS", "TILE", "FLAT", "WHOLE", "ELEM"])
+        r, c = rng.choice([1, 7, 64, 100, 128, 300]), rng.choice([1, 16, 48, 96, 130, 256])
+        p0 = rng.choice([1, 2, 16, 32]) if kind in ("ROWS", "TILE") else (rng.choice([64, 100, 2048]) if kind == "FLAT" else 0)
+        p1 = rng.choice([8, 16, 32]) if kind == "TILE" else 0
+        specs.append(TensorSpec(f"t{i}", r, c, kind, p0, p1))
+    V = rng.choice([2, 3, 8, 16, 64])
+    S, starts, order, name = rs.rs_plan_build(specs, V, 16)
+    ref = OP.plan(specs, V, 16)
+    assert (S, starts, name) == (ref.S, [int(s) for s in ref.starts], ref.order_name)
+    assert OP.check_plan(specs, V, S, starts, 16) == []
+
+
+def _status(fn):
+    from structure_aware_grouped_amd import binding
+    with pytest.raises(binding.RsError) as ei:
+        fn()
+    assert binding.load().rs_last_error().decode()
+    return ei.value.status
+
+
+def test_plan_build_rejects_bad_arguments(rs):
+    from structure_aware_grouped_amd import binding as b
+    good = [TensorSpec("a", 4, 4, "ROWS", 1)]
+    assert _status(lambda: rs.rs_plan_build(good, 0)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build(good, 4, 0)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 0, 4, "ELEM")], 4)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 4, 4, "TILE", 2, 0)], 4)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 4, 4, "ROWS", 0)], 4)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 4, 4, "ELEM", 3)], 4)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 4, 4, 9)], 4)) == b.RS_EINVAL
+
+
+def test_plan_load_rejects_invalid_plans_before_touching_a_gpu(rs):
+    from structure_aware_grouped_amd import binding as b
+    specs = [TensorSpec("a", 4, 16, "ROWS", 1), TensorSpec("b", 2, 32, "TILE", 2, 16)]
+    V, S = 4, 64
+    L = rs.rs_plan_load
+    assert _status(lambda: L(specs, V, 40, [0, 64])) == b.RS_EALIGN          # S % 16
+    assert _status(lambda: L(specs, V, S, [8, 64])) == b.RS_EALIGN           # start % 16
+    assert _status(lambda: L(specs, V, S, [0, 32])) == b.RS_EPLAN            # overlap
+    assert _status(lambda: L(specs, V, S, [0, 96])) == b.RS_EPLAN            # boundary 128 cuts the band
+    assert _status(lambda: L(specs, V, S, [0, 224])) == b.RS_EPLAN           # past V*S
+    assert _status(lambda: L(specs, V, S, [-16, 64])) == b.RS_EPLAN          # negative start
+    assert _status(lambda: L(specs, V, S, [0, 128], R_mat=2)) == b.RS_ERANGE  # R_mat < R_used = 3
+    assert _status(lambda: L(specs, V, S, [0, 128], R_mat=5)) == b.RS_ERANGE  # R_mat > V
+    assert _status(lambda: L(specs, 1 << 40, 1 << 30, [0, 128])) == b.RS_ERANGE  # V*S overflows
+    assert _status(lambda: L([TensorSpec("a", 4, 16, "FLAT", 0)], V, S, [0])) == b.RS_EINVAL
+    assert _status(lambda: L(specs, 0, S, [0, 128])) == b.RS_EINVAL
+    assert _status(lambda: L(specs, V, S, [0, 128], device=-1)) == b.RS_EINVAL
+
+
+def test_valid_plan_without_gpu_reports_a_hip_error(rs):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    from structure_aware_grouped_amd import binding as b
+    specs = [TensorSpec("a", 4, 16, "ROWS", 1), TensorSpec("b", 2, 32, "TILE", 2, 16)]
+    assert _status(lambda: rs.rs_plan_load(specs, 4, 64, [0, 128])) == b.RS_EHIP

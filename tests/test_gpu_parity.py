@@ -1,0 +1,292 @@
+"""HIP path vs the CPU oracle, element by element, on small groups that span
+several tiles, ragged tails and the degenerate cases. Every call goes through
+the C ABI (via the ctypes binding)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codes as OC, plan as OP, transform as OT
+from tests.gpu_util import garbage, guard_intact, guarded, tensor_bits, to_device_bits
+from workloads import TensorSpec, bf16_bits_from_f32, f32_from_bf16_bits, workload
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _plan(rs, specs, V, R_mat=None):
+    S, starts, _, _ = rs.rs_plan_build(specs, V)
+    ref = OP.plan(specs, V)
+    assert S == ref.S and starts == [int(s) for s in ref.starts]
+    return rs.rs_plan_load(specs, V, S, starts, V if R_mat is None else R_mat, 0)
+
+
+def _values(rng, n, dist="normal", scale=1.0):
+    if dist == "normal":
+        return (rng.standard_normal(n) * scale).astype(np.float32)
+    return (rng.random(n) * 2 - 1).astype(np.float32) * np.float32(scale)
+
+
+def _flat_input(rng, plan, pdtype, scale=1.0, positive=False):
+    """Flat buffer with tensor data at the plan's starts and NaN poison elsewhere.
+
+    Returns (device tensor, fp32 host values of the flat buffer, per-tensor host values)."""
+    total = plan.R_mat * plan.S
+    host = np.full(total, np.nan, dtype=np.float32)
+    per = []
+    for spec, s in zip(plan.specs, plan.starts):
+        v = _values(rng, spec.rows * spec.cols, scale=scale)
+        if positive:
+            v = np.abs(v)
+        if pdtype == torch.bfloat16:
+            v = f32_from_bf16_bits(bf16_bits_from_f32(v))
+        host[s: s + v.size] = v
+        per.append(v)
+    if pdtype == torch.bfloat16:
+        bits = bf16_bits_from_f32(host)
+        bits[np.isnan(host)] = 0x7FC1
+        dev = to_device_bits(bits, torch.bfloat16, DEV)
+    else:
+        dev = torch.from_numpy(host).to(DEV)
+    return dev, host, per
+
+
+def _full_check(rs, specs, V, pdtype, seed, fmts=("e4m3", "i8", "u8"), R_mat=None):
+    rng = _rng(seed)
+    plan = _plan(rs, specs, V, R_mat)
+    R, S = plan.R_mat, plan.S
+    total = R * S
+    G, Gh, xs = _flat_input(rng, plan, pdtype)
+
+    # unpack
+    outs = [garbage(sp.rows * sp.cols, pdtype, DEV).view(sp.rows, sp.cols) for sp in specs]
+    rs.rs_unpack_gathered(plan, G, outs)
+    want = OT.unpack(tensor_bits(G), specs, plan.starts)
+    for o, wv in zip(outs, want):
+        assert np.array_equal(tensor_bits(o), wv)
+
+    # pack, with and without accumulation, out of place and in place
+    grads_h = [_values(rng, sp.rows * sp.cols, scale=1e-3).reshape(sp.rows, sp.cols) for sp in specs]
+    gdt = pdtype
+    if gdt == torch.bfloat16:
+        grads_h = [f32_from_bf16_bits(bf16_bits_from_f32(g)).reshape(g.shape) for g in grads_h]
+    grads = [torch.from_numpy(g).to(DEV).to(gdt) for g in grads_h]
+    prev_h = _values(rng, total, scale=1e-3)
+    prev = torch.from_numpy(prev_h).to(DEV)
+    sigma = OT.inv_v(V)
+    whole, packed = guarded(total, torch.float32, DEV)
+    packed.view(torch.uint8).fill_(0xA5)
+    rs.rs_pack_scatter(plan, grads, packed, prev=prev)
+    want = OT.pack(grads_h, prev_h, specs, plan.starts, S, R, sigma, True)
+    assert np.array_equal(tensor_bits(packed), want.view(np.uint32))
+    assert guard_intact(whole, total)
+    rs.rs_pack_scatter(plan, grads, packed)
+    want0 = OT.pack(grads_h, None, specs, plan.starts, S, R, sigma, False)
+    assert np.array_equal(tensor_bits(packed), want0.view(np.uint32))
+    inplace = prev.clone()
+    rs.rs_pack_scatter(plan, grads, inplace, prev=inplace, scale=0.75)
+    want2 = OT.pack(grads_h, prev_h, specs, plan.starts, S, R, np.float32(0.75), True)
+    assert np.array_equal(tensor_bits(inplace), want2.view(np.uint32))
+
+    # quant and dequant of the flat parameter buffer
+    for fmt in fmts:
+        src_dev, src_h = G, Gh
+        if fmt == "u8":   # unsigned codes take non-negative values (Adam's v)
+            src_dev, src_h, _ = _flat_input(rng, plan, pdtype, positive=True)
+        qwhole, q = guarded(total, torch.uint8, DEV)
+        q.fill_(0x5A)
+        swhole, scales = guarded(max(plan.n_qblocks, 1), torch.float32, DEV)
+        rs.rs_block_quant(plan, src_dev, q, fmt, scales)
+        wq, ws = OT.block_quant(src_h, specs, plan.starts, S, R, fmt)
+        assert np.array_equal(tensor_bits(q), wq), fmt
+        assert np.array_equal(tensor_bits(scales)[: plan.n_qblocks], ws.view(np.uint32)), fmt
+        assert guard_intact(qwhole, total) and guard_intact(swhole, max(plan.n_qblocks, 1))
+        owhole, out = guarded(total, torch.float32, DEV)
+        out.view(torch.uint8).fill_(0x77)
+        rs.rs_block_dequant(plan, q, fmt, scales, out)
+        wd = OT.block_dequant(wq, ws, specs, plan.starts, S, R, fmt)
+        assert np.array_equal(tensor_bits(out), wd.view(np.uint32)), fmt
+        assert guard_intact(owhole, total)
+    plan.close()
+
+
+def test_tiny_workload(gpu_lib):
+    import structure_aware_grouped_amd as rs
+    w = workload(0)
+    _full_check(rs, list(w.specs), w.V, torch.float32, 0)
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 7, 8])
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_tiny_shapes_other_rank_counts(gpu_lib, V, pdtype):
+    import structure_aware_grouped_amd as rs
+    _full_check(rs, list(workload(0).specs), V, pdtype, 100 + V)
+
+
+RAGGED = [
+    TensorSpec("tile_partial", 37, 20, "TILE", 8, 6),     # partial tiles, unaligned columns
+    TensorSpec("tile_vec", 130, 64, "TILE", 16, 16),      # vector path, partial last band
+    TensorSpec("flat_tail", 1, 4099, "FLAT", 256),         # partial last flat block
+    TensorSpec("flat_big", 2048, 3, "FLAT", 2048),
+    TensorSpec("elem", 7, 130, "ELEM"),
+    TensorSpec("rows3", 10, 10, "ROWS", 3),
+    TensorSpec("whole", 5, 5, "WHOLE"),
+    TensorSpec("tile_wide", 33, 520, "TILE", 32, 128),    # 128-wide tiles and a 8-wide edge
+    TensorSpec("norm", 4096, 1, "ROWS", 1),
+]
+
+
+@pytest.mark.parametrize("V", [1, 3, 6, 16])
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_ragged_group(gpu_lib, V, pdtype):
+    import structure_aware_grouped_amd as rs
+    _full_check(rs, RAGGED, V, pdtype, 7 * V)
+
+
+def test_trailing_padding_ranks(gpu_lib):
+    """R_mat > R_used: ranks holding only padding come out zero."""
+    import structure_aware_grouped_amd as rs
+    specs = [TensorSpec("a", 64, 64, "TILE", 32, 32), TensorSpec("b", 100, 1, "ELEM")]
+    _full_check(rs, specs, 16, torch.bfloat16, 3)
+
+
+def test_single_element_group(gpu_lib):
+    import structure_aware_grouped_amd as rs
+    _full_check(rs, [TensorSpec("x", 1, 1, "FLAT", 1)], 1, torch.float32, 5)
+    _full_check(rs, [TensorSpec("x", 1, 1, "TILE", 1, 1)], 3, torch.bfloat16, 6)
+
+
+@pytest.mark.parametrize("encoder", ["sw", "hw"])
+def test_e4m3_encoder_sweep(gpu_lib, encoder, monkeypatch):
+    """Every fp32 mantissa at the rounding-critical exponents, and structured low bits at
+    all others, through rs_block_quant with a 448 pivot in each block (so r = 1)."""
+    import structure_aware_grouped_amd as rs
+    monkeypatch.setenv("RS_E4M3_ENCODER", encoder)
+    vals = []
+    full_exps = [-10, -7, -6, -1, 7, 8]
+    for e in full_exps:
+        m = np.arange(1 << 23, dtype=np.uint32)
+        vals.append(((e + 127) << 23) | m)
+    lows = np.array([0, 1, 2, (1 << 19) - 1, 1 << 19, (1 << 19) + 1, (1 << 20) - 1, 0x5A5A5], np.uint32)
+    for e in range(-20, 9):
+        m3 = np.arange(8, dtype=np.uint32)[:, None] << np.uint32(20)
+        vals.append((np.uint32((e + 127) << 23) | (m3 | lows[None, :]).ravel()))
+    u = np.concatenate(vals)
+    x = u.view(np.float32)
+    x = x[np.abs(x) < 448]
+    x = np.concatenate([x, -x, np.float32([0.0, -0.0, 2.0 ** -149, -(2.0 ** -149)])])
+    b = 2047
+    nblk = -(-x.size // b)
+    data = np.zeros(nblk * 2048, dtype=np.float32)
+    body = data.reshape(nblk, 2048)
+    body[:, 0] = 448.0
+    flat = np.zeros(nblk * b, dtype=np.float32)
+    flat[: x.size] = x
+    body[:, 1:] = flat.reshape(nblk, b)
+    spec = [TensorSpec("sweep", nblk, 2048, "FLAT", 2048)]
+    plan = rs.rs_plan_load(spec, 1, nblk * 2048, [0], 1, 0)
+    q = torch.empty(nblk * 2048, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(nblk, dtype=torch.float32, device=DEV)
+    rs.rs_block_quant(plan, torch.from_numpy(data).to(DEV), q, "e4m3", sc)
+    got = tensor_bits(q).reshape(nblk, 2048)
+    assert np.all(tensor_bits(sc) == np.float32(1.0).view(np.uint32))
+    assert np.all(got[:, 0] == 0x7E)
+    want = OC.e4m3_encode(flat)
+    assert np.array_equal(got[:, 1:].ravel(), want)
+    # decode of every code through dequant with unit scales
+    codes_all = np.tile(np.arange(256, dtype=np.uint8), 8)
+    spec2 = [TensorSpec("codes", 1, 2048, "FLAT", 2048)]
+    plan2 = rs.rs_plan_load(spec2, 1, 2048, [0], 1, 0)
+    out = torch.empty(2048, dtype=torch.float32, device=DEV)
+    rs.rs_block_dequant(plan2, torch.from_numpy(codes_all).to(DEV), "e4m3",
+                        torch.ones(1, dtype=torch.float32, device=DEV), out)
+    dec = out.cpu().numpy().astype(np.float64)
+    ref = OC.e4m3_decode(codes_all)
+    assert np.all((dec == ref) & (np.signbit(dec) == np.signbit(ref)) | (np.isnan(dec) & np.isnan(ref)))
+    plan.close()
+    plan2.close()
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8", "u8"])
+def test_special_blocks(gpu_lib, fmt):
+    """All-zero, subnormal-amax, constant, single-outlier and signed-zero blocks."""
+    import structure_aware_grouped_amd as rs
+    b = 256
+    blocks = [
+        np.zeros(b, np.float32),
+        np.full(b, 1e-41, np.float32) * np.sign(np.arange(b) % 3 - 1).astype(np.float32),
+        np.full(b, 3.25, np.float32),
+        np.where(np.arange(b) == 17, 1e4, 1e-3).astype(np.float32),
+        np.where(np.arange(b) % 2 == 0, -0.0, 0.5).astype(np.float32),
+        (np.random.default_rng(1).standard_normal(b) * 1e-30).astype(np.float32),
+        np.float32(np.random.default_rng(2).standard_normal(b) * 1e30),
+    ]
+    data = np.concatenate(blocks)
+    if fmt == "u8":
+        data = np.abs(data)
+    spec = [TensorSpec("s", 1, data.size, "FLAT", b)]
+    plan = rs.rs_plan_load(spec, 1, data.size, [0], 1, 0)
+    q = torch.empty(data.size, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(len(blocks), dtype=torch.float32, device=DEV)
+    rs.rs_block_quant(plan, torch.from_numpy(data).to(DEV), q, fmt, sc)
+    wq, ws = OT.block_quant(data, spec, [0], data.size, 1, fmt)
+    assert np.array_equal(tensor_bits(q), wq)
+    assert np.array_equal(tensor_bits(sc), ws.view(np.uint32))
+    out = torch.empty(data.size, dtype=torch.float32, device=DEV)
+    rs.rs_block_dequant(plan, q, fmt, sc, out)
+    assert np.array_equal(tensor_bits(out), OT.block_dequant(wq, ws, spec, [0], data.size, 1, fmt).view(np.uint32))
+    plan.close()
+
+
+def test_pointer_table_refresh(gpu_lib):
+    """New destination / source tensors on a later call are picked up."""
+    import structure_aware_grouped_amd as rs
+    specs = RAGGED[:4]
+    plan = _plan(rs, specs, 4)
+    rng = _rng(9)
+    G, Gh, xs = _flat_input(rng, plan, torch.float32)
+    for _ in range(3):
+        outs = [torch.zeros(sp.rows, sp.cols, device=DEV) for sp in specs]
+        rs.rs_unpack_gathered(plan, G, outs)
+        for o, x in zip(outs, xs):
+            assert np.array_equal(tensor_bits(o).ravel(), x.view(np.uint32))
+    for k in range(3):
+        grads_h = [_values(rng, sp.rows * sp.cols) for sp in specs]
+        packed = torch.empty(plan.R_mat * plan.S, device=DEV)
+        rs.rs_pack_scatter(plan, [torch.from_numpy(g).to(DEV) for g in grads_h], packed)
+        want = OT.pack(grads_h, None, specs, plan.starts, plan.S, plan.R_mat, OT.inv_v(4), False)
+        assert np.array_equal(tensor_bits(packed), want.view(np.uint32))
+    plan.close()
+
+
+def test_bad_arguments_launch_nothing(gpu_lib):
+    import structure_aware_grouped_amd as rs
+    from structure_aware_grouped_amd import binding as b
+    specs = [TensorSpec("a", 64, 64, "TILE", 16, 16)]
+    plan = _plan(rs, specs, 2)
+    total = plan.R_mat * plan.S
+    G = torch.zeros(total + 4, device=DEV)
+    dst = [torch.full((64, 64), 7.0, device=DEV)]
+    lib = b.load()
+    st = lib.rs_unpack_gathered(plan.handle, G[1:].data_ptr(), b.RS_F32, b._ptrs(dst),
+                                b._stream(0))
+    assert st == b.RS_EALIGN
+    st = lib.rs_unpack_gathered(plan.handle, G.data_ptr(), 9, b._ptrs(dst), b._stream(0))
+    assert st == b.RS_EDTYPE
+    q = torch.full((total,), 3, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(plan.n_qblocks, device=DEV)
+    st = lib.rs_block_quant(plan.handle, G.data_ptr(), b.RS_F32, q.data_ptr(), b.RS_F32,
+                            sc.data_ptr(), b._stream(0))
+    assert st == b.RS_EDTYPE
+    st = lib.rs_pack_scatter(plan.handle, b._ptrs([dst[0]]), b.RS_E4M3, None, G.data_ptr(), 0,
+                             0.0, b._stream(0))
+    assert st == b.RS_EDTYPE
+    torch.cuda.synchronize()
+    assert bool((dst[0] == 7.0).all()) and bool((q == 3).all())
+    plan.close()
