@@ -1,0 +1,318 @@
+"""Throughput of the RaggedShard / DBuffer layout transform on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+
+One step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: for the Llama-3-8B layer at V=64 (the default),
+unpack of the gathered bf16 parameter buffer into the 9 parameter tensors,
+pack of the 9 fp32 gradients into the fp32 rank slices (scale by 1/V,
+accumulate into the previous packed buffer, zero the padding), and E4M3
+quantisation of every 128x128 tile of the bf16 parameter buffer. The Adam
+workload (--workload 4) steps through pack, int8/uint8 quant and dequant of m
+and v.
+
+Throughput counts algorithmic bytes (each byte a kernel must read or write
+once) per second of wall time over the K timed steps. Per-kernel durations
+come from HIP events recorded on the stream the kernels run on. The CPU
+baseline times the CPU oracle on a bounded sample of the same workload.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
+METRIC = "DBuffer pack/unpack+blockquant GB/s, % HBM peak (Llama-3-8B layer, V=64)"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_llama3_8b_v64.md")
+KERNEL_SOURCE = os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--cpu-sample", type=int, default=1, help="0 disables the CPU-oracle baseline")
+    ap.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size of the device-to-device copy timed as the practical ceiling "
+                         "(and used to calibrate HBM byte counters); 0 disables it")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, plan) -> dict:
+    """Bytes each kernel must move once per call (read + write)."""
+    n_all = sum(plan.numels)
+    R, S = plan.R_mat, plan.S
+    pb = 2 if w.param_dtype == "bf16" else 4
+    out = {}
+    if w.adam_states:
+        nq = sum(n for sp, n in zip(w.specs, plan.numels) if sp.kind in ("TILE", "FLAT"))
+        pack = n_all * (4 + 4) + 4 * plan.padding
+        quant = nq * 4 + R * S + 4 * plan.n_qblocks
+        dequant = nq * 1 + 4 * plan.n_qblocks + 4 * R * S
+        for which in ("m", "v"):
+            out[f"pack_{which}"] = pack
+            out[f"quant_{which}"] = quant
+            out[f"dequant_{which}"] = dequant
+        return out
+    out["unpack"] = 2 * n_all * pb
+    out["pack"] = n_all * (4 + (4 if w.accumulate else 0) + 4) + 4 * plan.padding
+    if w.quant:
+        nq = sum(n for sp, n in zip(w.specs, plan.numels) if sp.kind in ("TILE", "FLAT"))
+        out["quant"] = nq * pb + R * S + 4 * plan.n_qblocks
+    return out
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """Measured HBM bytes per launch of `kernel` from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    text = open(PROFILE_TRAFFIC).read()
+    m = re.search(r"kernels\.hip sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    if not m or m.group(1) != kernel_hash():
+        return None
+    m = re.search(rf"\|\s*{kernel}\s*\|[^\n]*?\|\s*([0-9.]+)\s*\|\s*$", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(w, plan) -> dict:
+    """The CPU oracle (single-threaded NumPy) on a bounded sample: the attention
+    block of the layer (wq, wk, wv, wo and both norms), same byte accounting."""
+    from oracle import plan as OP, transform as OT
+    from tests.gpu_util import Inputs
+    import workloads as W
+
+    names = ("wq", "wk", "wv", "wo", "attn_norm", "mlp_norm")
+    idx = [i for i, sp in enumerate(w.specs) if sp.name in names]
+    inp = Inputs(w, plan.S, plan.starts, plan.R_mat, device="cpu")
+    specs = [w.specs[i] for i in idx]
+    weights = [inp.weight_bits(i) for i in idx]
+    grads = [inp.grad(i) for i in idx]
+    starts = [plan.starts[i] for i in idx]
+    prevs = [inp.prev_range(s, s + sp.numel) for s, sp in zip(starts, specs)]
+    pb = 2 if w.param_dtype == "bf16" else 4
+    sigma = OT.inv_v(w.V)
+    t0 = time.perf_counter()
+    moved = 0
+    for spec, s, wb, g, p in zip(specs, starts, weights, grads, prevs):
+        n = spec.numel
+        # unpack: the tensor is its slice of the gathered buffer
+        OT.unpack(wb, [spec], [0])
+        moved += 2 * n * pb
+        # pack: scale, accumulate
+        OT.pack_values(g.ravel(), p, sigma, True)
+        moved += n * 12
+        # quant: every tile of the tensor
+        if spec.kind in ("TILE", "FLAT") and w.quant:
+            x = W.f32_from_bf16_bits(wb) if wb.dtype == np.uint16 else wb.view(np.float32)
+            for _, b, pos in OT.quant_blocks([spec], [0]):
+                OT.quantize_block(x[pos], w.quant)
+            moved += n * pb + n + 4 * OT.count_quant_blocks([spec])
+    dt = time.perf_counter() - t0
+    return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"attention block of the layer ({', '.join(names)}): unpack + pack"
+                      f"{' + e4m3 tile quant' if w.quant else ''}, {moved / 1e9:.3f} GB in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the V logical ranks are slices of one device buffer "
+              f"and no collective is run (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import structure_aware_grouped_amd as rs
+    from tests.gpu_util import Inputs, garbage, tensor_bits
+    from workloads import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = workload(args.workload)
+    specs = list(w.specs)
+
+    t0 = time.perf_counter()
+    S, starts, order, order_name = rs.rs_plan_build(specs, w.V)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    R_used = -(-max(s + sp.numel for s, sp in zip(starts, specs)) // S)
+    R = w.V if w.materialize_all_ranks else R_used
+    plan = rs.rs_plan_load(specs, w.V, S, starts, R, 0)
+    inp = Inputs(w, S, starts, R, device=dev)
+    nbytes = algorithmic_bytes(w, plan)
+    avg_load = -(-sum(plan.numels) // w.V)
+
+    # ---- inputs resident in HBM
+    if w.adam_states:
+        m = inp.adam_states("m")
+        v = inp.adam_states("v")
+        pm = garbage(R * S, torch.float32, dev)
+        pv = garbage(R * S, torch.float32, dev)
+        qm = garbage(R * S, torch.uint8, dev)
+        qv = garbage(R * S, torch.uint8, dev)
+        sm = garbage(plan.n_qblocks, torch.float32, dev)
+        sv = garbage(plan.n_qblocks, torch.float32, dev)
+        dm = garbage(R * S, torch.float32, dev)
+        dv = garbage(R * S, torch.float32, dev)
+        steps = [
+            ("pack_m", lambda: rs.rs_pack_scatter(plan, m, pm, scale=1.0)),
+            ("pack_v", lambda: rs.rs_pack_scatter(plan, v, pv, scale=1.0)),
+            ("quant_m", lambda: rs.rs_block_quant(plan, pm, qm, "i8", sm)),
+            ("quant_v", lambda: rs.rs_block_quant(plan, pv, qv, "u8", sv)),
+            ("dequant_m", lambda: rs.rs_block_dequant(plan, qm, "i8", sm, dm)),
+            ("dequant_v", lambda: rs.rs_block_dequant(plan, qv, "u8", sv, dv)),
+        ]
+        dominant = "pack_m"
+    else:
+        G = inp.gathered()
+        params = inp.empty_params()
+        grads = inp.grads()
+        prev = inp.prev()
+        packed = garbage(R * S, torch.float32, dev)
+        steps = [
+            ("unpack", lambda: rs.rs_unpack_gathered(plan, G, params)),
+            ("pack", lambda: rs.rs_pack_scatter(plan, grads, packed, prev=prev)),
+        ]
+        if w.quant:
+            q = garbage(R * S, torch.uint8, dev)
+            scales = garbage(plan.n_qblocks, torch.float32, dev)
+            steps.append(("quant", lambda: rs.rs_block_quant(plan, G, q, w.quant, scales)))
+        dominant = "pack"
+    torch.cuda.synchronize()
+
+    copy = None
+    if args.copy_mib:
+        # a plain device-to-device copy of known size: the practical HBM ceiling, and the
+        # reference whose counter readings calibrate FETCH_SIZE / WRITE_SIZE
+        nb = args.copy_mib << 20
+        src_c = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst_c = torch.empty_like(src_c)
+        ms = []
+        for _ in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst_c.copy_(src_c)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        best = float(np.median(ms[1:]))
+        copy = {"bytes": 2 * nb, "median_ms": round(best, 4), "GBps": round(2 * nb / (best * 1e-3) / 1e9, 1)}
+        del src_c, dst_c
+
+    for _ in range(args.warmup):
+        for _, fn in steps:
+            fn()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, HIP events around every launch on its stream
+    stream = torch.cuda.current_stream(dev)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in steps] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for (name, fn), (a, b) in zip(steps, ev[k]):
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel = {}
+    for j, (name, _) in enumerate(steps):
+        ms = [ev[k][j][0].elapsed_time(ev[k][j][1]) for k in range(args.steps)]
+        avg = float(np.mean(ms))
+        per_kernel[name] = {"avg_ms": round(avg, 5), "min_ms": round(float(np.min(ms)), 5),
+                            "GBps": round(nbytes[name] / (avg * 1e-3) / 1e9, 1),
+                            "bytes": int(nbytes[name])}
+    step_bytes = sum(nbytes[name] for name, _ in steps)
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    # ---- sampled oracle check of the outputs of the last step
+    check = "skipped"
+    if not args.no_check and not w.adam_states:
+        from oracle import transform as OT
+        i = next(k for k, sp in enumerate(specs) if sp.name == "wk")
+        s, n = starts[i], plan.numels[i]
+        assert np.array_equal(tensor_bits(params[i]).ravel(), inp.weight_bits(i)), "unpack"
+        # pack reads prev (unchanged between steps): every step writes the same values
+        want = OT.pack_values(inp.grad(i).ravel(), inp.prev_range(s, s + n), OT.inv_v(w.V), True)
+        assert np.array_equal(tensor_bits(packed[s: s + n]), want.view(np.uint32)), "pack"
+        if w.quant:
+            from workloads import f32_from_bf16_bits
+            x = f32_from_bf16_bits(inp.weight_bits(i))
+            got = tensor_bits(q[s: s + n])
+            for _, b, pos in list(OT.quant_blocks([specs[i]], [0]))[:64]:
+                c, _sc = OT.quantize_block(x[pos], w.quant)
+                assert np.array_equal(got[pos], c), "quant"
+        check = "ok (wk: unpack, pack, 64 tiles of quant vs the oracle)"
+
+    dom_avg_s = per_kernel[dominant]["avg_ms"] * 1e-3
+    achieved = nbytes[dominant] / dom_avg_s / 1e9
+    traffic = read_traffic(dominant)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant])}
+
+    cpu = None
+    if args.cpu_sample and not w.adam_states:
+        cpu = cpu_baseline(w, plan)
+
+    names = {1: "Llama-3-8B layer (bf16, 128x128 tiles), V=64: unpack + pack(1/V, accumulate) + e4m3 tile quant",
+             2: "Llama-3-70B layer (bf16, whole-matrix blocks), V=1024, 4 ranks materialised: unpack + pack",
+             3: "MoE layer (128 experts, bf16, 128x128 tiles), V=256: unpack + pack + e4m3 tile quant",
+             4: "8-bit Adam states on the Llama-3-8B layer shapes, 2048-element blocks, V=64: "
+                "pack m,v + int8/uint8 quant + dequant"}
+    line = {
+        "metric": METRIC if args.workload == 1 else f"DBuffer layout transform GB/s (workload {args.workload})",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": names[args.workload], "V": w.V, "S": S, "R_mat": R,
+                   "order": order_name, "padding_frac": round(plan.padding / (R * S), 5),
+                   "S_over_avg_load": round(S / max(avg_load, 1), 4), "plan_ms": round(plan_ms, 2),
+                   "bytes_per_step": int(step_bytes), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "storage": "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales"
+                   if args.workload != 4 else "fp32 m/v, int8/uint8 codes + fp32 scales",
+                   "e4m3_encoder": "hw" if os.environ.get("RS_E4M3_ENCODER") == "hw" else "sw"},
+        "kernels": per_kernel,
+        "copy_ceiling": copy,
+        "check": check,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -57,8 +57,10 @@ def test_param_and_grad_workloads(gpu_lib, idx):
     G = inp.gathered()
     params = inp.empty_params()
     rs.rs_unpack_gathered(plan, G, params)
+    print("  params uploaded and unpacked", flush=True)
     grads = inp.grads()
     prev = inp.prev()
+    print("  grads and prev uploaded", flush=True)
     packed = garbage(R * S, torch.float32, DEV)
     rs.rs_pack_scatter(plan, grads, packed, prev=prev)
     q = scales = None
@@ -68,6 +70,7 @@ def test_param_and_grad_workloads(gpu_lib, idx):
         rs.rs_block_quant(plan, G, q, w.quant, scales)
     torch.cuda.synchronize()
 
+    print("  kernels done; checking against the oracle", flush=True)
     sample = _sample(len(specs), 12, idx)
     sigma = OT.inv_v(w.V)
     for i in sample:
@@ -79,6 +82,7 @@ def test_param_and_grad_workloads(gpu_lib, idx):
         assert np.array_equal(tensor_bits(packed[s: s + n]), want.view(np.uint32)), f"pack {i}"
     pads = OP.padding_ranges(specs, plan.starts, S, R)
     _zero_everywhere(packed, pads)
+    print(f"  unpack and pack match on tensors {sample}; padding zero", flush=True)
 
     if w.quant:
         first = [0]
