@@ -36,7 +36,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
 METRIC = "DBuffer pack/unpack+blockquant GB/s, % HBM peak (Llama-3-8B layer, V=64)"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_llama3_8b_v64.md")
-KERNEL_SOURCE = os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", "kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", f)
+                  for f in ("kernels.hip", "rs_internal.h", "plan.cpp")]
 
 
 def parse():
@@ -78,7 +79,11 @@ def algorithmic_bytes(w, plan) -> dict:
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """Hash of the sources that decide what the kernels do and how work is split."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str):
@@ -87,11 +92,11 @@ def read_traffic(kernel: str):
     if not os.path.exists(PROFILE_TRAFFIC):
         return None
     text = open(PROFILE_TRAFFIC).read()
-    m = re.search(r"kernels\.hip sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    m = re.search(r"kernel sources sha256\[:16\]:\s*`?([0-9a-f]{16})", text, re.I)
     if not m or m.group(1) != kernel_hash():
         return None
-    m = re.search(rf"\|\s*{kernel}\s*\|[^\n]*?\|\s*([0-9.]+)\s*\|\s*$", text, re.M)
-    return float(m.group(1)) if m else None
+    m = re.search(rf"^\|\s*{kernel}\s*\|[^\n]*?\|\s*([0-9]+)\s*\|\s*$", text, re.M)
+    return int(m.group(1)) if m else None
 
 
 def cpu_baseline(w, plan) -> dict:
@@ -303,7 +308,7 @@ def main():
                    "bytes_per_step": int(step_bytes), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "storage": "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales"
                    if args.workload != 4 else "fp32 m/v, int8/uint8 codes + fp32 scales",
-                   "e4m3_encoder": "hw" if os.environ.get("RS_E4M3_ENCODER") == "hw" else "sw"},
+                   "e4m3_encoder": "sw" if os.environ.get("RS_E4M3_ENCODER") == "sw" else "hw"},
         "kernels": per_kernel,
         "copy_ceiling": copy,
         "check": check,

@@ -188,6 +188,9 @@ int rs_pack_scatter(rs_plan* plan, const void* const* src, int32_t src_dt,
  *   code = enc(fl32(x * r)), enc being round-to-nearest-even with saturation
  *   (E4M3: to +-448, sign kept, -0 -> 0x80; I8: to [-127,127]; U8: [0,255]).
  * Every byte of q outside all blocks (padding, untiled tensors) is 0x00.
+ * E4M3 codes come from gfx950's FP8 conversion instructions unless the
+ * environment variable RS_E4M3_ENCODER=sw is set when the plan is loaded
+ * (then an integer encoder is used); both give identical codes.
  * src: device, R_mat*S elements of src_dt (RS_F32 or RS_BF16), 16-byte
  * aligned. q: device, R_mat*S bytes, 16-byte aligned. scales: device fp32
  * [n_qblocks] (rs_plan_info), ordered by tensor, then tile row-major or flat

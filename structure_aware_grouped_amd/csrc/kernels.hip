@@ -29,6 +29,31 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWave = 64;
 
+#ifndef RS_NT
+#define RS_NT 1
+#endif
+#ifndef RS_UNPACK_U
+#define RS_UNPACK_U 8
+#endif
+#ifndef RS_PACK_U
+#define RS_PACK_U 8
+#endif
+// Streamed data is touched once: load and store it with the nontemporal hint
+// so it does not displace anything in L2 / MALL.
+constexpr bool kNT = RS_NT != 0;
+
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+  if constexpr (kNT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void stg(T* p, T v) {
+  if constexpr (kNT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -234,7 +259,7 @@ __device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ 
       for (int k = 0; k < MAXV; ++k) {
         if (tid + k * NT < nvec) {
           const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * VE;
-          raw[k] = *reinterpret_cast<const u32x4*>(sb + e * I::EB);
+          raw[k] = ldg(reinterpret_cast<const u32x4*>(sb + e * I::EB));
           m = max(m, I::absmax(raw[k]));
         }
         w.next();
@@ -259,9 +284,9 @@ __device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ 
                                              __fmul_rn(x[4 * h + 2], r), __fmul_rn(x[4 * h + 3], r));
         }
         if constexpr (VE == 8) {
-          *reinterpret_cast<u32x2*>(q + e) = u32x2{words[0], words[1]};
+          stg(reinterpret_cast<u32x2*>(q + e), u32x2{words[0], words[1]});
         } else {
-          *reinterpret_cast<uint32_t*>(q + e) = words[0];
+          stg(reinterpret_cast<uint32_t*>(q + e), words[0]);
         }
       }
       w.next();
@@ -300,7 +325,7 @@ __device__ void zero_bytes(uint8_t* q, int64_t base, int64_t len, int tid) {
   for (int64_t i = a1 + tid; i < end; i += kThreads) q[i] = 0;
   u32x4* v = reinterpret_cast<u32x4*>(q + a0);
   const int64_t nv = (a1 - a0) >> 4;
-  for (int64_t i = tid; i < nv; i += kThreads) v[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int64_t i = tid; i < nv; i += kThreads) stg(v + i, u32x4{0u, 0u, 0u, 0u});
 }
 
 // Zero [base, base + len) of an fp32 array with 16-byte stores in the middle.
@@ -316,7 +341,7 @@ __device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
   for (int64_t i = a1 + tid; i < end; i += kThreads) o[i] = 0.0f;
   f32x4* v = reinterpret_cast<f32x4*>(o + a0);
   const int64_t nv = (a1 - a0) >> 2;
-  for (int64_t i = tid; i < nv; i += kThreads) v[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int64_t i = tid; i < nv; i += kThreads) stg(v + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 }
 
 template <bool BF16, int FMT, bool HW>
@@ -353,9 +378,9 @@ __device__ void dequant_block(const uint8_t* __restrict__ q, float* __restrict__
     GridWalk w(tid, vpr, NT);
     for (int i = tid; i < nvec; i += NT) {
       const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 4;
-      const f32x4 d = decode4<FMT, HW>(*reinterpret_cast<const uint32_t*>(q + e));
-      *reinterpret_cast<f32x4*>(out + e) =
-          f32x4{__fmul_rn(d.x, s), __fmul_rn(d.y, s), __fmul_rn(d.z, s), __fmul_rn(d.w, s)};
+      const f32x4 d = decode4<FMT, HW>(ldg(reinterpret_cast<const uint32_t*>(q + e)));
+      stg(reinterpret_cast<f32x4*>(out + e),
+          f32x4{__fmul_rn(d.x, s), __fmul_rn(d.y, s), __fmul_rn(d.z, s), __fmul_rn(d.w, s)});
       w.next();
     }
     return;
@@ -407,10 +432,10 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const CopyChunk* __res
     u32x4 r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (b + u * kThreads < nvec) r[u] = s4[b + u * kThreads];
+      if (b + u * kThreads < nvec) r[u] = ldg(s4 + b + u * kThreads);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (b + u * kThreads < nvec) d4[b + u * kThreads] = r[u];
+      if (b + u * kThreads < nvec) stg(d4 + b + u * kThreads, r[u]);
   }
   const int tail = nbytes & 15;
   if (static_cast<int>(threadIdx.x) < tail) d[(nvec << 4) + threadIdx.x] = s[(nvec << 4) + threadIdx.x];
@@ -421,11 +446,11 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(const CopyChunk* __res
 template <bool BF16>
 __device__ __forceinline__ f32x4 load4(const void* p, int64_t e) {
   if constexpr (BF16) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + e);
+    const u32x2 w = ldg(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + e));
     return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
   } else {
-    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + e);
+    return ldg(reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + e));
   }
 }
 
@@ -448,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackChunk* __restr
   f32x4* o4 = reinterpret_cast<f32x4*>(out + c.out);
   const int nv = c.n_total >> 2;
   if (c.tensor < 0) {
-    for (int i = threadIdx.x; i < nv; i += kThreads) o4[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = threadIdx.x; i < nv; i += kThreads) stg(o4 + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
     return;
   }
   const void* g = src[c.tensor];
@@ -461,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackChunk* __restr
       const int i = b + u * kThreads;
       if (i < nv && 4 * i + 4 <= nd) {
         gv[u] = load4<BF16>(g, c.off + 4 * i);
-        if constexpr (ACC) pv[u] = p4[i];
+        if constexpr (ACC) pv[u] = ldg(p4 + i);
       }
     }
 #pragma unroll
@@ -495,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackChunk* __restr
         }
         y = f32x4{t[0], t[1], t[2], t[3]};
       }
-      o4[i] = y;
+      stg(o4 + i, y);
     }
   }
 }
@@ -569,7 +594,7 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_table(p, &p->dst, dst, s, who);
   if (st != RS_OK) return st;
-  hipLaunchKernelGGL(unpack_kernel<4>, dim3(static_cast<unsigned>(p->n_unpack)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL(unpack_kernel<RS_UNPACK_U>, dim3(static_cast<unsigned>(p->n_unpack)), dim3(kThreads), 0, s,
                      p->unpack, static_cast<const uint8_t*>(gathered), p->dst.dev, eb);
   return launched(who);
 }
@@ -603,11 +628,11 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
   const dim3 grid(static_cast<unsigned>(p->n_pack)), block(kThreads);
   void** tab = p->src.dev;
   if (src_dt == RS_F32) {
-    if (prev) hipLaunchKernelGGL((pack_kernel<false, true, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
-    else hipLaunchKernelGGL((pack_kernel<false, false, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    if (prev) hipLaunchKernelGGL((pack_kernel<false, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    else hipLaunchKernelGGL((pack_kernel<false, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
   } else {
-    if (prev) hipLaunchKernelGGL((pack_kernel<true, true, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
-    else hipLaunchKernelGGL((pack_kernel<true, false, 4>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    if (prev) hipLaunchKernelGGL((pack_kernel<true, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    else hipLaunchKernelGGL((pack_kernel<true, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
   }
   return launched(who);
 }

@@ -256,8 +256,10 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->n_qjobs = static_cast<int64_t>(tb.qjobs.size());
     p->n_qblocks = tb.n_qblocks;
     p->max_tile_vec16 = tb.max_tile_vec16;
+    // gfx950's FP8 conversion (OCP E4M3, round to nearest even) by default;
+    // RS_E4M3_ENCODER=sw selects the integer encoder, which gives the same codes.
     const char* enc = std::getenv("RS_E4M3_ENCODER");
-    p->e4m3_hw = enc && std::strcmp(enc, "hw") == 0;
+    p->e4m3_hw = !(enc && std::strcmp(enc, "sw") == 0);
 
     const int64_t bytes = align_up(sizeof(CopyChunk) * std::max<int64_t>(p->n_unpack, 1), 256) +
                           align_up(sizeof(PackChunk) * std::max<int64_t>(p->n_pack, 1), 256) +

@@ -13,10 +13,21 @@
 namespace rs {
 
 // Elements per work item (tuned on gfx950; all multiples of 16 so every item
-// starts 16-element aligned when its tensor does).
-constexpr int64_t kUnpackChunk = 16384;   // elements per unpack work item
-constexpr int64_t kPackChunk = 8192;      // output elements per pack work item
-constexpr int64_t kZeroChunk = 65536;     // elements per zero-fill work item
+// starts 16-element aligned when its tensor does). Small items spread the
+// streams of the concurrently running workgroups over all HBM channels.
+#ifndef RS_UNPACK_CHUNK
+#define RS_UNPACK_CHUNK 8192
+#endif
+#ifndef RS_PACK_CHUNK
+#define RS_PACK_CHUNK 4096
+#endif
+#ifndef RS_ZERO_CHUNK
+#define RS_ZERO_CHUNK 65536
+#endif
+constexpr int64_t kUnpackChunk = RS_UNPACK_CHUNK;   // elements per unpack work item
+constexpr int64_t kPackChunk = RS_PACK_CHUNK;       // output elements per pack work item
+constexpr int64_t kZeroChunk = RS_ZERO_CHUNK;       // elements per zero-fill work item
+static_assert(kUnpackChunk % 16 == 0 && kPackChunk % 16 == 0, "work items keep 16-element alignment");
 constexpr int kFlatPerGroup = 4;          // flat quant blocks per 256-thread group (one per wave)
 
 // One tensor of a loaded plan.

@@ -142,11 +142,49 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("encoder", ["sw", "hw"])
 @pytest.mark.parametrize("V", [1, 3, 6, 16])
 @pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
-def test_ragged_group(gpu_lib, V, pdtype):
+def test_ragged_group(gpu_lib, V, pdtype, encoder, monkeypatch):
     import structure_aware_grouped_amd as rs
+    monkeypatch.setenv("RS_E4M3_ENCODER", encoder)
     _full_check(rs, RAGGED, V, pdtype, 7 * V)
+
+
+@pytest.mark.parametrize("encoder", ["sw", "hw"])
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_e4m3_amax_overshoot(gpu_lib, encoder, pdtype, monkeypatch):
+    """Block maxima whose scaled value rounds just above 448 (fl32(amax * fl32(448/amax)) >
+    448) must saturate to 0x7E / 0xFE, like every other value of the block."""
+    import structure_aware_grouped_amd as rs
+    monkeypatch.setenv("RS_E4M3_ENCODER", encoder)
+    rng = _rng(21)
+    a = (rng.random(200_000) * 100).astype(np.float32) + np.float32(1e-3)
+    if pdtype == torch.bfloat16:
+        a = f32_from_bf16_bits(bf16_bits_from_f32(a))
+    r = (448.0 / a.astype(np.float64)).astype(np.float32)
+    over = a[(a.astype(np.float64) * r.astype(np.float64)).astype(np.float32) > 448][:1024]
+    assert over.size >= 256
+    b = 64
+    blocks = np.empty((over.size, b), dtype=np.float32)
+    blocks[:] = (rng.random((over.size, b)) * 2 - 1) * over[:, None] * np.float32(0.99)
+    blocks[:, 3] = over
+    blocks[:, 40] = -over
+    if pdtype == torch.bfloat16:
+        blocks = f32_from_bf16_bits(bf16_bits_from_f32(blocks)).reshape(blocks.shape)
+    data = blocks.ravel()
+    spec = [TensorSpec("o", over.size, b, "FLAT", b)]
+    plan = rs.rs_plan_load(spec, 1, data.size, [0], 1, 0)
+    src = torch.from_numpy(data).to(DEV).to(pdtype)
+    q = torch.empty(data.size, dtype=torch.uint8, device=DEV)
+    sc = torch.empty(over.size, dtype=torch.float32, device=DEV)
+    rs.rs_block_quant(plan, src, q, "e4m3", sc)
+    wq, ws = OT.block_quant(data, spec, [0], data.size, 1, "e4m3")
+    got = tensor_bits(q)
+    assert np.array_equal(got, wq)
+    assert np.all(got.reshape(-1, b)[:, 3] == 0x7E) and np.all(got.reshape(-1, b)[:, 40] == 0xFE)
+    assert np.array_equal(tensor_bits(sc), ws.view(np.uint32))
+    plan.close()
 
 
 def test_trailing_padding_ranks(gpu_lib):
@@ -163,42 +201,36 @@ def test_single_element_group(gpu_lib):
 
 
 @pytest.mark.parametrize("encoder", ["sw", "hw"])
-def test_e4m3_encoder_sweep(gpu_lib, encoder, monkeypatch):
-    """Every fp32 mantissa at the rounding-critical exponents, and structured low bits at
-    all others, through rs_block_quant with a 448 pivot in each block (so r = 1)."""
+def test_e4m3_encoder_every_mantissa(gpu_lib, encoder, monkeypatch):
+    """Every fp32 value of magnitude in [2^-20, 448), both signs (all 2^23 mantissas of each
+    binade), plus signed zeros and subnormals, through rs_block_quant with a 448 pivot at
+    the head of each 2048-element block (so r = 1 and y = x). Everything below 2^-20 lies
+    under half the smallest E4M3 subnormal and must encode as a signed zero."""
     import structure_aware_grouped_amd as rs
     monkeypatch.setenv("RS_E4M3_ENCODER", encoder)
-    vals = []
-    full_exps = [-10, -7, -6, -1, 7, 8]
-    for e in full_exps:
-        m = np.arange(1 << 23, dtype=np.uint32)
-        vals.append(((e + 127) << 23) | m)
-    lows = np.array([0, 1, 2, (1 << 19) - 1, 1 << 19, (1 << 19) + 1, (1 << 20) - 1, 0x5A5A5], np.uint32)
-    for e in range(-20, 9):
-        m3 = np.arange(8, dtype=np.uint32)[:, None] << np.uint32(20)
-        vals.append((np.uint32((e + 127) << 23) | (m3 | lows[None, :]).ravel()))
-    u = np.concatenate(vals)
-    x = u.view(np.float32)
-    x = x[np.abs(x) < 448]
-    x = np.concatenate([x, -x, np.float32([0.0, -0.0, 2.0 ** -149, -(2.0 ** -149)])])
     b = 2047
-    nblk = -(-x.size // b)
-    data = np.zeros(nblk * 2048, dtype=np.float32)
-    body = data.reshape(nblk, 2048)
-    body[:, 0] = 448.0
-    flat = np.zeros(nblk * b, dtype=np.float32)
-    flat[: x.size] = x
-    body[:, 1:] = flat.reshape(nblk, b)
+    per = 2 * (1 << 23)
+    nblk = -(-per // b)
     spec = [TensorSpec("sweep", nblk, 2048, "FLAT", 2048)]
     plan = rs.rs_plan_load(spec, 1, nblk * 2048, [0], 1, 0)
     q = torch.empty(nblk * 2048, dtype=torch.uint8, device=DEV)
     sc = torch.empty(nblk, dtype=torch.float32, device=DEV)
-    rs.rs_block_quant(plan, torch.from_numpy(data).to(DEV), q, "e4m3", sc)
-    got = tensor_bits(q).reshape(nblk, 2048)
-    assert np.all(tensor_bits(sc) == np.float32(1.0).view(np.uint32))
-    assert np.all(got[:, 0] == 0x7E)
-    want = OC.e4m3_encode(flat)
-    assert np.array_equal(got[:, 1:].ravel(), want)
+    m = np.arange(1 << 23, dtype=np.uint32)
+    tiny = np.float32([0.0, -0.0, 2.0 ** -149, -(2.0 ** -149), 2.0 ** -127, 2.0 ** -21, -(2.0 ** -21)])
+    for e in range(-20, 9):
+        x = (np.uint32((e + 127) << 23) | m).view(np.float32)
+        x = x[x < 448]
+        x = np.concatenate([x, -x, tiny])
+        data = np.zeros((nblk, 2048), dtype=np.float32)
+        data[:, 0] = 448.0
+        flat = np.zeros(nblk * b, dtype=np.float32)
+        flat[: x.size] = x
+        data[:, 1:] = flat.reshape(nblk, b)
+        rs.rs_block_quant(plan, torch.from_numpy(data.ravel()).to(DEV), q, "e4m3", sc)
+        got = tensor_bits(q).reshape(nblk, 2048)
+        assert np.all(tensor_bits(sc) == np.float32(1.0).view(np.uint32)), e
+        assert np.all(got[:, 0] == 0x7E), e
+        assert np.array_equal(got[:, 1:].ravel()[: x.size], OC.e4m3_encode(x)), e
     # decode of every code through dequant with unit scales
     codes_all = np.tile(np.arange(256, dtype=np.uint8), 8)
     spec2 = [TensorSpec("codes", 1, 2048, "FLAT", 2048)]
@@ -208,15 +240,16 @@ def test_e4m3_encoder_sweep(gpu_lib, encoder, monkeypatch):
                         torch.ones(1, dtype=torch.float32, device=DEV), out)
     dec = out.cpu().numpy().astype(np.float64)
     ref = OC.e4m3_decode(codes_all)
-    assert np.all((dec == ref) & (np.signbit(dec) == np.signbit(ref)) | (np.isnan(dec) & np.isnan(ref)))
+    assert np.all(((dec == ref) & (np.signbit(dec) == np.signbit(ref))) | (np.isnan(dec) & np.isnan(ref)))
     plan.close()
     plan2.close()
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "i8", "u8"])
-def test_special_blocks(gpu_lib, fmt):
+@pytest.mark.parametrize("fmt,encoder", [("e4m3", "sw"), ("e4m3", "hw"), ("i8", "sw"), ("u8", "sw")])
+def test_special_blocks(gpu_lib, fmt, encoder, monkeypatch):
     """All-zero, subnormal-amax, constant, single-outlier and signed-zero blocks."""
     import structure_aware_grouped_amd as rs
+    monkeypatch.setenv("RS_E4M3_ENCODER", encoder)
     b = 256
     blocks = [
         np.zeros(b, np.float32),
