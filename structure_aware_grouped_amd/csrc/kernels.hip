@@ -344,27 +344,37 @@ __device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
   for (int64_t i = tid; i < nv; i += kThreads) stg(v + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 }
 
+// One workgroup per tile.
 template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void quant_kernel(const QJob* __restrict__ jobs,
-                                                         const void* __restrict__ src,
-                                                         uint8_t* __restrict__ q,
-                                                         float* __restrict__ scales) {
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(const QJob* __restrict__ jobs,
+                                                              const void* __restrict__ src,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales) {
   __shared__ uint32_t red[kThreads / kWave];
   const QJob j = jobs[blockIdx.x];
-  const int tid = threadIdx.x;
-  if (j.kind == QJOB_ZERO) {
-    zero_bytes(q, j.base, j.stride, tid);
-  } else if (j.kind == QJOB_TILE) {
-    quant_block<BF16, FMT, HW, kThreads, BF16 ? 8 : 16>(src, q, scales, j.base, j.stride, j.rows,
-                                                         j.cols, j.scale, tid, red);
-  } else {
-    const int wave = tid / kWave;
-    if (wave < j.rows) {
-      const int len = wave == j.rows - 1 ? j.last : j.cols;
-      quant_block<BF16, FMT, HW, kWave, 8>(src, q, scales, j.base + static_cast<int64_t>(wave) * j.cols,
-                                           len, 1, len, j.scale + wave, tid & (kWave - 1), nullptr);
-    }
-  }
+  quant_block<BF16, FMT, HW, kThreads, BF16 ? 8 : 16>(src, q, scales, j.base, j.stride, j.rows, j.cols,
+                                                       j.scale, threadIdx.x, red);
+}
+
+// One wave per flat block, up to four blocks per workgroup.
+template <bool BF16, int FMT, bool HW>
+__global__ __launch_bounds__(kThreads) void quant_flat_kernel(const QJob* __restrict__ jobs,
+                                                              const void* __restrict__ src,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales) {
+  const QJob j = jobs[blockIdx.x];
+  const int wave = threadIdx.x / kWave;
+  if (wave >= j.rows) return;
+  const int len = wave == j.rows - 1 ? j.last : j.cols;
+  quant_block<BF16, FMT, HW, kWave, 8>(src, q, scales, j.base + static_cast<int64_t>(wave) * j.cols, len,
+                                       1, len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr);
+}
+
+// Code bytes of positions outside every block.
+__global__ __launch_bounds__(kThreads) void zero_codes_kernel(const QJob* __restrict__ jobs,
+                                                              uint8_t* __restrict__ q) {
+  const QJob j = jobs[blockIdx.x];
+  zero_bytes(q, j.base, j.stride, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ dequant
@@ -394,25 +404,33 @@ __device__ void dequant_block(const uint8_t* __restrict__ q, float* __restrict__
 }
 
 template <int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void dequant_kernel(const QJob* __restrict__ jobs,
-                                                           const uint8_t* __restrict__ q,
-                                                           const float* __restrict__ scales,
-                                                           float* __restrict__ out) {
+__global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __restrict__ jobs,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out) {
   const QJob j = jobs[blockIdx.x];
-  const int tid = threadIdx.x;
-  if (j.kind == QJOB_ZERO) {
-    zero_f32(out, j.base, j.stride, tid);
-  } else if (j.kind == QJOB_TILE) {
-    dequant_block<FMT, HW, kThreads>(q, out, scales[j.scale], j.base, j.stride, j.rows, j.cols, tid);
-  } else {
-    const int wave = tid / kWave;
-    if (wave < j.rows) {
-      const int len = wave == j.rows - 1 ? j.last : j.cols;
-      dequant_block<FMT, HW, kWave>(q, out, scales[j.scale + wave],
-                                    j.base + static_cast<int64_t>(wave) * j.cols, len, 1, len,
-                                    tid & (kWave - 1));
-    }
-  }
+  dequant_block<FMT, HW, kThreads>(q, out, scales[j.scale], j.base, j.stride, j.rows, j.cols,
+                                   threadIdx.x);
+}
+
+template <int FMT, bool HW>
+__global__ __launch_bounds__(kThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out) {
+  const QJob j = jobs[blockIdx.x];
+  const int wave = threadIdx.x / kWave;
+  if (wave >= j.rows) return;
+  const int len = wave == j.rows - 1 ? j.last : j.cols;
+  dequant_block<FMT, HW, kWave>(q, out, scales[j.scale + wave], j.base + static_cast<int64_t>(wave) * j.cols,
+                                len, 1, len, threadIdx.x & (kWave - 1));
+}
+
+// Dequantised values of positions outside every block.
+__global__ __launch_bounds__(kThreads) void zero_values_kernel(const QJob* __restrict__ jobs,
+                                                               float* __restrict__ out) {
+  const QJob j = jobs[blockIdx.x];
+  zero_f32(out, j.base, j.stride, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ unpack
@@ -639,18 +657,49 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
 
 namespace {
 
+template <bool BF16, int FMT, bool HW>
+void launch_quant_kinds(const rs_plan* p, const void* src, uint8_t* q, float* scales, hipStream_t s) {
+  const dim3 block(kThreads);
+  const QJob* tiles = p->qjobs;
+  const QJob* flats = tiles + p->n_qtile;
+  if (p->n_qtile)
+    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qtile)), block,
+                       0, s, tiles, src, q, scales);
+  if (p->n_qflat)
+    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat)), block,
+                       0, s, flats, src, q, scales);
+}
+
 template <bool BF16>
 void launch_quant(const rs_plan* p, const void* src, int fmt, bool hw, uint8_t* q, float* scales,
                   hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p->n_qjobs)), block(kThreads);
   if (fmt == FMT_E4M3 && hw)
-    hipLaunchKernelGGL((quant_kernel<BF16, FMT_E4M3, true>), grid, block, 0, s, p->qjobs, src, q, scales);
+    launch_quant_kinds<BF16, FMT_E4M3, true>(p, src, q, scales, s);
   else if (fmt == FMT_E4M3)
-    hipLaunchKernelGGL((quant_kernel<BF16, FMT_E4M3, false>), grid, block, 0, s, p->qjobs, src, q, scales);
+    launch_quant_kinds<BF16, FMT_E4M3, false>(p, src, q, scales, s);
   else if (fmt == FMT_I8)
-    hipLaunchKernelGGL((quant_kernel<BF16, FMT_I8, false>), grid, block, 0, s, p->qjobs, src, q, scales);
+    launch_quant_kinds<BF16, FMT_I8, false>(p, src, q, scales, s);
   else
-    hipLaunchKernelGGL((quant_kernel<BF16, FMT_U8, false>), grid, block, 0, s, p->qjobs, src, q, scales);
+    launch_quant_kinds<BF16, FMT_U8, false>(p, src, q, scales, s);
+  if (p->n_qzero)
+    hipLaunchKernelGGL(zero_codes_kernel, dim3(static_cast<unsigned>(p->n_qzero)), dim3(kThreads), 0, s,
+                       p->qjobs + p->n_qtile + p->n_qflat, q);
+}
+
+template <int FMT, bool HW>
+void launch_dequant(const rs_plan* p, const uint8_t* q, const float* scales, float* out, hipStream_t s) {
+  const dim3 block(kThreads);
+  const QJob* tiles = p->qjobs;
+  const QJob* flats = tiles + p->n_qtile;
+  if (p->n_qtile)
+    hipLaunchKernelGGL((dequant_tile_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qtile)), block, 0, s,
+                       tiles, q, scales, out);
+  if (p->n_qflat)
+    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat)), block, 0, s,
+                       flats, q, scales, out);
+  if (p->n_qzero)
+    hipLaunchKernelGGL(zero_values_kernel, dim3(static_cast<unsigned>(p->n_qzero)), block, 0, s,
+                       flats + p->n_qflat, out);
 }
 
 int fmt_of(int32_t q_dt) {
@@ -696,15 +745,14 @@ extern "C" int rs_block_dequant(rs_plan* p, const void* q, int32_t q_dt, const f
   if (!aligned16(q) || !aligned16(out)) return fail(RS_EALIGN, std::string(who) + ": q / out not 16-byte aligned");
   if (p->n_qjobs == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(p->n_qjobs)), block(kThreads);
   const uint8_t* qb = static_cast<const uint8_t*>(q);
   if (fmt == FMT_E4M3 && p->e4m3_hw)
-    hipLaunchKernelGGL((dequant_kernel<FMT_E4M3, true>), grid, block, 0, s, p->qjobs, qb, scales, out);
+    launch_dequant<FMT_E4M3, true>(p, qb, scales, out, s);
   else if (fmt == FMT_E4M3)
-    hipLaunchKernelGGL((dequant_kernel<FMT_E4M3, false>), grid, block, 0, s, p->qjobs, qb, scales, out);
+    launch_dequant<FMT_E4M3, false>(p, qb, scales, out, s);
   else if (fmt == FMT_I8)
-    hipLaunchKernelGGL((dequant_kernel<FMT_I8, false>), grid, block, 0, s, p->qjobs, qb, scales, out);
+    launch_dequant<FMT_I8, false>(p, qb, scales, out, s);
   else
-    hipLaunchKernelGGL((dequant_kernel<FMT_U8, false>), grid, block, 0, s, p->qjobs, qb, scales, out);
+    launch_dequant<FMT_U8, false>(p, qb, scales, out, s);
   return launched(who);
 }

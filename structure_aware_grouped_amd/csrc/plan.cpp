@@ -75,7 +75,8 @@ int validate(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S, const
 struct Tables {
   std::vector<CopyChunk> unpack;
   std::vector<PackChunk> pack;
-  std::vector<QJob> qjobs;
+  std::vector<QJob> qjobs;          // sorted by kind: tiles, flat groups, zero ranges
+  int64_t n_qtile = 0, n_qflat = 0, n_qzero = 0;
   int64_t n_qblocks = 0;
   int64_t padding = 0;
   int32_t max_tile_vec16 = 0;
@@ -176,6 +177,14 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     pos = r.second;
   }
   zero(pos, top);
+  // one kernel per job kind: keep each kind contiguous
+  std::stable_sort(tb->qjobs.begin(), tb->qjobs.end(),
+                   [](const QJob& a, const QJob& b) { return a.kind < b.kind; });
+  for (const QJob& j : tb->qjobs) {
+    if (j.kind == QJOB_TILE) ++tb->n_qtile;
+    else if (j.kind == QJOB_FLAT) ++tb->n_qflat;
+    else ++tb->n_qzero;
+  }
 }
 
 template <typename T>
@@ -255,6 +264,9 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->n_pack = static_cast<int64_t>(tb.pack.size());
     p->n_qjobs = static_cast<int64_t>(tb.qjobs.size());
     p->n_qblocks = tb.n_qblocks;
+    p->n_qtile = tb.n_qtile;
+    p->n_qflat = tb.n_qflat;
+    p->n_qzero = tb.n_qzero;
     p->max_tile_vec16 = tb.max_tile_vec16;
     // gfx950's FP8 conversion (OCP E4M3, round to nearest even) by default;
     // RS_E4M3_ENCODER=sw selects the integer encoder, which gives the same codes.

@@ -105,8 +105,9 @@ struct rs_plan {
   int64_t n_unpack = 0;
   rs::PackChunk* pack = nullptr;
   int64_t n_pack = 0;
-  rs::QJob* qjobs = nullptr;
+  rs::QJob* qjobs = nullptr;   // tile jobs, then flat-group jobs, then zero ranges
   int64_t n_qjobs = 0;
+  int64_t n_qtile = 0, n_qflat = 0, n_qzero = 0;
   int64_t n_qblocks = 0;
   int32_t max_tile_vec16 = 0;  // largest tile, in 16-byte vectors of 4-byte input
 
