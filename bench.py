@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--mode", default="step", choices=["step", "fp8_gather"],
+                    help="step: the workload's steps; fp8_gather: block quant of the rank slices, then "
+                         "the fused unpack-dequant of the codes into the bf16 tensors")
     ap.add_argument("--cpu-sample", type=int, default=1, help="0 disables the CPU-oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
     ap.add_argument("--copy-mib", type=int, default=1024,
@@ -60,6 +63,8 @@ def algorithmic_bytes(w, plan) -> dict:
     R, S = plan.R_mat, plan.S
     pb = 2 if w.param_dtype == "bf16" else 4
     out = {}
+    nq_all = sum(n for sp, n in zip(w.specs, plan.numels) if sp.kind in ("TILE", "FLAT"))
+    out["unpack_dequant"] = nq_all * (1 + pb) + 4 * plan.n_qblocks
     if w.adam_states:
         nq = sum(n for sp, n in zip(w.specs, plan.numels) if sp.kind in ("TILE", "FLAT"))
         pack = n_all * (4 + 4) + 4 * plan.padding
@@ -188,6 +193,20 @@ def main():
             ("dequant_v", lambda: rs.rs_block_dequant(plan, qv, "u8", sv, dv)),
         ]
         dominant = "pack_m"
+    elif args.mode == "fp8_gather":
+        if not w.quant:
+            print("fp8_gather needs a workload with block quantisation (1 or 3)", file=sys.stderr)
+            sys.exit(2)
+        G = inp.gathered()
+        q = garbage(R * S, torch.uint8, dev)
+        scales = garbage(plan.n_qblocks, torch.float32, dev)
+        full = [torch.empty(sp.rows, sp.cols, dtype=inp.pdtype, device=dev)
+                if sp.kind in ("TILE", "FLAT") else None for sp in specs]
+        steps = [
+            ("quant", lambda: rs.rs_block_quant(plan, G, q, w.quant, scales)),
+            ("unpack_dequant", lambda: rs.rs_unpack_dequant(plan, q, w.quant, scales, full)),
+        ]
+        dominant = "unpack_dequant"
     else:
         G = inp.gathered()
         params = inp.empty_params()
@@ -256,7 +275,17 @@ def main():
 
     # ---- sampled oracle check of the outputs of the last step
     check = "skipped"
-    if not args.no_check and not w.adam_states:
+    if not args.no_check and args.mode == "fp8_gather":
+        from oracle import transform as OT
+        from workloads import f32_from_bf16_bits
+        i = 1
+        x = f32_from_bf16_bits(inp.weight_bits(i))
+        got = tensor_bits(full[i]).ravel()
+        for _, b, pos in list(OT.quant_blocks([specs[i]], [0]))[:64]:
+            c, sc = OT.quantize_block(x[pos], w.quant)
+            assert np.array_equal(got[pos], OT.bf16_round(OT.dequant_values(c, sc, w.quant))), "unpack_dequant"
+        check = f"ok ({specs[i].name}: 64 tiles of quant + unpack-dequant vs the oracle)"
+    elif not args.no_check and not w.adam_states:
         from oracle import transform as OT
         # the second tensor (wk for the Llama layers, the first expert's down projection for the MoE)
         i = 1
@@ -282,7 +311,7 @@ def main():
                 "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant])}
 
     cpu = None
-    if args.cpu_sample and not w.adam_states:
+    if args.cpu_sample and not w.adam_states and args.mode == "step":
         cpu = cpu_baseline(w, plan)
 
     names = {1: "Llama-3-8B layer (bf16, 128x128 tiles), V=64: unpack + pack(1/V, accumulate) + e4m3 tile quant",
@@ -290,8 +319,13 @@ def main():
              3: "MoE layer (128 experts, bf16, 128x128 tiles), V=256: unpack + pack + e4m3 tile quant",
              4: "8-bit Adam states on the Llama-3-8B layer shapes, 2048-element blocks, V=64: "
                 "pack m,v + int8/uint8 quant + dequant"}
+    if args.mode == "fp8_gather":
+        names = {k: v.split(":")[0] + ": e4m3 quant of the rank slices + fused unpack-dequant to bf16"
+                 for k, v in names.items()}
+    metric = METRIC if (args.workload == 1 and args.mode == "step") else \
+        f"DBuffer layout transform GB/s (workload {args.workload}, {args.mode})"
     line = {
-        "metric": METRIC if args.workload == 1 else f"DBuffer layout transform GB/s (workload {args.workload})",
+        "metric": metric,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -18,6 +18,7 @@
  *   rs_pack_scatter     N full gradients -> flat buffer, fused scale/add/zero
  *   rs_block_quant      per-block absmax 8-bit quantisation of the flat buffer
  *   rs_block_dequant    the inverse of rs_block_quant
+ *   rs_unpack_dequant   gathered codes + scales -> the quantised full tensors
  *   rs_last_error       text of the calling thread's last error
  *
  * Conventions
@@ -84,7 +85,9 @@ typedef enum rs_block_kind {
 } rs_block_kind;
 
 /* One tensor of the group. A 1-D tensor of n elements is rows = n, cols = 1.
- * p0: ROWS k, TILE br, FLAT b; p1: TILE bc; unused fields must be 0. */
+ * p0: ROWS k, TILE br, FLAT b; p1: TILE bc; unused fields must be 0.
+ * Limits: rows * cols <= 2^40; a tile (br * bc) or a flat block (b) holds at
+ * most 2^24 elements. */
 typedef struct rs_tensor_spec {
   int64_t rows;
   int64_t cols;
@@ -204,6 +207,23 @@ int rs_block_quant(rs_plan* plan, const void* src, int32_t src_dt, void* q, int3
  * rs_block_quant; out: device fp32 R_mat*S, 16-byte aligned. */
 int rs_block_dequant(rs_plan* plan, const void* q, int32_t q_dt, const float* scales,
                      float* out, void* stream);
+
+/* Gather side of block-wise FP8 training, fused (bud-325 summary, TL;DR and
+ * Key claims: DeepSeek-V3-style block-wise FP8; feynmanwiki walkthrough,
+ * block-quantisation paragraph): after the codes and scales of every rank
+ * slice are all-gathered, rebuild each quantised tensor straight from them:
+ *   T_i[e] = fl32(dec(q[s_i + e]) * scale[B])   for e in block B of T_i,
+ * rounded to bf16 (nearest, ties to even) when dst_dt is RS_BF16. This is
+ * rs_block_dequant followed by rs_unpack_gathered (and a cast), in one pass
+ * that reads each code once and writes each value once.
+ * q, q_dt, scales: as produced by rs_block_quant (device, R_mat*S bytes,
+ * 16-byte aligned; fp32 [n_qblocks]). dst: HOST array of n device pointers;
+ * entries of TILE and FLAT tensors point to contiguous row-major tensors of
+ * n_i elements of dst_dt (RS_BF16 or RS_F32), 16-byte aligned; entries of
+ * other tensors are ignored and may be NULL. Codes 0x7F / 0xFF (E4M3 NaN)
+ * give unspecified values. Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */
+int rs_unpack_dequant(rs_plan* plan, const void* q, int32_t q_dt, const float* scales,
+                      void* const* dst, int32_t dst_dt, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). The
  * pointer stays valid until the thread's next rs_* call. */

@@ -29,6 +29,12 @@ Readings (listed in the design notes):
     tensors) are 0x00. Dequantised values there are +0.0.
   * Scales are ordered by tensor (spec order), then tile row-major / flat
     block index.
+  * Fused gather side of FP8 training ([summary] TL;DR and Key claims on
+    DeepSeek-V3-style block-wise FP8; [walk] block-quantisation paragraph):
+    after the codes and scales are all-gathered, each quantised tensor is
+    rebuilt as fl32(decode(code) * scale) at its own positions and, for a
+    bf16 parameter, rounded once more to bf16 (nearest, ties to even).
+    Tensors that are not quantised are not produced by this step.
 """
 from __future__ import annotations
 
@@ -157,7 +163,44 @@ def block_dequant(q: np.ndarray, scales, specs, starts, S: int, R_mat: int, fmt:
     return out
 
 
+# ---------------------------------------------------------------- gather side
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bf16 value of each finite fp32, ties to the even bf16 mantissa; uint16 bits.
+
+    The two candidates are x's bits truncated to the top 16 and the next bf16
+    step up (in magnitude); the nearer one wins, a tie goes to the one whose
+    lowest kept bit is 0."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lo = u & np.uint32(0xFFFF0000)
+    hi = lo + np.uint32(0x10000)
+    a = np.abs(x.astype(np.float64))
+    d_lo = a - np.abs(lo.view(np.float32).astype(np.float64))
+    d_hi = np.abs(hi.view(np.float32).astype(np.float64)) - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo >> np.uint32(16)) & np.uint32(1)).astype(bool))
+    return (np.where(pick_hi, hi, lo) >> np.uint32(16)).astype(np.uint16)
+
+
+def unpack_dequant(q: np.ndarray, scales, specs, starts, fmt: str, out: str):
+    """Full tensors rebuilt from gathered codes and scales; None for tensors that are not
+    quantised. out: "f32" (fp32 values) or "bf16" (uint16 bit patterns)."""
+    full = {}
+    for i, b, pos in quant_blocks(specs, starts):
+        v = dequant_values(q[pos], scales[b], fmt)
+        full.setdefault(i, np.zeros(numel(specs[i]), dtype=np.float32))[pos - int(starts[i])] = v
+    res = []
+    for i, spec in enumerate(specs):
+        if i not in full:
+            res.append(None)
+            continue
+        v = full[i].reshape(spec.rows, spec.cols)
+        res.append(bf16_round(v) if out == "bf16" else v)
+    return res
+
+
 __all__ = [
+    "bf16_round", "unpack_dequant",
     "f32", "inv_v", "unpack", "pack_values", "pack", "quant_blocks", "count_quant_blocks",
     "quantize_block", "block_quant", "dequant_values", "block_dequant", "padding_ranges",
 ]

@@ -12,5 +12,6 @@ from .binding import (  # noqa: F401
     rs_pack_scatter,
     rs_plan_build,
     rs_plan_load,
+    rs_unpack_dequant,
     rs_unpack_gathered,
 )

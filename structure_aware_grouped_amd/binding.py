@@ -25,7 +25,7 @@ ORDER_KINDS = {0: "default", 1: "by_block_size", 2: "by_shape"}
 RS_F32, RS_BF16, RS_E4M3, RS_I8, RS_U8 = 0, 1, 2, 3, 4
 CODE_FORMATS = {"e4m3": RS_E4M3, "i8": RS_I8, "u8": RS_U8}
 EXPORTS = ("rs_plan_build", "rs_plan_load", "rs_plan_info", "rs_plan_free", "rs_unpack_gathered",
-           "rs_pack_scatter", "rs_block_quant", "rs_block_dequant", "rs_last_error")
+           "rs_pack_scatter", "rs_block_quant", "rs_block_dequant", "rs_unpack_dequant", "rs_last_error")
 
 
 class RsError(RuntimeError):
@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rs_pack_scatter.argtypes = [P, ctypes.POINTER(P), I32, P, P, I32, F, P]
     lib.rs_block_quant.argtypes = [P, P, I32, P, I32, P, P]
     lib.rs_block_dequant.argtypes = [P, P, I32, P, P, P]
+    lib.rs_unpack_dequant.argtypes = [P, P, I32, P, ctypes.POINTER(P), I32, P]
     lib.rs_last_error.argtypes = []
     lib.rs_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -231,3 +232,24 @@ def rs_block_dequant(plan: Plan, q: torch.Tensor, fmt: str, scales: torch.Tensor
         raise ValueError("q / scales too short")
     _check(load().rs_block_dequant(plan.handle, q.data_ptr(), CODE_FORMATS[fmt], scales.data_ptr(),
                                    out.data_ptr(), _stream(plan.device)))
+
+
+def rs_unpack_dequant(plan: Plan, q: torch.Tensor, fmt: str, scales: torch.Tensor,
+                      dsts: List[Optional[torch.Tensor]]):
+    """dst_i <- fl32(code value * block scale) (rounded to bf16 for bf16 tensors) for every
+    quantised tensor; entries for other tensors may be None."""
+    _dev_check(plan, q, scales, *[d for d in dsts if d is not None])
+    if q.numel() * q.element_size() < plan.R_mat * plan.S or scales.numel() < plan.n_qblocks:
+        raise ValueError("q / scales too short")
+    dt = None
+    for d, n, sp in zip(dsts, plan.numels, plan.specs):
+        if d is None:
+            continue
+        if d.numel() != n or d.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("destination size or dtype does not match its tensor")
+        if dt is not None and d.dtype != dt:
+            raise ValueError("destinations share one dtype")
+        dt = d.dtype
+    ptrs = (ctypes.c_void_p * len(dsts))(*[d.data_ptr() if d is not None else None for d in dsts])
+    _check(load().rs_unpack_dequant(plan.handle, q.data_ptr(), CODE_FORMATS[fmt], scales.data_ptr(), ptrs,
+                                    RS_BF16 if dt == torch.bfloat16 else RS_F32, _stream(plan.device)))

@@ -433,6 +433,159 @@ __global__ __launch_bounds__(kThreads) void zero_values_kernel(const QJob* __res
   zero_f32(out, j.base, j.stride, threadIdx.x);
 }
 
+// ------------------------------------------------------------------ gather side
+
+// Nearest bf16 of a finite fp32, ties to even: add 0x7fff plus the kept lsb,
+// keep the top half.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One block of gathered codes -> its values inside the full tensor: element
+// (r, c) comes from q[qbase + r*stride + c] and goes to dst[dbase + r*stride + c]
+// as fl32(decode * s), rounded to bf16 when BF16OUT. Eight codes per 8-byte
+// load, four loads in flight per thread.
+template <int FMT, bool HW, bool BF16OUT, int NT>
+__device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ dst, float s,
+                             int64_t qbase, int64_t dbase, int64_t stride, int rows, int cols,
+                             int tid) {
+  if ((qbase % 8 == 0) && (dbase % 8 == 0) && (stride % 8 == 0) && (cols % 8 == 0)) {
+    constexpr int U = 4;
+    const int vpr = cols / 8;
+    const int nvec = rows * vpr;
+    GridWalk w(tid, vpr, NT);
+    for (int i0 = tid; i0 < nvec; i0 += NT * U) {
+      u32x2 c[U];
+      int64_t off[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        off[u] = static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 8;
+        if (i0 + u * NT < nvec) c[u] = ldg(reinterpret_cast<const u32x2*>(q + qbase + off[u]));
+        w.next();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i0 + u * NT >= nvec) continue;
+        const f32x4 a = decode4<FMT, HW>(c[u].x), b = decode4<FMT, HW>(c[u].y);
+        const float v[8] = {__fmul_rn(a.x, s), __fmul_rn(a.y, s), __fmul_rn(a.z, s), __fmul_rn(a.w, s),
+                            __fmul_rn(b.x, s), __fmul_rn(b.y, s), __fmul_rn(b.z, s), __fmul_rn(b.w, s)};
+        if constexpr (BF16OUT) {
+          const u32x4 o{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
+                        bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)};
+          stg(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + dbase + off[u]), o);
+        } else {
+          f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(dst) + dbase + off[u]);
+          stg(o, f32x4{v[0], v[1], v[2], v[3]});
+          stg(o + 1, f32x4{v[4], v[5], v[6], v[7]});
+        }
+      }
+    }
+    return;
+  }
+  const int64_t total = static_cast<int64_t>(rows) * cols;
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    const int64_t off = rr * stride + cc;
+    const float v = __fmul_rn(decode1<FMT, HW>(q[qbase + off]), s);
+    if constexpr (BF16OUT)
+      static_cast<uint16_t*>(dst)[dbase + off] = static_cast<uint16_t>(bf16_rne(v));
+    else
+      static_cast<float*>(dst)[dbase + off] = v;
+  }
+}
+
+// Contiguous row runs of a quantised tensor (see GatherChunk). Each lane turns
+// VEC codes into one 16-byte store (8 codes -> 8 bf16, 4 codes -> 4 fp32), so
+// the lanes of a wave read and write one contiguous range each; eight vectors
+// in flight per thread. A TILE run's rows share the band's scales: the scale
+// of every column vector is staged in LDS once per workgroup.
+template <int FMT, bool HW, bool BF16OUT>
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const GatherChunk* __restrict__ chunks,
+                                                               const uint8_t* __restrict__ q,
+                                                               const float* __restrict__ scales,
+                                                               void* const* __restrict__ dst) {
+  constexpr int VEC = BF16OUT ? 8 : 4;
+  constexpr int U = 8;
+  __shared__ float col_scale[kGatherMaxCols / 4];
+  const GatherChunk c = chunks[blockIdx.x];
+  void* out = dst[c.tensor];
+  const int vpr = c.cols / VEC;
+  const int nvec = c.rows * vpr;
+  const uint8_t* qb = q + c.qbase;
+  const bool band = c.rstep == 0;
+  if (band) {
+    for (int t = threadIdx.x; t < vpr; t += kThreads) col_scale[t] = scales[c.scale0 + (t * VEC) / c.bc];
+    __syncthreads();
+  }
+  GridWalk w(threadIdx.x, vpr, kThreads);
+  for (int i0 = threadIdx.x; i0 < nvec; i0 += kThreads * U) {
+    uint32_t code[U][VEC / 4];
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i < nvec) {
+        if constexpr (VEC == 8) {
+          const u32x2 t = ldg(reinterpret_cast<const u32x2*>(qb) + i);
+          code[u][0] = t.x;
+          code[u][1] = t.y;
+        } else {
+          code[u][0] = ldg(reinterpret_cast<const uint32_t*>(qb) + i);
+        }
+        sc[u] = band ? col_scale[w.col] : scales[c.scale0 + w.row];
+      }
+      w.next();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i >= nvec) continue;
+      const int64_t e = c.toff + static_cast<int64_t>(i) * VEC;
+      float v[VEC];
+#pragma unroll
+      for (int h = 0; h < VEC / 4; ++h) {
+        const f32x4 d = decode4<FMT, HW>(code[u][h]);
+        v[4 * h] = __fmul_rn(d.x, sc[u]);
+        v[4 * h + 1] = __fmul_rn(d.y, sc[u]);
+        v[4 * h + 2] = __fmul_rn(d.z, sc[u]);
+        v[4 * h + 3] = __fmul_rn(d.w, sc[u]);
+      }
+      if constexpr (BF16OUT) {
+        stg(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e),
+            u32x4{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
+                  bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)});
+      } else {
+        stg(reinterpret_cast<f32x4*>(static_cast<float*>(out) + e), f32x4{v[0], v[1], v[2], v[3]});
+      }
+    }
+  }
+}
+
+template <int FMT, bool HW, bool BF16OUT>
+__global__ __launch_bounds__(kThreads) void gather_tile_kernel(const QJob* __restrict__ jobs,
+                                                               const uint8_t* __restrict__ q,
+                                                               const float* __restrict__ scales,
+                                                               void* const* __restrict__ dst) {
+  const QJob j = jobs[blockIdx.x];
+  gather_block<FMT, HW, BF16OUT, kThreads>(q, dst[j.tensor], scales[j.scale], j.base, j.toff, j.stride,
+                                           j.rows, j.cols, threadIdx.x);
+}
+
+template <int FMT, bool HW, bool BF16OUT>
+__global__ __launch_bounds__(kThreads) void gather_flat_kernel(const QJob* __restrict__ jobs,
+                                                               const uint8_t* __restrict__ q,
+                                                               const float* __restrict__ scales,
+                                                               void* const* __restrict__ dst) {
+  const QJob j = jobs[blockIdx.x];
+  const int wave = threadIdx.x / kWave;
+  if (wave >= j.rows) return;
+  const int len = wave == j.rows - 1 ? j.last : j.cols;
+  const int64_t step = static_cast<int64_t>(wave) * j.cols;
+  gather_block<FMT, HW, BF16OUT, kWave>(q, dst[j.tensor], scales[j.scale + wave], j.base + step,
+                                        j.toff + step, len, 1, len, threadIdx.x & (kWave - 1));
+}
+
 // ------------------------------------------------------------------ unpack
 
 template <int U>
@@ -754,5 +907,65 @@ extern "C" int rs_block_dequant(rs_plan* p, const void* q, int32_t q_dt, const f
     launch_dequant<FMT_I8, false>(p, qb, scales, out, s);
   else
     launch_dequant<FMT_U8, false>(p, qb, scales, out, s);
+  return launched(who);
+}
+
+namespace {
+
+template <int FMT, bool HW, bool BF16OUT>
+void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipStream_t s) {
+  const dim3 block(kThreads);
+  const QJob* tiles = p->gjobs;
+  const QJob* flats = tiles + p->n_gtile;
+  if (p->n_gchunks)
+    hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gchunks)),
+                       block, 0, s, p->gchunks, q, scales, p->gdst.dev);
+  if (p->n_gtile)
+    hipLaunchKernelGGL((gather_tile_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gtile)),
+                       block, 0, s, tiles, q, scales, p->gdst.dev);
+  if (p->n_gflat)
+    hipLaunchKernelGGL((gather_flat_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gflat)),
+                       block, 0, s, flats, q, scales, p->gdst.dev);
+}
+
+template <bool BF16OUT>
+void launch_gather_fmt(const rs_plan* p, int fmt, const uint8_t* q, const float* scales, hipStream_t s) {
+  if (fmt == FMT_E4M3 && p->e4m3_hw)
+    launch_gather<FMT_E4M3, true, BF16OUT>(p, q, scales, s);
+  else if (fmt == FMT_E4M3)
+    launch_gather<FMT_E4M3, false, BF16OUT>(p, q, scales, s);
+  else if (fmt == FMT_I8)
+    launch_gather<FMT_I8, false, BF16OUT>(p, q, scales, s);
+  else
+    launch_gather<FMT_U8, false, BF16OUT>(p, q, scales, s);
+}
+
+}  // namespace
+
+extern "C" int rs_unpack_dequant(rs_plan* p, const void* q, int32_t q_dt, const float* scales,
+                                 void* const* dst, int32_t dst_dt, void* stream) {
+  const char* who = "rs_unpack_dequant";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  const int fmt = fmt_of(q_dt);
+  if (fmt < 0) return fail(RS_EDTYPE, std::string(who) + ": code format must be E4M3, I8 or U8");
+  if (dst_dt != RS_F32 && dst_dt != RS_BF16) return fail(RS_EDTYPE, std::string(who) + ": dst must be fp32 or bf16");
+  if (!q || !dst || (!scales && p->n_qblocks > 0)) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (!aligned16(q)) return fail(RS_EALIGN, std::string(who) + ": q not 16-byte aligned");
+  for (int64_t i = 0; i < p->n; ++i) {
+    if (p->t[i].kind != RS_TILE && p->t[i].kind != RS_FLAT) continue;
+    if (!dst[i]) return fail(RS_EINVAL, std::string(who) + ": null destination " + std::to_string(i));
+    if (!aligned16(dst[i])) return fail(RS_EALIGN, std::string(who) + ": destination " + std::to_string(i) + " not 16-byte aligned");
+  }
+  if (p->n_gchunks + p->n_gtile + p->n_gflat == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = sync_table(p, &p->gdst, dst, s, who);
+  if (st != RS_OK) return st;
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  if (dst_dt == RS_BF16)
+    launch_gather_fmt<true>(p, fmt, qb, scales, s);
+  else
+    launch_gather_fmt<false>(p, fmt, qb, scales, s);
   return launched(who);
 }

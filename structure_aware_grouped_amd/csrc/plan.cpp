@@ -77,6 +77,9 @@ struct Tables {
   std::vector<PackChunk> pack;
   std::vector<QJob> qjobs;          // sorted by kind: tiles, flat groups, zero ranges
   int64_t n_qtile = 0, n_qflat = 0, n_qzero = 0;
+  std::vector<GatherChunk> gchunks;
+  std::vector<QJob> gjobs;          // tiles, then flat groups
+  int64_t n_gtile = 0, n_gflat = 0;
   int64_t n_qblocks = 0;
   int64_t padding = 0;
   int32_t max_tile_vec16 = 0;
@@ -123,7 +126,8 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
 
   // quant / dequant: tiles and flat blocks in scale order, then zero ranges
   int64_t q = 0;
-  for (const Tensor& x : t) {
+  for (int64_t ti = 0; ti < n; ++ti) {
+    const Tensor& x = t[ti];
     if (x.kind == RS_TILE) {
       for (int64_t r0 = 0; r0 < x.rows; r0 += x.p0) {
         for (int64_t c0 = 0; c0 < x.cols; c0 += x.p1) {
@@ -135,6 +139,8 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
           j.cols = static_cast<int32_t>(std::min(x.p1, x.cols - c0));
           j.kind = QJOB_TILE;
           j.last = 0;
+          j.tensor = static_cast<int32_t>(ti);
+          j.toff = j.base - x.start;
           tb->qjobs.push_back(j);
           const int64_t v16 = int64_t(j.rows) * ((int64_t(j.cols) * 4 + 15) / 16);
           tb->max_tile_vec16 = static_cast<int32_t>(std::max<int64_t>(tb->max_tile_vec16, std::min<int64_t>(v16, 1 << 30)));
@@ -152,6 +158,8 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
         j.cols = static_cast<int32_t>(x.p0);
         j.kind = QJOB_FLAT;
         j.last = static_cast<int32_t>(std::min(x.p0, x.n - (b0 + cnt - 1) * x.p0));
+        j.tensor = static_cast<int32_t>(ti);
+        j.toff = j.base - x.start;
         tb->qjobs.push_back(j);
         q += cnt;
       }
@@ -168,6 +176,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
       j.base = p;
       j.stride = std::min(kZeroChunk, to - p);
       j.kind = QJOB_ZERO;
+      j.tensor = -1;
       tb->qjobs.push_back(j);
     }
   };
@@ -185,6 +194,80 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     else if (j.kind == QJOB_FLAT) ++tb->n_qflat;
     else ++tb->n_qzero;
   }
+
+  // gather side: contiguous row runs where every 16-element vector has one
+  // scale; per-block jobs (as for quant) for everything else
+  std::vector<char> tile_vec(n, 0);
+  for (int64_t ti = 0; ti < n; ++ti)
+    tile_vec[ti] = t[ti].kind == RS_TILE && t[ti].cols % 16 == 0 && t[ti].p1 % 16 == 0 &&
+                   t[ti].cols <= kGatherMaxCols;
+  for (const QJob& j : tb->qjobs)
+    if (j.kind == QJOB_TILE && !tile_vec[j.tensor]) tb->gjobs.push_back(j);
+  q = 0;
+  for (int64_t ti = 0; ti < n; ++ti) {
+    const Tensor& x = t[ti];
+    if (x.kind == RS_TILE) {
+      const int64_t ntc = (x.cols + x.p1 - 1) / x.p1;
+      if (tile_vec[ti]) {
+        const int64_t per = std::max<int64_t>(1, kGatherChunk / x.cols);
+        for (int64_t r0 = 0; r0 < x.rows; r0 += x.p0) {
+          const int64_t band_end = std::min(x.rows, r0 + x.p0);
+          for (int64_t r = r0; r < band_end; r += per) {
+            GatherChunk c{};
+            c.qbase = x.start + r * x.cols;
+            c.toff = r * x.cols;
+            c.scale0 = q + (r0 / x.p0) * ntc;
+            c.rows = static_cast<int32_t>(std::min(per, band_end - r));
+            c.cols = static_cast<int32_t>(x.cols);
+            c.bc = static_cast<int32_t>(x.p1);
+            c.rstep = 0;
+            c.tensor = static_cast<int32_t>(ti);
+            tb->gchunks.push_back(c);
+          }
+        }
+      }
+      q += ((x.rows + x.p0 - 1) / x.p0) * ntc;
+    } else if (x.kind == RS_FLAT) {
+      const int64_t nfull = x.n / x.p0;            // whole blocks
+      int64_t done = 0;
+      if (x.p0 % 16 == 0) {
+        const int64_t per = std::max<int64_t>(1, kGatherChunk / x.p0);
+        for (; done < nfull; done += per) {
+          GatherChunk c{};
+          c.qbase = x.start + done * x.p0;
+          c.toff = done * x.p0;
+          c.scale0 = q + done;
+          c.rows = static_cast<int32_t>(std::min(per, nfull - done));
+          c.cols = static_cast<int32_t>(x.p0);
+          c.bc = static_cast<int32_t>(x.p0);
+          c.rstep = 1;
+          c.tensor = static_cast<int32_t>(ti);
+          tb->gchunks.push_back(c);
+        }
+        done = nfull;
+      }
+      // remaining blocks (all of them, or the partial last one) as flat groups
+      const int64_t nblk = (x.n + x.p0 - 1) / x.p0;
+      for (int64_t b0 = done; b0 < nblk; b0 += kFlatPerGroup) {
+        const int64_t cnt = std::min<int64_t>(kFlatPerGroup, nblk - b0);
+        QJob j{};
+        j.base = x.start + b0 * x.p0;
+        j.stride = x.p0;
+        j.scale = q + b0;
+        j.rows = static_cast<int32_t>(cnt);
+        j.cols = static_cast<int32_t>(x.p0);
+        j.kind = QJOB_FLAT;
+        j.last = static_cast<int32_t>(std::min(x.p0, x.n - (b0 + cnt - 1) * x.p0));
+        j.tensor = static_cast<int32_t>(ti);
+        j.toff = j.base - x.start;
+        tb->gjobs.push_back(j);
+      }
+      q += nblk;
+    }
+  }
+  std::stable_sort(tb->gjobs.begin(), tb->gjobs.end(),
+                   [](const QJob& a, const QJob& b) { return a.kind < b.kind; });
+  for (const QJob& j : tb->gjobs) (j.kind == QJOB_TILE ? tb->n_gtile : tb->n_gflat)++;
 }
 
 template <typename T>
@@ -213,7 +296,7 @@ static void release(rs_plan* p) {
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(p->device);
   (void)hipDeviceSynchronize();
-  for (PtrTable* tab : {&p->dst, &p->src}) {
+  for (PtrTable* tab : {&p->dst, &p->src, &p->gdst}) {
     if (tab->done) (void)hipEventDestroy(tab->done);
     if (tab->stage) (void)hipHostFree(tab->stage);
   }
@@ -267,6 +350,9 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->n_qtile = tb.n_qtile;
     p->n_qflat = tb.n_qflat;
     p->n_qzero = tb.n_qzero;
+    p->n_gchunks = static_cast<int64_t>(tb.gchunks.size());
+    p->n_gtile = tb.n_gtile;
+    p->n_gflat = tb.n_gflat;
     p->max_tile_vec16 = tb.max_tile_vec16;
     // gfx950's FP8 conversion (OCP E4M3, round to nearest even) by default;
     // RS_E4M3_ENCODER=sw selects the integer encoder, which gives the same codes.
@@ -276,7 +362,9 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     const int64_t bytes = align_up(sizeof(CopyChunk) * std::max<int64_t>(p->n_unpack, 1), 256) +
                           align_up(sizeof(PackChunk) * std::max<int64_t>(p->n_pack, 1), 256) +
                           align_up(sizeof(QJob) * std::max<int64_t>(p->n_qjobs, 1), 256) +
-                          2 * align_up(sizeof(void*) * n, 256);
+                          align_up(sizeof(GatherChunk) * std::max<int64_t>(p->n_gchunks, 1), 256) +
+                          align_up(sizeof(QJob) * std::max<int64_t>(p->n_gtile + p->n_gflat, 1), 256) +
+                          3 * align_up(sizeof(void*) * n, 256);
     if (hipMalloc(&p->dmem, bytes) != hipSuccess) {
       p->dmem = nullptr;
       release(p);
@@ -287,12 +375,17 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->unpack = carve<CopyChunk>(cur, p->n_unpack);
     p->pack = carve<PackChunk>(cur, p->n_pack);
     p->qjobs = carve<QJob>(cur, p->n_qjobs);
+    p->gchunks = carve<GatherChunk>(cur, p->n_gchunks);
+    p->gjobs = carve<QJob>(cur, p->n_gtile + p->n_gflat);
     void** dst_dev = carve<void*>(cur, n);
     void** src_dev = carve<void*>(cur, n);
+    void** gdst_dev = carve<void*>(cur, n);
 
     bool ok = hipMemcpy(p->unpack, tb.unpack.data(), sizeof(CopyChunk) * p->n_unpack, hipMemcpyHostToDevice) == hipSuccess &&
               hipMemcpy(p->pack, tb.pack.data(), sizeof(PackChunk) * p->n_pack, hipMemcpyHostToDevice) == hipSuccess &&
-              (p->n_qjobs == 0 || hipMemcpy(p->qjobs, tb.qjobs.data(), sizeof(QJob) * p->n_qjobs, hipMemcpyHostToDevice) == hipSuccess);
+              (p->n_qjobs == 0 || hipMemcpy(p->qjobs, tb.qjobs.data(), sizeof(QJob) * p->n_qjobs, hipMemcpyHostToDevice) == hipSuccess) &&
+              (p->n_gchunks == 0 || hipMemcpy(p->gchunks, tb.gchunks.data(), sizeof(GatherChunk) * p->n_gchunks, hipMemcpyHostToDevice) == hipSuccess) &&
+              (tb.gjobs.empty() || hipMemcpy(p->gjobs, tb.gjobs.data(), sizeof(QJob) * tb.gjobs.size(), hipMemcpyHostToDevice) == hipSuccess);
     if (!ok) {
       release(p);
       (void)hipSetDevice(prev);
@@ -300,6 +393,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     }
     st = init_table(&p->dst, dst_dev, n);
     if (st == RS_OK) st = init_table(&p->src, src_dev, n);
+    if (st == RS_OK) st = init_table(&p->gdst, gdst_dev, n);
     if (st != RS_OK) {
       std::string msg = rs_last_error();
       release(p);

@@ -56,10 +56,12 @@ bool spec_ok(const rs_tensor_spec& s, std::string* why) {
       break;
     case RS_FLAT:
       if (s.p0 < 1 || s.p1 != 0) return bad("FLAT needs p0 >= 1 elements and p1 = 0");
+      if (s.p0 > (int64_t(1) << 24)) return bad("flat block larger than 2^24 elements");
       break;
     case RS_TILE:
       if (s.p0 < 1 || s.p1 < 1) return bad("TILE needs p0, p1 >= 1");
-      if (s.p0 > (int64_t(1) << 20) || s.p1 > (int64_t(1) << 20)) return bad("tile too large");
+      if (s.p0 > (int64_t(1) << 24) || s.p1 > (int64_t(1) << 24) || s.p0 * s.p1 > (int64_t(1) << 24))
+        return bad("tile larger than 2^24 elements");
       break;
     default:
       return bad("unknown block kind");

@@ -64,15 +64,44 @@ enum QJobKind : int32_t { QJOB_TILE = 0, QJOB_FLAT = 1, QJOB_ZERO = 2 };
 //   FLAT: `rows` (1..kFlatPerGroup) consecutive flat blocks of `cols` elements
 //         from base; the last one has `last` elements. Scales scale..scale+rows-1.
 //   ZERO: elements [base, base + stride) lie in no block (codes 0, values +0.0).
+// TILE and FLAT jobs also name their tensor and the offset of `base` inside
+// it (base - s_tensor), for kernels that write the full tensors.
 struct QJob {
   int64_t base;
   int64_t stride;
   int64_t scale;
+  int64_t toff;
   int32_t rows;
   int32_t cols;
   int32_t kind;
   int32_t last;
+  int32_t tensor;
+  int32_t unused;
 };
+
+// Gather-side work item: a contiguous run of whole rows of one quantised
+// tensor, inside one band of tiles (TILE) or made of whole flat blocks (FLAT,
+// a "row" being one block). Element (r, c) of the run sits at r*cols + c and
+// its scale is scales[scale0 + r*rstep + c/bc]. Only tensors whose rows and
+// tile widths are multiples of 16 elements (TILE: at most kGatherMaxCols
+// columns) or whose flat blocks are, use these.
+struct GatherChunk {
+  int64_t qbase;   // flat position of the first element
+  int64_t toff;    // the same element's offset inside the tensor
+  int64_t scale0;
+  int32_t rows;
+  int32_t cols;    // a multiple of 8
+  int32_t bc;      // width sharing one scale: tile columns, or the flat block
+  int32_t rstep;   // 0: every row of the run shares the band's scales; 1: one block per row
+  int32_t tensor;
+  int32_t unused;
+};
+
+#ifndef RS_GATHER_CHUNK
+#define RS_GATHER_CHUNK 16384
+#endif
+constexpr int64_t kGatherChunk = RS_GATHER_CHUNK;   // target elements per gather work item
+constexpr int64_t kGatherMaxCols = 16384;           // widest TILE tensor handled as row runs
 
 // Device copy of a per-tensor pointer table plus the host state that decides
 // when it must be uploaded again.
@@ -111,7 +140,13 @@ struct rs_plan {
   int64_t n_qblocks = 0;
   int32_t max_tile_vec16 = 0;  // largest tile, in 16-byte vectors of 4-byte input
 
-  rs::PtrTable dst;  // unpack destinations
-  rs::PtrTable src;  // pack sources
+  rs::GatherChunk* gchunks = nullptr;  // gather side, vector-friendly tensors
+  int64_t n_gchunks = 0;
+  rs::QJob* gjobs = nullptr;           // gather side, other tensors: tile jobs, then flat groups
+  int64_t n_gtile = 0, n_gflat = 0;
+
+  rs::PtrTable dst;   // unpack destinations
+  rs::PtrTable src;   // pack sources
+  rs::PtrTable gdst;  // unpack-dequant destinations
   bool e4m3_hw = false;  // use gfx950's FP8 conversion instructions
 };

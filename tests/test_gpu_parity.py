@@ -113,6 +113,17 @@ def _full_check(rs, specs, V, pdtype, seed, fmts=("e4m3", "i8", "u8"), R_mat=Non
         wd = OT.block_dequant(wq, ws, specs, plan.starts, S, R, fmt)
         assert np.array_equal(tensor_bits(out), wd.view(np.uint32)), fmt
         assert guard_intact(owhole, total)
+        # gather side: gathered codes + scales -> the quantised full tensors
+        for out_dt, tag in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+            quantised = [sp.kind in ("TILE", "FLAT") for sp in specs]
+            dsts = [garbage(sp.rows * sp.cols, out_dt, DEV).view(sp.rows, sp.cols) if qz else None
+                    for sp, qz in zip(specs, quantised)]
+            rs.rs_unpack_dequant(plan, q, fmt, scales, dsts)
+            want = OT.unpack_dequant(wq, ws, specs, plan.starts, fmt, tag)
+            for d, wv in zip(dsts, want):
+                assert (d is None) == (wv is None)
+                if d is not None:
+                    assert np.array_equal(tensor_bits(d), wv.view(np.uint32) if tag == "f32" else wv), (fmt, tag)
     plan.close()
 
 

@@ -63,11 +63,15 @@ def test_param_and_grad_workloads(gpu_lib, idx):
     print("  grads and prev uploaded", flush=True)
     packed = garbage(R * S, torch.float32, DEV)
     rs.rs_pack_scatter(plan, grads, packed, prev=prev)
-    q = scales = None
+    q = scales = gathered = None
     if w.quant:
         q = garbage(R * S, torch.uint8, DEV, 0x3C)
         scales = garbage(plan.n_qblocks, torch.float32, DEV)
         rs.rs_block_quant(plan, G, q, w.quant, scales)
+        # gather side: the codes and scales rebuild the quantised bf16 tensors
+        gathered = [garbage(sp.rows * sp.cols, torch.bfloat16, DEV) if sp.kind in ("TILE", "FLAT") else None
+                    for sp in specs]
+        rs.rs_unpack_dequant(plan, q, w.quant, scales, gathered)
     torch.cuda.synchronize()
 
     print("  kernels done; checking against the oracle", flush=True)
@@ -93,10 +97,13 @@ def test_param_and_grad_workloads(gpu_lib, idx):
             s, n = plan.starts[i], plan.numels[i]
             x = _tensor_param_f32(inp, i)
             got_q = tensor_bits(q[s: s + n])
+            got_g = tensor_bits(gathered[i]) if gathered[i] is not None else None
             for _, b, pos in OT.quant_blocks([specs[i]], [0]):
                 c, sc = OT.quantize_block(x[pos], w.quant)
                 assert np.array_equal(got_q[pos], c), f"quant {i} block {b}"
                 assert sc_bits[first[i] + b] == np.float32(sc).view(np.uint32), f"scale {i} block {b}"
+                want_g = OT.bf16_round(OT.dequant_values(c, sc, w.quant))
+                assert np.array_equal(got_g[pos], want_g), f"unpack-dequant {i} block {b}"
         _zero_everywhere(q, OP.padding_ranges([sp for sp in specs if sp.kind in ("TILE", "FLAT")],
                                               [st for sp, st in zip(specs, plan.starts)
                                                if sp.kind in ("TILE", "FLAT")], S, R))

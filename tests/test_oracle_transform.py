@@ -208,3 +208,55 @@ def test_pack_pin_catches_add_before_scale(monkeypatch):
     monkeypatch.setattr(T, "pack_values", wrong)
     with pytest.raises(AssertionError):
         test_pack_values_exact(3, True)
+
+
+def test_bf16_round_matches_torch_and_hand_cases():
+    import torch
+    rng = np.random.default_rng(31)
+    x = np.concatenate([
+        (rng.standard_normal(200_000) * 10.0 ** rng.integers(-30, 30, 200_000)).astype(np.float32),
+        # exact ties: low 16 bits 0x8000, with even and odd kept lsb
+        (np.arange(1000, dtype=np.uint32) * np.uint32(0x10000) + np.uint32(0x3F808000)).view(np.float32),
+        np.float32([0.0, -0.0, 1e-40, -1e-40, 3.3895314e38]),
+    ])
+    got = T.bf16_round(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to the even mantissa (1.0)
+    assert T.bf16_round(np.float32([1 + 2 ** -8]))[0] == 0x3F80
+    assert T.bf16_round(np.float32([1 + 3 * 2 ** -8]))[0] == 0x3F82
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8", "u8"])
+def test_unpack_dequant_round_trips_values_on_the_code_grid(fmt):
+    """Blocks whose values are code values times a power-of-two scale with amax exactly Q*2^k
+    come back exactly (in fp32 and, being short-mantissa values, in bf16)."""
+    specs = [TensorSpec("a", 48, 40, "TILE", 16, 8), TensorSpec("n", 9, 1, "ROWS", 1),
+             TensorSpec("f", 1, 700, "FLAT", 256)]
+    V = 3
+    p = P.plan(specs, V)
+    rng = np.random.default_rng(4)
+    Q = codes.FORMAT_QMAX[fmt]
+    src = np.zeros(V * p.S, dtype=np.float32)
+    if fmt == "e4m3":
+        grid = codes.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    elif fmt == "i8":
+        grid = np.arange(-127, 128, dtype=np.float64)
+    else:
+        grid = np.arange(0, 256, dtype=np.float64)
+    for _, b, pos in T.quant_blocks(specs, p.starts):
+        k = int(rng.integers(-8, 8))
+        v = rng.choice(grid, pos.size) * 2.0 ** k
+        if fmt == "e4m3":
+            v *= rng.choice([-1.0, 1.0], pos.size)
+        v[0] = Q * 2.0 ** k
+        src[pos] = v
+    q, sc = T.block_quant(src, specs, p.starts, p.S, V, fmt)
+    for out in ("f32", "bf16"):
+        full = T.unpack_dequant(q, sc, specs, p.starts, fmt, out)
+        assert full[1] is None
+        for i in (0, 2):
+            s, n = int(p.starts[i]), specs[i].rows * specs[i].cols
+            want = src[s: s + n].reshape(specs[i].rows, specs[i].cols)
+            got = full[i] if out == "f32" else (full[i].astype(np.uint32) << 16).view(np.float32)
+            assert np.array_equal(got, want)
