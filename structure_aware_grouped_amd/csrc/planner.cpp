@@ -14,16 +14,22 @@
 //     at the first valid start after the previous one (the DP's state f(i, j)
 //     only grows with j, and a tensor's constraint depends on its own start
 //     alone, so first-fit reaches every state's minimum);
-//   * candidate S values start at the lower bound and step by the alignment;
+//   * candidate S values start at the lower bound and step by the alignment
+//     (an order after the first stops at the best S found so far); after a
+//     short sequential start, candidates are checked in batches on host
+//     threads and the smallest feasible one is kept, which gives the same S
+//     as a sequential scan;
 //     a tensor longer than 2S always holds two boundaries, so S must then be a
 //     multiple of its g (the pages' case of a tensor that fully contains a
 //     shard): such S values are skipped in one jump. The pages binary-search
 //     over aligned candidates; feasibility is not monotone there in general,
 //     so this planner scans upward and returns the exact smallest S per order.
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <numeric>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "rs_internal.h"
@@ -112,11 +118,17 @@ int64_t first_fit(int64_t e, const Item& it, int64_t S, int64_t a, int64_t cap) 
   }
 }
 
-bool place(const std::vector<Item>& items, const std::vector<int>& order, int64_t S, int64_t V,
-           int64_t a, std::vector<int64_t>* starts, int64_t* end) {
+// First fit of every tensor in `order`; false as soon as the tensors still to
+// place cannot fit after the current end even without padding (`rest[k]` is
+// the total size of order[k..]).
+bool place(const std::vector<Item>& items, const std::vector<int>& order,
+           const std::vector<int64_t>& rest, int64_t S, int64_t V, int64_t a,
+           std::vector<int64_t>* starts, int64_t* end) {
   const int64_t cap = V * S;
   int64_t e = 0;
-  for (int i : order) {
+  for (size_t k = 0; k < order.size(); ++k) {
+    if (e > cap - rest[k]) return false;
+    const int i = order[k];
     const int64_t s = first_fit(e, items[i], S, a, cap);
     if (s < 0) return false;
     if (starts) (*starts)[i] = s;
@@ -124,6 +136,80 @@ bool place(const std::vector<Item>& items, const std::vector<int>& order, int64_
   }
   if (end) *end = e;
   return true;
+}
+
+// Candidate shard sizes in increasing order: multiples of the alignment from
+// the lower bound, skipping every S that a tensor longer than 2S forces to be
+// a multiple of its g (by_n: tensors by size, largest first; prefix_lcm[p]:
+// lcm of the alignment and the g of the first p of them).
+struct Candidates {
+  const std::vector<Item>* items;
+  const std::vector<int>* by_n;
+  const std::vector<int64_t>* prefix_lcm;
+  int64_t align, s_max;
+
+  // smallest admissible candidate >= S
+  int64_t next(int64_t S) const {
+    const int64_t n = static_cast<int64_t>(by_n->size());
+    for (;;) {
+      int64_t p = 0;
+      while (p < n && (*items)[(*by_n)[p]].n > 2 * S) ++p;
+      const int64_t A = (*prefix_lcm)[p];
+      if (S % A == 0) return S;
+      // the next multiple of A, or where the smallest forced tensor stops being
+      // forced, whichever comes first
+      const int64_t to_a = A <= s_max ? align_up(S, A) : s_max + align;
+      const int64_t release = align_up(((*items)[(*by_n)[p - 1]].n + 1) / 2, align);
+      S = std::max(S + align, std::min(to_a, release));
+    }
+  }
+};
+
+// Smallest feasible candidate in [from, bound] for one order, or -1.
+int64_t scan(const std::vector<Item>& items, const std::vector<int>& order,
+             const std::vector<int64_t>& rest, const Candidates& cand, int64_t from, int64_t bound,
+             int64_t V) {
+  const int64_t a = cand.align;
+  int64_t S = from;
+  for (int k = 0; k < 64; ++k) {  // most groups are settled by the first few candidates
+    S = cand.next(S);
+    if (S > bound) return -1;
+    if (place(items, order, rest, S, V, a, nullptr, nullptr)) return S;
+    S += a;
+  }
+  const unsigned hw = std::thread::hardware_concurrency();
+  const int T = static_cast<int>(std::max(1u, std::min(16u, hw)));
+  int64_t batch = 256;
+  while (S <= bound) {
+    std::vector<int64_t> list;
+    list.reserve(batch);
+    while (static_cast<int64_t>(list.size()) < batch) {
+      S = cand.next(S);
+      if (S > bound) break;
+      list.push_back(S);
+      S += a;
+    }
+    if (list.empty()) return -1;
+    std::atomic<int64_t> first(static_cast<int64_t>(list.size()));
+    auto work = [&](int t) {
+      for (int64_t i = t; i < static_cast<int64_t>(list.size()); i += T) {
+        if (i > first.load(std::memory_order_relaxed)) break;
+        if (place(items, order, rest, list[i], V, a, nullptr, nullptr)) {
+          int64_t cur = first.load();
+          while (i < cur && !first.compare_exchange_weak(cur, i)) {
+          }
+          break;
+        }
+      }
+    };
+    std::vector<std::thread> pool;
+    for (int t = 1; t < T; ++t) pool.emplace_back(work, t);
+    work(0);
+    for (auto& th : pool) th.join();
+    if (first.load() < static_cast<int64_t>(list.size())) return list[first.load()];
+    batch = std::min<int64_t>(batch * 4, 1 << 16);
+  }
+  return -1;
 }
 
 }  // namespace
@@ -192,29 +278,22 @@ extern "C" int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, 
       orders.push_back(by_shape);
     }
 
+    const Candidates cand{&items, &by_n, &prefix_lcm, align, s_max};
     int64_t best_S = -1, best_end = -1;
     int best_o = -1;
     std::vector<int64_t> starts(n), best_starts(n);
     for (size_t o = 0; o < orders.size(); ++o) {
-      int64_t S = LB;
-      int64_t end = 0;
-      for (;;) {
-        if (S > s_max) return fail(RS_EPLAN, "rs_plan_build: internal error, no feasible S");
-        // tensors longer than 2S: the first p of by_n
-        int64_t p = 0;
-        while (p < n && items[by_n[p]].n > 2 * S) ++p;
-        const int64_t A = prefix_lcm[p];
-        if (S % A != 0) {
-          // jump to the next multiple of A, or to where the smallest forced
-          // tensor stops being forced, whichever comes first
-          int64_t next = A <= s_max ? align_up(S, A) : s_max + align;
-          const int64_t release = align_up((items[by_n[p - 1]].n + 1) / 2, align);
-          S = std::max(S + align, std::min(next, release));
-          continue;
-        }
-        if (place(items, orders[o], S, V, align, &starts, &end)) break;
-        S += align;
+      std::vector<int64_t> rest(n + 1, 0);
+      for (int64_t k = n - 1; k >= 0; --k) rest[k] = rest[k + 1] + items[orders[o][k]].n;
+      // an order can only win with an S no larger than the best one so far
+      const int64_t bound = best_o < 0 ? s_max : best_S;
+      const int64_t S = scan(items, orders[o], rest, cand, LB, bound, V);
+      if (S < 0) {
+        if (best_o < 0) return fail(RS_EPLAN, "rs_plan_build: internal error, no feasible S");
+        continue;
       }
+      int64_t end = 0;
+      place(items, orders[o], rest, S, V, align, &starts, &end);
       if (best_o < 0 || S < best_S || (S == best_S && end < best_end)) {
         best_S = S;
         best_end = end;
