@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
-    ap.add_argument("--mode", default="step", choices=["step", "fp8_gather"],
+    ap.add_argument("--mode", default="step", choices=["step", "fp8_gather", "adam8"],
                     help="step: the workload's steps; fp8_gather: block quant of the rank slices, then "
-                         "the fused unpack-dequant of the codes into the bf16 tensors")
+                         "the fused unpack-dequant of the codes into the bf16 tensors; adam8 (workload 4): "
+                         "one AdamW step on the int8/uint8 block-quantised m and v")
     ap.add_argument("--cpu-sample", type=int, default=1, help="0 disables the CPU-oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
     ap.add_argument("--copy-mib", type=int, default=1024,
@@ -65,6 +66,8 @@ def algorithmic_bytes(w, plan) -> dict:
     out = {}
     nq_all = sum(n for sp, n in zip(w.specs, plan.numels) if sp.kind in ("TILE", "FLAT"))
     out["unpack_dequant"] = nq_all * (1 + pb) + 4 * plan.n_qblocks
+    # param read + write, grad read, m and v codes read + write (fp32 param/grad); 2 scales read + write
+    out["adam8_step"] = nq_all * (4 + 4 + 4 + 2 + 2) + 16 * plan.n_qblocks
     if w.adam_states:
         nq = sum(n for sp, n in zip(w.specs, plan.numels) if sp.kind in ("TILE", "FLAT"))
         pack = n_all * (4 + 4) + 4 * plan.padding
@@ -153,7 +156,7 @@ def main():
     import torch
     import structure_aware_grouped_amd as rs
     from tests.gpu_util import Inputs, garbage, tensor_bits
-    from workloads import workload
+    from workloads import Role, tensor_values, workload
 
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
@@ -173,7 +176,34 @@ def main():
     avg_load = -(-sum(plan.numels) // w.V)
 
     # ---- inputs resident in HBM
-    if w.adam_states:
+    if args.mode == "adam8":
+        if not w.adam_states:
+            print("adam8 needs the Adam-state workload (4)", file=sys.stderr)
+            sys.exit(2)
+        flat = lambda: garbage(R * S, torch.float32, dev)
+        param, grad, mbuf, vbuf = flat(), flat(), flat(), flat()
+        weights = [torch.from_numpy(tensor_values(w, i, Role.WEIGHT)).to(dev) for i in range(len(specs))]
+        rs.rs_pack_scatter(plan, weights, param, scale=1.0)
+        del weights
+        rs.rs_pack_scatter(plan, inp.grads(), grad, scale=1.0)
+        rs.rs_pack_scatter(plan, inp.adam_states("m"), mbuf, scale=1.0)
+        rs.rs_pack_scatter(plan, inp.adam_states("v"), vbuf, scale=1.0)
+        qm = garbage(R * S, torch.uint8, dev)
+        qv = garbage(R * S, torch.uint8, dev)
+        sm = garbage(plan.n_qblocks, torch.float32, dev)
+        sv = garbage(plan.n_qblocks, torch.float32, dev)
+        rs.rs_block_quant(plan, mbuf, qm, "i8", sm)
+        rs.rs_block_quant(plan, vbuf, qv, "u8", sv)
+        del mbuf, vbuf
+        counter = {"t": 0}
+
+        def adam_step():
+            counter["t"] += 1
+            rs.rs_adam8_step(plan, param, grad, qm, sm, qv, sv, 1e-4, 0.9, 0.999, 1e-8, 0.01, counter["t"])
+
+        steps = [("adam8_step", adam_step)]
+        dominant = "adam8_step"
+    elif w.adam_states:
         m = inp.adam_states("m")
         v = inp.adam_states("v")
         pm = garbage(R * S, torch.float32, dev)
@@ -310,6 +340,8 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant])}
 
+    if not args.no_check and args.mode == "adam8":
+        check = "skipped (the Adam step is checked by tests/test_gpu_adam.py)"
     cpu = None
     if args.cpu_sample and not w.adam_states and args.mode == "step":
         cpu = cpu_baseline(w, plan)
@@ -322,6 +354,9 @@ def main():
     if args.mode == "fp8_gather":
         names = {k: v.split(":")[0] + ": e4m3 quant of the rank slices + fused unpack-dequant to bf16"
                  for k, v in names.items()}
+    if args.mode == "adam8":
+        names[4] = ("8-bit Adam states on the Llama-3-8B layer shapes, 2048-element blocks, V=64: one fused "
+                    "AdamW step (dequant m, v; update fp32 params; requant m int8, v uint8)")
     metric = METRIC if (args.workload == 1 and args.mode == "step") else \
         f"DBuffer layout transform GB/s (workload {args.workload}, {args.mode})"
     line = {

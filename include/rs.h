@@ -19,6 +19,7 @@
  *   rs_block_quant      per-block absmax 8-bit quantisation of the flat buffer
  *   rs_block_dequant    the inverse of rs_block_quant
  *   rs_unpack_dequant   gathered codes + scales -> the quantised full tensors
+ *   rs_adam8_step       one AdamW step on block-quantised int8 / uint8 state
  *   rs_last_error       text of the calling thread's last error
  *
  * Conventions
@@ -224,6 +225,42 @@ int rs_block_dequant(rs_plan* plan, const void* q, int32_t q_dt, const float* sc
  * give unspecified values. Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */
 int rs_unpack_dequant(rs_plan* plan, const void* q, int32_t q_dt, const float* scales,
                       void* const* dst, int32_t dst_dt, void* stream);
+
+/* Hyper-parameters of one Adam step; step counts from 1. */
+typedef struct rs_adam_hparams {
+  float lr;
+  float beta1;         /* in [0, 1) */
+  float beta2;         /* in [0, 1) */
+  float eps;           /* >= 0 */
+  float weight_decay;  /* decoupled (AdamW); 0 for plain Adam */
+  int32_t reserved;    /* must be 0 */
+  int64_t step;        /* >= 1 */
+} rs_adam_hparams;
+
+/* One 8-bit Adam step on every quantisation block of the plan, in place
+ * (feynmanwiki walkthrough, 8-bit Adam paragraph: optimizer state quantised
+ * in blocks that stay whole on their device, so each device updates and
+ * requantises its own blocks with no scale exchange). The pages give no
+ * update formula; this is AdamW. Host scalars, computed in double from the
+ * fp32 hyper-parameters and rounded once to fp32:
+ *   c1 = 1 - b1, c2 = 1 - b2, step_size = lr / (1 - b1^t),
+ *   inv_bc2_sqrt = 1 / sqrt(1 - b2^t), decay = 1 - lr*wd.
+ * Per element of a block B, each operation one fp32 round-to-nearest-even
+ * step (no fused multiply-add):
+ *   m0 = dec_i8(q_m) * s_m[B]        v0 = dec_u8(q_v) * s_v[B]
+ *   m1 = b1*m0 + c1*g                v1 = b2*v0 + c2*(g*g)
+ *   den = sqrt(v1)*inv_bc2_sqrt + eps
+ *   param = param*decay - step_size*(m1/den)
+ * then m1 and v1 are requantised per block exactly as rs_block_quant does
+ * (int8 and uint8). Positions outside quantisation blocks are not touched.
+ * param: device fp32 R_mat*S (in place); grad: device fp32 R_mat*S (the
+ * packed gradient, e.g. from rs_pack_scatter); q_m / q_v: device int8 / uint8
+ * codes, R_mat*S bytes, in place; s_m / s_v: device fp32 [n_qblocks], in
+ * place. All 16-byte aligned. hp: host pointer.
+ * Errors: RS_EINVAL (null, step < 1, beta outside [0,1), eps < 0, non-finite
+ * lr / wd), RS_EALIGN, RS_EHIP. */
+int rs_adam8_step(rs_plan* plan, float* param, const float* grad, void* q_m, float* s_m,
+                  void* q_v, float* s_v, const rs_adam_hparams* hp, void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). The
  * pointer stays valid until the thread's next rs_* call. */

@@ -22,6 +22,6 @@ Parity status: every function here is pinned by a CPU test except the
 planner's choice among the valid plans beyond the 2x bound ("parity unpinned"
 for optimality; validity and the bound are pinned).
 """
-from . import codes, plan, transform
+from . import adam, codes, plan, transform
 
-__all__ = ["codes", "plan", "transform"]
+__all__ = ["adam", "codes", "plan", "transform"]

@@ -5,6 +5,7 @@ include/rs.h); ``binding`` exposes its calls under the same names.
 """
 from .binding import (  # noqa: F401
     Plan,
+    rs_adam8_step,
     RsError,
     load,
     rs_block_dequant,

@@ -25,13 +25,20 @@ ORDER_KINDS = {0: "default", 1: "by_block_size", 2: "by_shape"}
 RS_F32, RS_BF16, RS_E4M3, RS_I8, RS_U8 = 0, 1, 2, 3, 4
 CODE_FORMATS = {"e4m3": RS_E4M3, "i8": RS_I8, "u8": RS_U8}
 EXPORTS = ("rs_plan_build", "rs_plan_load", "rs_plan_info", "rs_plan_free", "rs_unpack_gathered",
-           "rs_pack_scatter", "rs_block_quant", "rs_block_dequant", "rs_unpack_dequant", "rs_last_error")
+           "rs_pack_scatter", "rs_block_quant", "rs_block_dequant", "rs_unpack_dequant", "rs_adam8_step",
+           "rs_last_error")
 
 
 class RsError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
         self.status = status
+
+
+class AdamHParamsC(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("step", ctypes.c_int64)]
 
 
 class TensorSpecC(ctypes.Structure):
@@ -65,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rs_block_quant.argtypes = [P, P, I32, P, I32, P, P]
     lib.rs_block_dequant.argtypes = [P, P, I32, P, P, P]
     lib.rs_unpack_dequant.argtypes = [P, P, I32, P, ctypes.POINTER(P), I32, P]
+    lib.rs_adam8_step.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(AdamHParamsC), P]
     lib.rs_last_error.argtypes = []
     lib.rs_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -253,3 +261,22 @@ def rs_unpack_dequant(plan: Plan, q: torch.Tensor, fmt: str, scales: torch.Tenso
     ptrs = (ctypes.c_void_p * len(dsts))(*[d.data_ptr() if d is not None else None for d in dsts])
     _check(load().rs_unpack_dequant(plan.handle, q.data_ptr(), CODE_FORMATS[fmt], scales.data_ptr(), ptrs,
                                     RS_BF16 if dt == torch.bfloat16 else RS_F32, _stream(plan.device)))
+
+
+def rs_adam8_step(plan: Plan, param: torch.Tensor, grad: torch.Tensor, q_m: torch.Tensor,
+                  s_m: torch.Tensor, q_v: torch.Tensor, s_v: torch.Tensor, lr: float, beta1: float,
+                  beta2: float, eps: float, weight_decay: float, step: int):
+    """One AdamW step on every quantisation block, in place: param (fp32 flat), int8 m codes and
+    scales, uint8 v codes and scales; grad is the packed fp32 gradient."""
+    _dev_check(plan, param, grad, q_m, s_m, q_v, s_v)
+    total = plan.R_mat * plan.S
+    for t, dt in ((param, torch.float32), (grad, torch.float32), (s_m, torch.float32), (s_v, torch.float32)):
+        if t.dtype != dt:
+            raise ValueError("param, grad and scales are fp32")
+    if param.numel() < total or grad.numel() < total or q_m.numel() < total or q_v.numel() < total:
+        raise ValueError("buffers shorter than R_mat * S")
+    if s_m.numel() < plan.n_qblocks or s_v.numel() < plan.n_qblocks:
+        raise ValueError("scales shorter than n_qblocks")
+    hp = AdamHParamsC(lr, beta1, beta2, eps, weight_decay, 0, int(step))
+    _check(load().rs_adam8_step(plan.handle, param.data_ptr(), grad.data_ptr(), q_m.data_ptr(), s_m.data_ptr(),
+                                q_v.data_ptr(), s_v.data_ptr(), ctypes.byref(hp), _stream(plan.device)))

@@ -86,3 +86,29 @@ def int_nearest(y: float, lo: int, hi: int) -> int:
     rem = a - fl
     r = fl + 1 if (rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1)) else fl
     return max(lo, min(hi, r))
+
+
+def sqrt_f32(x: float) -> float:
+    """Correctly rounded binary32 square root of a non-negative binary32 value, by exact
+    comparison of squares (nearest, ties to even)."""
+    a = Fraction(x)
+    if a == 0:
+        return x
+    import math
+    import numpy as _np
+    y0 = _np.float32(math.sqrt(float(a)))
+    cands = [y0]
+    for _ in range(3):
+        cands.append(_np.nextafter(cands[-1], _np.float32(_np.inf)))
+        cands.insert(0, _np.nextafter(cands[0], _np.float32(0)))
+    cands = [Fraction(float(c)) for c in cands]
+    for lo, hi in zip(cands, cands[1:]):
+        if lo * lo <= a <= hi * hi:
+            mid = (lo + hi) / 2
+            if a < mid * mid:
+                return float(lo)
+            if a > mid * mid:
+                return float(hi)
+            lo_bits = f32_bits(float(lo))
+            return float(lo) if lo_bits % 2 == 0 else float(hi)
+    raise AssertionError("sqrt bracket not found")
