@@ -14,8 +14,10 @@ Readings where the pages are silent or garbled (each is listed in the design
 notes):
   * g_i per block kind: ELEM 1, ROWS(k) k*cols, TILE(br, bc) br*cols (a tile
     of a row-major tensor stays whole only when cuts fall on br-row bands),
-    FLAT(b) b, WHOLE n_i. The block count is ceil(n_i / g_i); the last block
-    may be partial.
+    FLAT(b) b, WHOLE n_i, TILEMAJOR(br, bc) br*bc (the tensor is stored tile
+    by tile, each tile contiguous, so a cut may fall between any two tiles;
+    the tiles must cover the tensor exactly). The block count is
+    ceil(n_i / g_i); the last block may be partial.
   * Alignment: S and every s_i are multiples of a "collective-preferred"
     alignment a (16 elements here, a parameter).
   * Orders ([walk], "the planner first fixes a tensor order"; [summary],
@@ -67,7 +69,24 @@ def granularity(spec) -> int:
         return int(spec.p0)
     if k == "WHOLE":
         return n
+    if k == "TILEMAJOR":
+        return int(spec.p0) * int(spec.p1)
     raise ValueError(f"unknown block kind {k!r}")
+
+
+def layout_offsets(spec) -> np.ndarray:
+    """Offset inside the tensor's interval of each element, in row-major element order.
+
+    Row-major for every kind but TILEMAJOR, whose element (r, c) lives in tile
+    (r // br, c // bc), tiles in row-major order, each tile row-major inside."""
+    r, c = int(spec.rows), int(spec.cols)
+    if spec.kind != "TILEMAJOR":
+        return np.arange(r * c, dtype=np.int64)
+    br, bc = int(spec.p0), int(spec.p1)
+    rr = np.arange(r, dtype=np.int64)[:, None]
+    cc = np.arange(c, dtype=np.int64)[None, :]
+    tile = (rr // br) * (c // bc) + cc // bc
+    return (tile * (br * bc) + (rr % br) * bc + cc % bc).ravel()
 
 
 def atomic_blocks(spec) -> List[tuple]:

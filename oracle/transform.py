@@ -18,8 +18,14 @@ Readings (listed in the design notes):
   * Quantisation blocks ([walk], "every quantization block should ideally
     live entirely on one device"; the 8-bit Adam paragraph's 32x32 blocks at
     32-row granularity): TILE tensors are cut into br x bc tiles of the
-    row-major tensor (partial at the right and bottom edges); FLAT tensors
-    into their b-element blocks. Other kinds are not quantised.
+    row-major tensor (partial at the right and bottom edges); TILEMAJOR
+    tensors into their tiles (contiguous in the buffer); FLAT tensors into
+    their b-element blocks. Other kinds are not quantised.
+  * Layouts: a tensor occupies [s_i, s_i + n_i); element (r, c) sits at
+    s_i + r*cols + c, except for TILEMAJOR tensors, stored tile by tile
+    (tile-row-major, each tile row-major inside). Unpack and pack apply that
+    reordering ([walk], RaggedShard paragraphs: 2-D blocks distributed
+    asymmetrically across devices).
   * Per block: amax = max |x| (exact). If amax > 0 the stored scale is
     fl32(amax / Q) and values are multiplied by r = min(fl32(Q / amax),
     FLT_MAX) before encoding (one correctly rounded division per block; the
@@ -43,7 +49,7 @@ from typing import Iterator, List, Sequence, Tuple
 import numpy as np
 
 from . import codes
-from .plan import numel, padding_ranges
+from .plan import layout_offsets, numel, padding_ranges
 
 FLT_MAX = float(np.finfo(np.float32).max)
 
@@ -61,11 +67,11 @@ def inv_v(V: int) -> np.float32:
 # ---------------------------------------------------------------- unpack
 
 def unpack(G: np.ndarray, specs, starts) -> List[np.ndarray]:
-    """Full tensors from the gathered flat buffer: T_i[e] = G[s_i + e] (any dtype, bitwise)."""
+    """Full tensors from the gathered flat buffer: T_i[e] = G[s_i + L_i(e)] (any dtype,
+    bitwise), L_i the tensor's layout (identity, or tile-major for TILEMAJOR)."""
     out = []
     for spec, s in zip(specs, starts):
-        n = numel(spec)
-        out.append(np.array(G[int(s): int(s) + n]).reshape(spec.rows, spec.cols))
+        out.append(np.array(G[int(s) + layout_offsets(spec)]).reshape(spec.rows, spec.cols))
     return out
 
 
@@ -84,9 +90,9 @@ def pack(grads: Sequence[np.ndarray], prev, specs, starts, S: int, R_mat: int,
     """Packed flat fp32 buffer of R_mat*S values; padding is +0.0."""
     out = np.zeros(R_mat * S, dtype=np.float32)
     for g, spec, s in zip(grads, specs, starts):
-        s, n = int(s), numel(spec)
-        p = prev[s: s + n] if accumulate else None
-        out[s: s + n] = pack_values(np.ravel(g), p, sigma, accumulate)
+        pos = int(s) + layout_offsets(spec)
+        p = prev[pos] if accumulate else None
+        out[pos] = pack_values(np.ravel(g), p, sigma, accumulate)
     return out
 
 
@@ -111,12 +117,17 @@ def quant_blocks(specs, starts) -> Iterator[Tuple[int, int, np.ndarray]]:
             for e0 in range(0, n, b):
                 yield i, q, s + np.arange(e0, min(e0 + b, n), dtype=np.int64)
                 q += 1
+        elif spec.kind == "TILEMAJOR":   # whole tiles, each contiguous, tile-row-major
+            tsz = int(spec.p0) * int(spec.p1)
+            for t in range(numel(spec) // tsz):
+                yield i, q, s + t * tsz + np.arange(tsz, dtype=np.int64)
+                q += 1
 
 
 def count_quant_blocks(specs) -> int:
     total = 0
     for spec in specs:
-        if spec.kind == "TILE":
+        if spec.kind in ("TILE", "TILEMAJOR"):
             total += (-(-int(spec.rows) // int(spec.p0))) * (-(-int(spec.cols) // int(spec.p1)))
         elif spec.kind == "FLAT":
             total += -(-numel(spec) // int(spec.p0))
@@ -189,6 +200,8 @@ def unpack_dequant(q: np.ndarray, scales, specs, starts, fmt: str, out: str):
     for i, b, pos in quant_blocks(specs, starts):
         v = dequant_values(q[pos], scales[b], fmt)
         full.setdefault(i, np.zeros(numel(specs[i]), dtype=np.float32))[pos - int(starts[i])] = v
+    for i in full:   # interval order -> row-major order
+        full[i] = full[i][layout_offsets(specs[i])]
     res = []
     for i, spec in enumerate(specs):
         if i not in full:

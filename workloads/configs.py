@@ -21,9 +21,9 @@ class TensorSpec:
     name: str
     rows: int
     cols: int
-    kind: str          # "ELEM" | "ROWS" | "TILE" | "FLAT" | "WHOLE"
-    p0: int = 0        # ROWS: rows per block; TILE: block rows; FLAT: block elements
-    p1: int = 0        # TILE: block columns
+    kind: str          # "ELEM" | "ROWS" | "TILE" | "FLAT" | "WHOLE" | "TILEMAJOR"
+    p0: int = 0        # ROWS: rows per block; TILE / TILEMAJOR: block rows; FLAT: block elements
+    p1: int = 0        # TILE / TILEMAJOR: block columns
 
     @property
     def numel(self) -> int:
@@ -144,3 +144,10 @@ def workload(index: int) -> Workload:
 def tiny_variant(base: Workload, **changes) -> Workload:
     """A copy of a workload with some fields changed (for parity-only variants)."""
     return replace(base, **changes)
+
+
+def tile_major_variant(w: Workload) -> Workload:
+    """The same workload with every TILE tensor stored tile by tile (TILEMAJOR, same tiles)."""
+    specs = tuple(TensorSpec(s.name, s.rows, s.cols, "TILEMAJOR", s.p0, s.p1) if s.kind == "TILE" else s
+                  for s in w.specs)
+    return replace(w, specs=specs, name=w.name.replace("128x128 tiles", "128x128 tiles stored tile-major"))
