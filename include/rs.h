@@ -79,10 +79,19 @@ typedef enum rs_dtype {
  *   RS_FLAT(b)     b consecutive elements             g = b
  *   RS_WHOLE       the whole tensor (one matrix per rank, as Muon wants)
  *                                                     g = rows * cols
- * The last block of a tensor may be partial. TILE and FLAT tensors are the
- * ones rs_block_quant quantises (tiles / flat blocks); the others are not. */
+ *   RS_TILEMAJOR(br,bc) br x bc tiles stored tile by tile: in the flat buffer
+ *                  the tensor is its tiles in tile-row-major order, each tile
+ *                  contiguous and row-major inside, so a rank boundary may
+ *                  fall between any two tiles (the walkthrough's 2-D blocks
+ *                  distributed asymmetrically)           g = br * bc
+ *                  Needs rows % br == 0, cols % bc == 0, br*bc % 16 == 0 and
+ *                  bc <= 8192. Unpack and pack reorder between this layout and
+ *                  the row-major tensor (through LDS on the GPU).
+ * The last block of a tensor may be partial. TILE, TILEMAJOR and FLAT
+ * tensors are the ones rs_block_quant quantises (tiles / flat blocks); the
+ * others are not. */
 typedef enum rs_block_kind {
-  RS_ELEM = 0, RS_ROWS = 1, RS_TILE = 2, RS_FLAT = 3, RS_WHOLE = 4
+  RS_ELEM = 0, RS_ROWS = 1, RS_TILE = 2, RS_FLAT = 3, RS_WHOLE = 4, RS_TILEMAJOR = 5
 } rs_block_kind;
 
 /* One tensor of the group. A 1-D tensor of n elements is rows = n, cols = 1.
@@ -150,7 +159,8 @@ int rs_plan_info(const rs_plan* plan, int64_t* R_used, int64_t* n_qblocks,
 void rs_plan_free(rs_plan* plan);   /* NULL is a no-op; waits for the device */
 
 /* Unpack after the (simulated) AllGather: T_i[e] = gathered[s_i + e] for
- * every tensor i and 0 <= e < n_i, bit for bit (feynmanwiki walkthrough,
+ * every tensor i and 0 <= e < n_i, bit for bit (for a TILEMAJOR tensor,
+ * element (r, c) is read from its place in its tile) (feynmanwiki walkthrough,
  * DBuffer paragraphs: a tensor is its planned slice; this call does the
  * Copy-Out of FSDP2's Copy-Out / Copy-In paragraph in one launch).
  * gathered: device, R_mat*S elements of `dt`, 16-byte aligned.
@@ -169,6 +179,7 @@ enum { RS_SCALE_INV_V = 0, RS_SCALE_GIVEN = 1 };
  *   sigma = fl32(1/V) for RS_SCALE_INV_V, else `scale`;
  *   y = fl32(src_i[e] * sigma);
  *   packed[s_i + e] = prev ? fl32(prev[s_i + e] + y) : y
+ * (for a TILEMAJOR tensor, element (r, c) goes to its place in its tile)
  * (scale first, then add: two IEEE round-to-nearest-even operations, never a
  * fused multiply-add), and packed[p] = +0.0 at every padding position p in
  * [0, R_mat*S). Padding of `prev` is never read.
@@ -219,7 +230,7 @@ int rs_block_dequant(rs_plan* plan, const void* q, int32_t q_dt, const float* sc
  * that reads each code once and writes each value once.
  * q, q_dt, scales: as produced by rs_block_quant (device, R_mat*S bytes,
  * 16-byte aligned; fp32 [n_qblocks]). dst: HOST array of n device pointers;
- * entries of TILE and FLAT tensors point to contiguous row-major tensors of
+ * entries of TILE, TILEMAJOR and FLAT tensors point to contiguous row-major tensors of
  * n_i elements of dst_dt (RS_BF16 or RS_F32), 16-byte aligned; entries of
  * other tensors are ignored and may be NULL. Codes 0x7F / 0xFF (E4M3 NaN)
  * give unspecified values. Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "librs_hip.so")
 RS_OK, RS_EINVAL, RS_EPLAN, RS_EALIGN, RS_EDTYPE, RS_ENOMEM, RS_EHIP, RS_ERANGE = 0, -1, -2, -3, -4, -5, -6, -7
 STATUS_NAMES = {0: "RS_OK", -1: "RS_EINVAL", -2: "RS_EPLAN", -3: "RS_EALIGN", -4: "RS_EDTYPE",
                 -5: "RS_ENOMEM", -6: "RS_EHIP", -7: "RS_ERANGE"}
-KINDS = {"ELEM": 0, "ROWS": 1, "TILE": 2, "FLAT": 3, "WHOLE": 4}
+KINDS = {"ELEM": 0, "ROWS": 1, "TILE": 2, "FLAT": 3, "WHOLE": 4, "TILEMAJOR": 5}
 ORDER_KINDS = {0: "default", 1: "by_block_size", 2: "by_shape"}
 RS_F32, RS_BF16, RS_E4M3, RS_I8, RS_U8 = 0, 1, 2, 3, 4
 CODE_FORMATS = {"e4m3": RS_E4M3, "i8": RS_I8, "u8": RS_U8}

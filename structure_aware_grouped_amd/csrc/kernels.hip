@@ -449,9 +449,9 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 // load, four loads in flight per thread.
 template <int FMT, bool HW, bool BF16OUT, int NT>
 __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ dst, float s,
-                             int64_t qbase, int64_t dbase, int64_t stride, int rows, int cols,
-                             int tid) {
-  if ((qbase % 8 == 0) && (dbase % 8 == 0) && (stride % 8 == 0) && (cols % 8 == 0)) {
+                             int64_t qbase, int64_t dbase, int64_t stride, int64_t dstride, int rows,
+                             int cols, int tid) {
+  if ((qbase % 8 == 0) && (dbase % 8 == 0) && (stride % 8 == 0) && (dstride % 8 == 0) && (cols % 8 == 0)) {
     constexpr int U = 4;
     const int vpr = cols / 8;
     const int nvec = rows * vpr;
@@ -461,8 +461,10 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
       int64_t off[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        off[u] = static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 8;
-        if (i0 + u * NT < nvec) c[u] = ldg(reinterpret_cast<const u32x2*>(q + qbase + off[u]));
+        off[u] = static_cast<int64_t>(w.row) * dstride + static_cast<int64_t>(w.col) * 8;
+        if (i0 + u * NT < nvec)
+          c[u] = ldg(reinterpret_cast<const u32x2*>(q + qbase + static_cast<int64_t>(w.row) * stride +
+                                                     static_cast<int64_t>(w.col) * 8));
         w.next();
       }
 #pragma unroll
@@ -487,12 +489,12 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
   const int64_t total = static_cast<int64_t>(rows) * cols;
   for (int64_t i = tid; i < total; i += NT) {
     const int64_t rr = i / cols, cc = i - rr * cols;
-    const int64_t off = rr * stride + cc;
-    const float v = __fmul_rn(decode1<FMT, HW>(q[qbase + off]), s);
+    const float v = __fmul_rn(decode1<FMT, HW>(q[qbase + rr * stride + cc]), s);
+    const int64_t d = dbase + rr * dstride + cc;
     if constexpr (BF16OUT)
-      static_cast<uint16_t*>(dst)[dbase + off] = static_cast<uint16_t>(bf16_rne(v));
+      static_cast<uint16_t*>(dst)[d] = static_cast<uint16_t>(bf16_rne(v));
     else
-      static_cast<float*>(dst)[dbase + off] = v;
+      static_cast<float*>(dst)[d] = v;
   }
 }
 
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void gather_tile_kernel(const QJob* __res
                                                                void* const* __restrict__ dst) {
   const QJob j = jobs[blockIdx.x];
   gather_block<FMT, HW, BF16OUT, kThreads>(q, dst[j.tensor], scales[j.scale], j.base, j.toff, j.stride,
-                                           j.rows, j.cols, threadIdx.x);
+                                           j.tstride, j.rows, j.cols, threadIdx.x);
 }
 
 template <int FMT, bool HW, bool BF16OUT>
@@ -584,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void gather_flat_kernel(const QJob* __res
   const int len = wave == j.rows - 1 ? j.last : j.cols;
   const int64_t step = static_cast<int64_t>(wave) * j.cols;
   gather_block<FMT, HW, BF16OUT, kWave>(q, dst[j.tensor], scales[j.scale + wave], j.base + step,
-                                        j.toff + step, len, 1, len, threadIdx.x & (kWave - 1));
+                                        j.toff + step, len, len, 1, len, threadIdx.x & (kWave - 1));
 }
 
 // ------------------------------------------------------------------ 8-bit Adam step
@@ -842,6 +844,104 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackChunk* __restr
   }
 }
 
+// ------------------------------------------------------------------ tile-major layout
+
+// Tile-major -> row-major (unpack of a TILEMAJOR tensor), one TmJob per
+// workgroup: the job's k runs of h*bc elements (one per tile, contiguous in
+// the buffer) are staged in LDS as h rows of k*bc elements, which are then
+// written as h contiguous row segments of the tensor. Both global sides move
+// long contiguous ranges; the reorder happens in LDS.
+template <int EB>
+__global__ __launch_bounds__(kThreads) void unpack_tm_kernel(const TmJob* __restrict__ jobs,
+                                                             const uint8_t* __restrict__ gathered,
+                                                             void* const* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kTmStage * 4];
+  const TmJob j = jobs[blockIdx.x];
+  const int bc = j.bc, h = j.h, k = j.k, tid = threadIdx.x;
+  const int run = h * bc, width = k * bc;
+  const uint8_t* src = gathered + j.base * EB;
+  uint8_t* out = static_cast<uint8_t*>(dst[j.tensor]) + j.toff * EB;
+  if ((bc * EB) % 16 == 0 && (j.cols * EB) % 16 == 0) {
+    constexpr int VE = 16 / EB;
+    const int rv = run / VE, total = k * rv;
+    for (int v = tid; v < total; v += kThreads) {
+      const int t = v / rv, e = (v - t * rv) * VE, r = e / bc, c = e - r * bc;
+      *reinterpret_cast<u32x4*>(stage + (r * width + t * bc + c) * EB) =
+          ldg(reinterpret_cast<const u32x4*>(src + (static_cast<int64_t>(t) * j.tile_elems + e) * EB));
+    }
+    __syncthreads();
+    const int wv = width / VE, total2 = h * wv;
+    for (int v = tid; v < total2; v += kThreads) {
+      const int r = v / wv, w = v - r * wv;
+      stg(reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(r) * j.cols + w * VE) * EB),
+          *reinterpret_cast<const u32x4*>(stage + (r * width + w * VE) * EB));
+    }
+    return;
+  }
+  for (int v = tid; v < k * run; v += kThreads) {
+    const int t = v / run, e = v - t * run, r = e / bc, c = e - r * bc;
+    const uint8_t* from = src + (static_cast<int64_t>(t) * j.tile_elems + e) * EB;
+    uint8_t* to = stage + (r * width + t * bc + c) * EB;
+    for (int b = 0; b < EB; ++b) to[b] = from[b];
+  }
+  __syncthreads();
+  for (int v = tid; v < h * width; v += kThreads) {
+    const int r = v / width, w = v - r * width;
+    uint8_t* to = out + (static_cast<int64_t>(r) * j.cols + w) * EB;
+    const uint8_t* from = stage + v * EB;
+    for (int b = 0; b < EB; ++b) to[b] = from[b];
+  }
+}
+
+// Row-major -> tile-major with the pack arithmetic (pack of a TILEMAJOR
+// tensor): h rows of k*bc gradients are staged in LDS as fp32, then each
+// tile's run of h*bc elements is written contiguously as
+// [prev +] fl32(g * sigma). `prev` may alias `out` (each element is read and
+// written by the same thread).
+template <bool BF16, bool ACC>
+__global__ __launch_bounds__(kThreads) void pack_tm_kernel(const TmJob* __restrict__ jobs,
+                                                           const void* const* __restrict__ src,
+                                                           const float* prev, float* out, float sigma) {
+  __shared__ __attribute__((aligned(16))) float stage[kTmStage];
+  const TmJob j = jobs[blockIdx.x];
+  const int bc = j.bc, h = j.h, k = j.k, tid = threadIdx.x;
+  const int run = h * bc, width = k * bc;
+  const void* g = src[j.tensor];
+  if (bc % 4 == 0 && j.cols % 4 == 0) {
+    const int wv = width / 4, total = h * wv;
+    for (int v = tid; v < total; v += kThreads) {
+      const int r = v / wv, w = v - r * wv;
+      *reinterpret_cast<f32x4*>(stage + r * width + 4 * w) = load4<BF16>(g, j.toff + static_cast<int64_t>(r) * j.cols + 4 * w);
+    }
+    __syncthreads();
+    const int rv = run / 4, total2 = k * rv;
+    for (int v = tid; v < total2; v += kThreads) {
+      const int t = v / rv, e = (v - t * rv) * 4, r = e / bc, c = e - r * bc;
+      const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(stage + r * width + t * bc + c);
+      f32x4 y{__fmul_rn(x.x, sigma), __fmul_rn(x.y, sigma), __fmul_rn(x.z, sigma), __fmul_rn(x.w, sigma)};
+      if constexpr (ACC) {
+        const f32x4 pv = ldg(reinterpret_cast<const f32x4*>(prev + pos));
+        y = f32x4{__fadd_rn(pv.x, y.x), __fadd_rn(pv.y, y.y), __fadd_rn(pv.z, y.z), __fadd_rn(pv.w, y.w)};
+      }
+      stg(reinterpret_cast<f32x4*>(out + pos), y);
+    }
+    return;
+  }
+  for (int v = tid; v < h * width; v += kThreads) {
+    const int r = v / width, w = v - r * width;
+    stage[v] = load1<BF16>(g, j.toff + static_cast<int64_t>(r) * j.cols + w);
+  }
+  __syncthreads();
+  for (int v = tid; v < k * run; v += kThreads) {
+    const int t = v / run, e = v - t * run, r = e / bc, c = e - r * bc;
+    const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
+    float y = __fmul_rn(stage[r * width + t * bc + c], sigma);
+    if constexpr (ACC) y = __fadd_rn(prev[pos], y);
+    out[pos] = y;
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -911,8 +1011,16 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_table(p, &p->dst, dst, s, who);
   if (st != RS_OK) return st;
-  hipLaunchKernelGGL(unpack_kernel<RS_UNPACK_U>, dim3(static_cast<unsigned>(p->n_unpack)), dim3(kThreads), 0, s,
-                     p->unpack, static_cast<const uint8_t*>(gathered), p->dst.dev, eb);
+  const uint8_t* gb = static_cast<const uint8_t*>(gathered);
+  if (p->n_unpack)
+    hipLaunchKernelGGL(unpack_kernel<RS_UNPACK_U>, dim3(static_cast<unsigned>(p->n_unpack)), dim3(kThreads), 0, s,
+                       p->unpack, gb, p->dst.dev, eb);
+  if (p->n_tm) {
+    const dim3 g(static_cast<unsigned>(p->n_tm));
+    if (eb == 4) hipLaunchKernelGGL(unpack_tm_kernel<4>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
+    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_kernel<2>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
+    else hipLaunchKernelGGL(unpack_tm_kernel<1>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
+  }
   return launched(who);
 }
 
@@ -944,12 +1052,24 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
   if (st != RS_OK) return st;
   const dim3 grid(static_cast<unsigned>(p->n_pack)), block(kThreads);
   void** tab = p->src.dev;
-  if (src_dt == RS_F32) {
-    if (prev) hipLaunchKernelGGL((pack_kernel<false, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
-    else hipLaunchKernelGGL((pack_kernel<false, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
-  } else {
-    if (prev) hipLaunchKernelGGL((pack_kernel<true, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
-    else hipLaunchKernelGGL((pack_kernel<true, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+  if (p->n_pack) {
+    if (src_dt == RS_F32) {
+      if (prev) hipLaunchKernelGGL((pack_kernel<false, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+      else hipLaunchKernelGGL((pack_kernel<false, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    } else {
+      if (prev) hipLaunchKernelGGL((pack_kernel<true, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+      else hipLaunchKernelGGL((pack_kernel<true, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+    }
+  }
+  if (p->n_tm) {
+    const dim3 g(static_cast<unsigned>(p->n_tm));
+    if (src_dt == RS_F32) {
+      if (prev) hipLaunchKernelGGL((pack_tm_kernel<false, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
+      else hipLaunchKernelGGL((pack_tm_kernel<false, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
+    } else {
+      if (prev) hipLaunchKernelGGL((pack_tm_kernel<true, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
+      else hipLaunchKernelGGL((pack_tm_kernel<true, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
+    }
   }
   return launched(who);
 }
@@ -1100,7 +1220,7 @@ extern "C" int rs_unpack_dequant(rs_plan* p, const void* q, int32_t q_dt, const 
   if (!q || !dst || (!scales && p->n_qblocks > 0)) return fail(RS_EINVAL, std::string(who) + ": null buffer");
   if (!aligned16(q)) return fail(RS_EALIGN, std::string(who) + ": q not 16-byte aligned");
   for (int64_t i = 0; i < p->n; ++i) {
-    if (p->t[i].kind != RS_TILE && p->t[i].kind != RS_FLAT) continue;
+    if (p->t[i].kind != RS_TILE && p->t[i].kind != RS_FLAT && p->t[i].kind != RS_TILEMAJOR) continue;
     if (!dst[i]) return fail(RS_EINVAL, std::string(who) + ": null destination " + std::to_string(i));
     if (!aligned16(dst[i])) return fail(RS_EALIGN, std::string(who) + ": destination " + std::to_string(i) + " not 16-byte aligned");
   }

@@ -73,6 +73,7 @@ int validate(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S, const
 }
 
 struct Tables {
+  std::vector<TmJob> tm;
   std::vector<CopyChunk> unpack;
   std::vector<PackChunk> pack;
   std::vector<QJob> qjobs;          // sorted by kind: tiles, flat groups, zero ranges
@@ -89,12 +90,34 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   const int64_t top = R_mat * S;
   const int64_t n = static_cast<int64_t>(t.size());
 
-  // unpack: every tensor in chunks
-  for (int64_t i = 0; i < n; ++i)
-    for (int64_t off = 0; off < t[i].n; off += kUnpackChunk)
-      tb->unpack.push_back({t[i].start + off, off,
-                            static_cast<int32_t>(std::min(kUnpackChunk, t[i].n - off)),
+  // unpack: every row-major tensor in chunks; TILEMAJOR tensors in strips of
+  // rows across up to k tiles of one tile row (unpack and pack share them)
+  for (int64_t i = 0; i < n; ++i) {
+    const Tensor& x = t[i];
+    if (x.kind == RS_TILEMAJOR) {
+      const int64_t br = x.p0, bc = x.p1, ntc = x.cols / bc;
+      const int64_t h = std::min<int64_t>(br, std::max<int64_t>(1, std::min<int64_t>(8, kTmStage / bc)));
+      const int64_t k = std::max<int64_t>(1, std::min(ntc, kTmStage / (h * bc)));
+      for (int64_t tr = 0; tr < x.rows / br; ++tr)
+        for (int64_t tc0 = 0; tc0 < ntc; tc0 += k)
+          for (int64_t r0 = 0; r0 < br; r0 += h) {
+            TmJob j{};
+            j.base = x.start + (tr * ntc + tc0) * br * bc + r0 * bc;
+            j.toff = (tr * br + r0) * x.cols + tc0 * bc;
+            j.cols = x.cols;
+            j.tile_elems = br * bc;
+            j.tensor = static_cast<int32_t>(i);
+            j.k = static_cast<int32_t>(std::min(k, ntc - tc0));
+            j.h = static_cast<int32_t>(std::min(h, br - r0));
+            j.bc = static_cast<int32_t>(bc);
+            tb->tm.push_back(j);
+          }
+      continue;
+    }
+    for (int64_t off = 0; off < x.n; off += kUnpackChunk)
+      tb->unpack.push_back({x.start + off, off, static_cast<int32_t>(std::min(kUnpackChunk, x.n - off)),
                             static_cast<int32_t>(i)});
+  }
 
   // pack: walk the buffer in address order; data chunks own the padding up
   // to the next 16-element boundary after their tensor ends
@@ -110,6 +133,10 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     const Tensor& x = t[k];
     pad(pos, x.start);
     const int64_t end16 = align_up(x.start + x.n, 16);
+    if (x.kind == RS_TILEMAJOR) {   // packed by the tile-major jobs; n is a multiple of 16
+      pos = end16;
+      continue;
+    }
     for (int64_t off = 0; off < x.n; off += kPackChunk) {
       const int64_t n_data = std::min(kPackChunk, x.n - off);
       const int64_t n_total = (off + kPackChunk >= x.n) ? end16 - (x.start + off) : n_data;
@@ -141,9 +168,28 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
           j.last = 0;
           j.tensor = static_cast<int32_t>(ti);
           j.toff = j.base - x.start;
+          j.tstride = x.cols;
           tb->qjobs.push_back(j);
           const int64_t v16 = int64_t(j.rows) * ((int64_t(j.cols) * 4 + 15) / 16);
           tb->max_tile_vec16 = static_cast<int32_t>(std::max<int64_t>(tb->max_tile_vec16, std::min<int64_t>(v16, 1 << 30)));
+        }
+      }
+    } else if (x.kind == RS_TILEMAJOR) {
+      const int64_t br = x.p0, bc = x.p1, ntc = x.cols / bc;
+      for (int64_t tr = 0; tr < x.rows / br; ++tr) {
+        for (int64_t tc = 0; tc < ntc; ++tc) {
+          QJob j{};
+          j.base = x.start + (tr * ntc + tc) * br * bc;   // the tile is contiguous
+          j.stride = bc;
+          j.scale = q++;
+          j.rows = static_cast<int32_t>(br);
+          j.cols = static_cast<int32_t>(bc);
+          j.kind = QJOB_TILE;
+          j.last = 0;
+          j.tensor = static_cast<int32_t>(ti);
+          j.toff = tr * br * x.cols + tc * bc;
+          j.tstride = x.cols;
+          tb->qjobs.push_back(j);
         }
       }
     } else if (x.kind == RS_FLAT) {
@@ -160,6 +206,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
         j.last = static_cast<int32_t>(std::min(x.p0, x.n - (b0 + cnt - 1) * x.p0));
         j.tensor = static_cast<int32_t>(ti);
         j.toff = j.base - x.start;
+        j.tstride = x.p0;
         tb->qjobs.push_back(j);
         q += cnt;
       }
@@ -168,7 +215,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   tb->n_qblocks = q;
   std::vector<std::pair<int64_t, int64_t>> qiv;
   for (const Tensor& x : t)
-    if (x.kind == RS_TILE || x.kind == RS_FLAT) qiv.push_back({x.start, x.start + x.n});
+    if (x.kind == RS_TILE || x.kind == RS_FLAT || x.kind == RS_TILEMAJOR) qiv.push_back({x.start, x.start + x.n});
   std::sort(qiv.begin(), qiv.end());
   auto zero = [&](int64_t from, int64_t to) {
     for (int64_t p = from; p < to; p += kZeroChunk) {
@@ -202,7 +249,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     tile_vec[ti] = t[ti].kind == RS_TILE && t[ti].cols % 16 == 0 && t[ti].p1 % 16 == 0 &&
                    t[ti].cols <= kGatherMaxCols;
   for (const QJob& j : tb->qjobs)
-    if (j.kind == QJOB_TILE && !tile_vec[j.tensor]) tb->gjobs.push_back(j);
+    if (j.kind == QJOB_TILE && !tile_vec[j.tensor]) tb->gjobs.push_back(j);   // incl. TILEMAJOR tiles
   q = 0;
   for (int64_t ti = 0; ti < n; ++ti) {
     const Tensor& x = t[ti];
@@ -227,6 +274,8 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
         }
       }
       q += ((x.rows + x.p0 - 1) / x.p0) * ntc;
+    } else if (x.kind == RS_TILEMAJOR) {
+      q += x.n / (x.p0 * x.p1);
     } else if (x.kind == RS_FLAT) {
       const int64_t nfull = x.n / x.p0;            // whole blocks
       int64_t done = 0;
@@ -260,6 +309,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
         j.last = static_cast<int32_t>(std::min(x.p0, x.n - (b0 + cnt - 1) * x.p0));
         j.tensor = static_cast<int32_t>(ti);
         j.toff = j.base - x.start;
+        j.tstride = x.p0;
         tb->gjobs.push_back(j);
       }
       q += nblk;
@@ -344,6 +394,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->padding = tb.padding;
     p->t = t;
     p->n_unpack = static_cast<int64_t>(tb.unpack.size());
+    p->n_tm = static_cast<int64_t>(tb.tm.size());
     p->n_pack = static_cast<int64_t>(tb.pack.size());
     p->n_qjobs = static_cast<int64_t>(tb.qjobs.size());
     p->n_qblocks = tb.n_qblocks;
@@ -359,7 +410,8 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     const char* enc = std::getenv("RS_E4M3_ENCODER");
     p->e4m3_hw = !(enc && std::strcmp(enc, "sw") == 0);
 
-    const int64_t bytes = align_up(sizeof(CopyChunk) * std::max<int64_t>(p->n_unpack, 1), 256) +
+    const int64_t bytes = align_up(sizeof(TmJob) * std::max<int64_t>(p->n_tm, 1), 256) +
+                          align_up(sizeof(CopyChunk) * std::max<int64_t>(p->n_unpack, 1), 256) +
                           align_up(sizeof(PackChunk) * std::max<int64_t>(p->n_pack, 1), 256) +
                           align_up(sizeof(QJob) * std::max<int64_t>(p->n_qjobs, 1), 256) +
                           align_up(sizeof(GatherChunk) * std::max<int64_t>(p->n_gchunks, 1), 256) +
@@ -372,6 +424,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
       return fail(RS_ENOMEM, "rs_plan_load: device allocation of the work lists failed");
     }
     char* cur = static_cast<char*>(p->dmem);
+    p->tmjobs = carve<TmJob>(cur, p->n_tm);
     p->unpack = carve<CopyChunk>(cur, p->n_unpack);
     p->pack = carve<PackChunk>(cur, p->n_pack);
     p->qjobs = carve<QJob>(cur, p->n_qjobs);
@@ -381,8 +434,9 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     void** src_dev = carve<void*>(cur, n);
     void** gdst_dev = carve<void*>(cur, n);
 
-    bool ok = hipMemcpy(p->unpack, tb.unpack.data(), sizeof(CopyChunk) * p->n_unpack, hipMemcpyHostToDevice) == hipSuccess &&
-              hipMemcpy(p->pack, tb.pack.data(), sizeof(PackChunk) * p->n_pack, hipMemcpyHostToDevice) == hipSuccess &&
+    bool ok = (p->n_tm == 0 || hipMemcpy(p->tmjobs, tb.tm.data(), sizeof(TmJob) * p->n_tm, hipMemcpyHostToDevice) == hipSuccess) &&
+              (p->n_unpack == 0 || hipMemcpy(p->unpack, tb.unpack.data(), sizeof(CopyChunk) * p->n_unpack, hipMemcpyHostToDevice) == hipSuccess) &&
+              (p->n_pack == 0 || hipMemcpy(p->pack, tb.pack.data(), sizeof(PackChunk) * p->n_pack, hipMemcpyHostToDevice) == hipSuccess) &&
               (p->n_qjobs == 0 || hipMemcpy(p->qjobs, tb.qjobs.data(), sizeof(QJob) * p->n_qjobs, hipMemcpyHostToDevice) == hipSuccess) &&
               (p->n_gchunks == 0 || hipMemcpy(p->gchunks, tb.gchunks.data(), sizeof(GatherChunk) * p->n_gchunks, hipMemcpyHostToDevice) == hipSuccess) &&
               (tb.gjobs.empty() || hipMemcpy(p->gjobs, tb.gjobs.data(), sizeof(QJob) * tb.gjobs.size(), hipMemcpyHostToDevice) == hipSuccess);

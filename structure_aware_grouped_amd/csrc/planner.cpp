@@ -43,6 +43,7 @@ int64_t granularity(const rs_tensor_spec& s) {
     case RS_TILE: return s.p0 * s.cols;
     case RS_FLAT: return s.p0;
     case RS_WHOLE: return s.rows * s.cols;
+    case RS_TILEMAJOR: return s.p0 * s.p1;
     default: return 0;
   }
 }
@@ -68,6 +69,13 @@ bool spec_ok(const rs_tensor_spec& s, std::string* why) {
       if (s.p0 < 1 || s.p1 < 1) return bad("TILE needs p0, p1 >= 1");
       if (s.p0 > (int64_t(1) << 24) || s.p1 > (int64_t(1) << 24) || s.p0 * s.p1 > (int64_t(1) << 24))
         return bad("tile larger than 2^24 elements");
+      break;
+    case RS_TILEMAJOR:
+      if (s.p0 < 1 || s.p1 < 1) return bad("TILEMAJOR needs p0, p1 >= 1");
+      if (s.p0 > (int64_t(1) << 24) || s.p1 > 8192 || s.p0 * s.p1 > (int64_t(1) << 24))
+        return bad("TILEMAJOR tiles hold at most 2^24 elements and 8192 columns");
+      if (s.rows % s.p0 != 0 || s.cols % s.p1 != 0) return bad("TILEMAJOR tiles must cover the tensor exactly");
+      if ((s.p0 * s.p1) % 16 != 0) return bad("TILEMAJOR tile size must be a multiple of 16 elements");
       break;
     default:
       return bad("unknown block kind");

@@ -64,13 +64,17 @@ enum QJobKind : int32_t { QJOB_TILE = 0, QJOB_FLAT = 1, QJOB_ZERO = 2 };
 //   FLAT: `rows` (1..kFlatPerGroup) consecutive flat blocks of `cols` elements
 //         from base; the last one has `last` elements. Scales scale..scale+rows-1.
 //   ZERO: elements [base, base + stride) lie in no block (codes 0, values +0.0).
-// TILE and FLAT jobs also name their tensor and the offset of `base` inside
-// it (base - s_tensor), for kernels that write the full tensors.
+// TILE and FLAT jobs also name their tensor and where the block's element
+// (0, 0) sits in the full row-major tensor (toff) with the tensor's row
+// stride (tstride), for kernels that write the full tensors. For a
+// row-major tensor toff = base - s_tensor and tstride = stride; a TILEMAJOR
+// tile has stride = bc in the buffer but tstride = cols in the tensor.
 struct QJob {
   int64_t base;
   int64_t stride;
   int64_t scale;
   int64_t toff;
+  int64_t tstride;
   int32_t rows;
   int32_t cols;
   int32_t kind;
@@ -78,6 +82,23 @@ struct QJob {
   int32_t tensor;
   int32_t unused;
 };
+
+// Tile-major reorder work item: rows [r0, r0 + h) of tiles tc0 .. tc0 + k - 1
+// of tile row tr of a TILEMAJOR tensor, staged through LDS. In the buffer
+// those are k runs of h*bc elements (one per tile, tile_elems apart) from
+// `base`; in the row-major tensor, h rows of k*bc elements from `toff`.
+struct TmJob {
+  int64_t base;        // flat position of row r0 of tile (tr, tc0)
+  int64_t toff;        // row-major offset of element (tr*br + r0, tc0*bc)
+  int64_t cols;        // tensor columns (row stride of the tensor)
+  int64_t tile_elems;  // br * bc
+  int32_t tensor;
+  int32_t k;
+  int32_t h;
+  int32_t bc;
+};
+
+constexpr int64_t kTmStage = 8192;   // elements staged in LDS per tile-major job (32 KiB as fp32)
 
 // Gather-side work item: a contiguous run of whole rows of one quantised
 // tensor, inside one band of tiles (TILE) or made of whole flat blocks (FLAT,
@@ -140,6 +161,8 @@ struct rs_plan {
   int64_t n_qblocks = 0;
   int32_t max_tile_vec16 = 0;  // largest tile, in 16-byte vectors of 4-byte input
 
+  rs::TmJob* tmjobs = nullptr;         // unpack / pack of TILEMAJOR tensors
+  int64_t n_tm = 0;
   rs::GatherChunk* gchunks = nullptr;  // gather side, vector-friendly tensors
   int64_t n_gchunks = 0;
   rs::QJob* gjobs = nullptr;           // gather side, other tensors: tile jobs, then flat groups

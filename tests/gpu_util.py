@@ -46,8 +46,11 @@ class Inputs:
     def weight_bits(self, i: int) -> np.ndarray:
         return W.weight_bits(self.w, i).ravel()
 
-    def gathered(self) -> torch.Tensor:
-        """The all-gathered flat parameter buffer; padding holds a NaN pattern."""
+    def gathered(self, arrange=None) -> torch.Tensor:
+        """The all-gathered flat parameter buffer; padding holds a NaN pattern.
+
+        ``arrange(i, bits)`` returns tensor i's row-major bits in the order of its
+        interval in the buffer (default: row-major, every kind but TILEMAJOR)."""
         total = self.R * self.S
         fill = POISON_BF16 if self.pdtype == torch.bfloat16 else POISON_F32
         if self.pdtype == torch.bfloat16:
@@ -59,8 +62,10 @@ class Inputs:
             idx = list(range(lo, min(lo + 16, n_specs)))
             bits = W.parallel_map(self.weight_bits, idx)
             for i, b in zip(idx, bits):
+                if arrange is not None:
+                    b = arrange(i, b)
                 s = self.starts[i]
-                G[s: s + b.size].copy_(to_device_bits(b, self.pdtype, self.device))
+                G[s: s + b.size].copy_(to_device_bits(np.ascontiguousarray(b), self.pdtype, self.device))
         return G
 
     def empty_params(self) -> List[torch.Tensor]:

@@ -125,3 +125,26 @@ def test_valid_plan_without_gpu_reports_a_hip_error(rs):
     from structure_aware_grouped_amd import binding as b
     specs = [TensorSpec("a", 4, 16, "ROWS", 1), TensorSpec("b", 2, 32, "TILE", 2, 16)]
     assert _status(lambda: rs.rs_plan_load(specs, 4, 64, [0, 128])) == b.RS_EHIP
+
+
+def test_tile_major_specs_are_checked(rs):
+    from structure_aware_grouped_amd import binding as b
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 30, 32, "TILEMAJOR", 16, 16)], 4)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 32, 30, "TILEMAJOR", 16, 16)], 4)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 9, 9, "TILEMAJOR", 3, 3)], 4)) == b.RS_EINVAL
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("a", 1, 16384, "TILEMAJOR", 1, 16384)], 4)) == b.RS_EINVAL
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_host_planner_matches_oracle_on_tile_major_groups(rs, seed):
+    rng = random.Random(500 + seed)
+    specs = []
+    for i in range(rng.randint(1, 6)):
+        kind = rng.choice(["TILEMAJOR", "TILEMAJOR", "TILE", "ROWS"])
+        br, bc = rng.choice([(16, 16), (32, 32), (8, 64), (128, 128), (16, 3)])
+        r, c = br * rng.randint(1, 6), bc * rng.randint(1, 6)
+        specs.append(TensorSpec(f"t{i}", r, c, kind, br if kind != "ROWS" else 1, bc if kind != "ROWS" else 0))
+    V = rng.choice([1, 2, 3, 8, 16])
+    S, starts, order, name = rs.rs_plan_build(specs, V, 16)
+    ref = OP.plan(specs, V, 16)
+    assert (S, starts, name) == (ref.S, [int(s) for s in ref.starts], ref.order_name)

@@ -29,7 +29,8 @@ def _run(rs, plan, state, h):
 @pytest.mark.parametrize("V", [1, 4])
 def test_chained_steps_on_a_ragged_group(gpu_lib, V):
     import structure_aware_grouped_amd as rs
-    specs = RAGGED + [TensorSpec("tile32", 64, 96, "TILE", 32, 32)]
+    specs = RAGGED + [TensorSpec("tile32", 64, 96, "TILE", 32, 32),
+                      TensorSpec("tm32", 64, 96, "TILEMAJOR", 32, 32)]
     S, starts, _, _ = rs.rs_plan_build(specs, V)
     plan = rs.rs_plan_load(specs, V, S, starts, V, 0)
     rng = np.random.default_rng(V)

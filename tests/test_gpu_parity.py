@@ -115,7 +115,7 @@ def _full_check(rs, specs, V, pdtype, seed, fmts=("e4m3", "i8", "u8"), R_mat=Non
         assert guard_intact(owhole, total)
         # gather side: gathered codes + scales -> the quantised full tensors
         for out_dt, tag in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
-            quantised = [sp.kind in ("TILE", "FLAT") for sp in specs]
+            quantised = [sp.kind in ("TILE", "TILEMAJOR", "FLAT") for sp in specs]
             dsts = [garbage(sp.rows * sp.cols, out_dt, DEV).view(sp.rows, sp.cols) if qz else None
                     for sp, qz in zip(specs, quantised)]
             rs.rs_unpack_dequant(plan, q, fmt, scales, dsts)
@@ -196,6 +196,25 @@ def test_e4m3_amax_overshoot(gpu_lib, encoder, pdtype, monkeypatch):
     assert np.all(got.reshape(-1, b)[:, 3] == 0x7E) and np.all(got.reshape(-1, b)[:, 40] == 0xFE)
     assert np.array_equal(tensor_bits(sc), ws.view(np.uint32))
     plan.close()
+
+
+TILE_MAJOR = [
+    TensorSpec("tm32", 64, 96, "TILEMAJOR", 32, 32),
+    TensorSpec("tm_wide", 32, 2048, "TILEMAJOR", 16, 128),  # strips split by the LDS budget
+    TensorSpec("tm_odd", 32, 12, "TILEMAJOR", 16, 3),        # runs not a multiple of 16 bytes
+    TensorSpec("rows", 10, 10, "ROWS", 1),
+    TensorSpec("tile_rm", 48, 64, "TILE", 16, 16),
+    TensorSpec("flat", 1, 1000, "FLAT", 256),
+]
+
+
+@pytest.mark.parametrize("V", [1, 3, 8])
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_tile_major_group(gpu_lib, V, pdtype):
+    """Tile-major tensors through unpack / pack (LDS reorder), quant, dequant and the
+    fused unpack-dequant, next to row-major ones."""
+    import structure_aware_grouped_amd as rs
+    _full_check(rs, TILE_MAJOR, V, pdtype, 40 + V)
 
 
 def test_trailing_padding_ranks(gpu_lib):

@@ -11,14 +11,16 @@ import torch
 
 from oracle import plan as OP, transform as OT
 from tests.gpu_util import Inputs, garbage, tensor_bits
-from workloads import f32_from_bf16_bits, workload
+from workloads import f32_from_bf16_bits, tile_major_variant, workload
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _setup(rs, idx):
+def _setup(rs, idx, tile_major=False):
     w = workload(idx)
+    if tile_major:
+        w = tile_major_variant(w)
     S, starts, _, _ = rs.rs_plan_build(list(w.specs), w.V)
     ref = OP.plan(w.specs, w.V)
     assert S == ref.S and starts == [int(s) for s in ref.starts]
@@ -46,15 +48,27 @@ def _tensor_param_f32(inp, i):
     return f32_from_bf16_bits(bits) if bits.dtype == np.uint16 else bits.view(np.float32)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3])
-def test_param_and_grad_workloads(gpu_lib, idx):
+def _arrange(specs):
+    """Row-major bits -> the order of the tensor's interval (the oracle's layout)."""
+    def arrange(i, bits):
+        if specs[i].kind != "TILEMAJOR":
+            return bits
+        out = np.empty_like(bits)
+        out[OP.layout_offsets(specs[i])] = bits
+        return out
+    return arrange
+
+
+@pytest.mark.parametrize("idx,tile_major", [(1, False), (2, False), (3, False), (1, True)])
+def test_param_and_grad_workloads(gpu_lib, idx, tile_major):
     import structure_aware_grouped_amd as rs
-    w, plan, inp = _setup(rs, idx)
+    w, plan, inp = _setup(rs, idx, tile_major)
     R, S = plan.R_mat, plan.S
     specs = list(w.specs)
-    print(f"workload {idx}: S={S} R_mat={R} tensors={len(specs)}", flush=True)
+    print(f"workload {idx}{' (tile-major)' if tile_major else ''}: S={S} R_mat={R} tensors={len(specs)}",
+          flush=True)
 
-    G = inp.gathered()
+    G = inp.gathered(_arrange(specs))
     params = inp.empty_params()
     rs.rs_unpack_gathered(plan, G, params)
     print("  params uploaded and unpacked", flush=True)
@@ -69,7 +83,7 @@ def test_param_and_grad_workloads(gpu_lib, idx):
         scales = garbage(plan.n_qblocks, torch.float32, DEV)
         rs.rs_block_quant(plan, G, q, w.quant, scales)
         # gather side: the codes and scales rebuild the quantised bf16 tensors
-        gathered = [garbage(sp.rows * sp.cols, torch.bfloat16, DEV) if sp.kind in ("TILE", "FLAT") else None
+        gathered = [garbage(sp.rows * sp.cols, torch.bfloat16, DEV) if sp.kind in ("TILE", "TILEMAJOR", "FLAT") else None
                     for sp in specs]
         rs.rs_unpack_dequant(plan, q, w.quant, scales, gathered)
     torch.cuda.synchronize()
@@ -79,11 +93,12 @@ def test_param_and_grad_workloads(gpu_lib, idx):
     sigma = OT.inv_v(w.V)
     for i in sample:
         s, n = plan.starts[i], plan.numels[i]
+        lay = OP.layout_offsets(specs[i]) if specs[i].kind == "TILEMAJOR" else slice(None)
         # unpack: T_i is the gathered slice
         assert np.array_equal(tensor_bits(params[i]).ravel(), inp.weight_bits(i)), f"unpack {i}"
         # pack: every element of the tensor's slice
-        want = OT.pack_values(inp.grad(i).ravel(), inp.prev_range(s, s + n), sigma, True)
-        assert np.array_equal(tensor_bits(packed[s: s + n]), want.view(np.uint32)), f"pack {i}"
+        want = OT.pack_values(inp.grad(i).ravel(), inp.prev_range(s, s + n)[lay], sigma, True)
+        assert np.array_equal(tensor_bits(packed[s: s + n])[lay], want.view(np.uint32)), f"pack {i}"
     pads = OP.padding_ranges(specs, plan.starts, S, R)
     _zero_everywhere(packed, pads)
     print(f"  unpack and pack match on tensors {sample}; padding zero", flush=True)
@@ -95,18 +110,22 @@ def test_param_and_grad_workloads(gpu_lib, idx):
         sc_bits = tensor_bits(scales)
         for i in sample[: min(len(sample), 6)]:
             s, n = plan.starts[i], plan.numels[i]
-            x = _tensor_param_f32(inp, i)
+            lay = OP.layout_offsets(specs[i])
+            x = np.empty(n, np.float32)
+            x[lay] = _tensor_param_f32(inp, i)           # the tensor's interval order
+            elem = np.empty(n, np.int64)
+            elem[lay] = np.arange(n)                     # interval position -> row-major element
             got_q = tensor_bits(q[s: s + n])
-            got_g = tensor_bits(gathered[i]) if gathered[i] is not None else None
+            got_g = tensor_bits(gathered[i]).ravel() if gathered[i] is not None else None
             for _, b, pos in OT.quant_blocks([specs[i]], [0]):
                 c, sc = OT.quantize_block(x[pos], w.quant)
                 assert np.array_equal(got_q[pos], c), f"quant {i} block {b}"
                 assert sc_bits[first[i] + b] == np.float32(sc).view(np.uint32), f"scale {i} block {b}"
                 want_g = OT.bf16_round(OT.dequant_values(c, sc, w.quant))
-                assert np.array_equal(got_g[pos], want_g), f"unpack-dequant {i} block {b}"
-        _zero_everywhere(q, OP.padding_ranges([sp for sp in specs if sp.kind in ("TILE", "FLAT")],
+                assert np.array_equal(got_g[elem[pos]], want_g), f"unpack-dequant {i} block {b}"
+        _zero_everywhere(q, OP.padding_ranges([sp for sp in specs if sp.kind in ("TILE", "TILEMAJOR", "FLAT")],
                                               [st for sp, st in zip(specs, plan.starts)
-                                               if sp.kind in ("TILE", "FLAT")], S, R))
+                                               if sp.kind in ("TILE", "TILEMAJOR", "FLAT")], S, R))
         sf = scales.float()
         assert bool(torch.isfinite(sf).all()) and bool((sf > 0).all())
     plan.close()
