@@ -132,26 +132,25 @@ def read_traffic(kernel: str):
     return int(m.group(1)) if m else None
 
 
-def cpu_baseline(w, plan) -> dict:
-    """The CPU oracle (single-threaded NumPy) on a bounded sample: the attention
-    block of the layer (wq, wk, wv, wo and both norms), same byte accounting."""
-    from oracle import plan as OP, transform as OT
+def cpu_baseline(w, plan, names=None) -> dict:
+    """The CPU oracle (single-threaded NumPy) on a bounded sample of the workload:
+    the tensors named in `names` (default: every tensor, i.e. one whole step),
+    one at a time, with the bench's byte accounting. Inputs are generated before
+    the clock starts."""
+    from oracle import transform as OT
     from tests.gpu_util import Inputs
     import workloads as W
 
-    names = ("wq", "wk", "wv", "wo", "attn_norm", "mlp_norm")
+    names = [sp.name for sp in w.specs] if names is None else list(names)
     idx = [i for i, sp in enumerate(w.specs) if sp.name in names]
     inp = Inputs(w, plan.S, plan.starts, plan.R_mat, device="cpu")
-    specs = [w.specs[i] for i in idx]
-    weights = [inp.weight_bits(i) for i in idx]
-    grads = [inp.grad(i) for i in idx]
-    starts = [plan.starts[i] for i in idx]
-    prevs = [inp.prev_range(s, s + sp.numel) for s, sp in zip(starts, specs)]
     pb = 2 if w.param_dtype == "bf16" else 4
     sigma = OT.inv_v(w.V)
-    t0 = time.perf_counter()
-    moved = 0
-    for spec, s, wb, g, p in zip(specs, starts, weights, grads, prevs):
+    moved, dt = 0, 0.0
+    for i in idx:
+        spec, s = w.specs[i], plan.starts[i]
+        wb, g, p = inp.weight_bits(i), inp.grad(i), inp.prev_range(s, s + spec.numel)
+        t0 = time.perf_counter()
         n = spec.numel
         # unpack: the tensor is its slice of the gathered buffer
         OT.unpack(wb, [spec], [0])
@@ -165,10 +164,11 @@ def cpu_baseline(w, plan) -> dict:
             for _, b, pos in OT.quant_blocks([spec], [0]):
                 OT.quantize_block(x[pos], w.quant)
             moved += n * pb + n + 4 * OT.count_quant_blocks([spec])
-    dt = time.perf_counter() - t0
+        dt += time.perf_counter() - t0
+    what = "every tensor of the layer (one whole step)" if len(idx) == len(w.specs) else ", ".join(names)
     return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"attention block of the layer ({', '.join(names)}): unpack + pack"
-                      f"{' + e4m3 tile quant' if w.quant else ''}, {moved / 1e9:.3f} GB in {dt:.1f} s"}
+            "sample": f"{what}: unpack + pack{' + e4m3 tile quant' if w.quant else ''}, "
+                      f"{moved / 1e9:.3f} GB in {dt:.1f} s"}
 
 
 def main():
