@@ -112,9 +112,9 @@ typedef struct rs_plan rs_plan;   /* opaque, owned by the library */
 enum { RS_ORDER_BEST = 0, RS_ORDER_DEFAULT = 1 };
 enum { RS_ORDER_KIND_DEFAULT = 0, RS_ORDER_KIND_BLOCK = 1, RS_ORDER_KIND_SHAPE = 2 };
 
-/* Host planner (feynmanwiki walkthrough: "the planner first fixes a tensor
- * order", "for a candidate per-device size", "the outer search"; bud-325
- * summary, Method (2)).
+/* Host planner (feynmanwiki walkthrough: the planner paragraphs on the
+ * tensor order, on one candidate per-device size and on the search over
+ * sizes; bud-325 summary, Method (2)).
  * For each tensor order tried — the caller's order, block size descending,
  * shape descending (element count, then rows), all stable — find the
  * smallest S that is a multiple of `align` and at least
@@ -142,7 +142,9 @@ int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t ali
  * Checks (RS_EPLAN unless noted): S > 0 and S % 16 == 0 and every
  * s_i % 16 == 0 (RS_EALIGN); intervals disjoint and inside [0, V*S); no
  * rank boundary inside a tensor except at a multiple of g_i from s_i;
- * R_mat in [R_used, V] (RS_ERANGE); V*S fits int64 (RS_ERANGE).
+ * R_mat in [R_used, V] (RS_ERANGE); V*S fits int64 (RS_ERANGE); no
+ * kernel launch of the plan needs more than (2^32 - 1) / 256 work items
+ * (RS_ERANGE: about 2^37 elements of R_mat*S, beyond one device's memory).
  * On success *out owns host memory and one device allocation, released by
  * rs_plan_free. Errors: the above, RS_ENOMEM, RS_EHIP. */
 int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,

@@ -7,7 +7,7 @@ mantissa bits. Exponent field 0 holds subnormals m/8 * 2^-6; exponent field
 15 with mantissa 7 is NaN; there is no infinity, so the largest finite
 magnitude is 1.75 * 2^8 = 448 (code 0x7E).
 
-Encoding (the reading for the pages' "block-wise FP8", [summary] TL;DR and
+Encoding (the reading for the pages' block-wise FP8, [summary] TL;DR and
 Key claims on DeepSeek-V3-style FP8): round |y| to the nearest finite E4M3
 magnitude, ties to the code with an even mantissa, saturate everything at or
 above 448 to 448, and keep the sign bit (so -0.0 encodes as 0x80). NaN

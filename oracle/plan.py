@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Notation ([walk], "the planner can be stated as a packing problem"): tensors
+Notation ([walk], the paragraph that states the planner as packing): tensors
 T_1..T_N with n_i elements share one buffer of V*S elements; rank k owns
 [kS, (k+1)S). Tensor i occupies the contiguous interval [s_i, s_i + n_i);
 intervals are disjoint and lie inside [0, V*S); padding lives only in the
@@ -18,9 +18,9 @@ notes):
     by tile, each tile contiguous, so a cut may fall between any two tiles;
     the tiles must cover the tensor exactly). The block count is
     ceil(n_i / g_i); the last block may be partial.
-  * Alignment: S and every s_i are multiples of a "collective-preferred"
-    alignment a (16 elements here, a parameter).
-  * Orders ([walk], "the planner first fixes a tensor order"; [summary],
+  * Alignment: S and every s_i are multiples of an alignment a that the
+    pages leave to the collective (16 elements here, a parameter).
+  * Orders ([walk], the planner's tensor-order paragraph; [summary],
     Method): caller order, block size descending, shape descending (element
     count, then rows), each stable.
   * Search over S: for each order, the smallest feasible multiple of a that
@@ -56,7 +56,7 @@ def numel(spec) -> int:
 
 
 def granularity(spec) -> int:
-    """Flat size g of one atomic block ([walk], "RaggedShard makes the forbidden cut explicit")."""
+    """Flat size g of one atomic block ([walk], RaggedShard paragraph on the forbidden cut)."""
     n = numel(spec)
     k = spec.kind
     if k == "ELEM":

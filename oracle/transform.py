@@ -15,8 +15,8 @@ Readings (listed in the design notes):
     y = fl32(g * sigma) and out = fl32(prev + y) when accumulating, else y:
     scale first, then add, two roundings, no fused multiply-add. Every
     padding position is written as +0.0; padding of prev is never read.
-  * Quantisation blocks ([walk], "every quantization block should ideally
-    live entirely on one device"; the 8-bit Adam paragraph's 32x32 blocks at
+  * Quantisation blocks ([walk], the block-quantisation paragraph: a block
+    should sit whole on one device; the 8-bit Adam paragraph's 32x32 blocks at
     32-row granularity): TILE tensors are cut into br x bc tiles of the
     row-major tensor (partial at the right and bottom edges); TILEMAJOR
     tensors into their tiles (contiguous in the buffer); FLAT tensors into

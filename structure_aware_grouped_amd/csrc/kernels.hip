@@ -345,25 +345,36 @@ __device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
   for (int64_t i = tid; i < nv; i += kThreads) stg(v + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 }
 
-// One workgroup per tile.
+// One workgroup per tile. Workgroups from n_main on take the zero-range jobs
+// that follow the tiles in the list and clear code bytes outside every block,
+// so the whole call is one launch.
 template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void quant_tile_kernel(const QJob* __restrict__ jobs,
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
                                                               const void* __restrict__ src,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ scales) {
   __shared__ uint32_t red[kThreads / kWave];
   const QJob j = jobs[blockIdx.x];
+  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+    zero_bytes(q, j.base, j.stride, threadIdx.x);
+    return;
+  }
   quant_block<BF16, FMT, HW, kThreads, BF16 ? 8 : 16>(src, q, scales, j.base, j.stride, j.rows, j.cols,
                                                        j.scale, threadIdx.x, red);
 }
 
-// One wave per flat block, up to four blocks per workgroup.
+// One wave per flat block, up to four blocks per workgroup; zero-range jobs
+// from n_main on, as in the tile kernel.
 template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void quant_flat_kernel(const QJob* __restrict__ jobs,
+__global__ __launch_bounds__(kThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
                                                               const void* __restrict__ src,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ scales) {
   const QJob j = jobs[blockIdx.x];
+  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+    zero_bytes(q, j.base, j.stride, threadIdx.x);
+    return;
+  }
   const int wave = threadIdx.x / kWave;
   if (wave >= j.rows) return;
   const int len = wave == j.rows - 1 ? j.last : j.cols;
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void quant_flat_kernel(const QJob* __rest
                                        1, len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr);
 }
 
-// Code bytes of positions outside every block.
+// Code bytes of positions outside every block (a plan with no block at all).
 __global__ __launch_bounds__(kThreads) void zero_codes_kernel(const QJob* __restrict__ jobs,
                                                               uint8_t* __restrict__ q) {
   const QJob j = jobs[blockIdx.x];
@@ -404,22 +415,32 @@ __device__ void dequant_block(const uint8_t* __restrict__ q, float* __restrict__
   }
 }
 
+// Workgroups from n_main on clear the values outside every block (zero-range
+// jobs), as in the quant kernels.
 template <int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __restrict__ jobs,
+__global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
                                                                 const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ scales,
                                                                 float* __restrict__ out) {
   const QJob j = jobs[blockIdx.x];
+  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+    zero_f32(out, j.base, j.stride, threadIdx.x);
+    return;
+  }
   dequant_block<FMT, HW, kThreads>(q, out, scales[j.scale], j.base, j.stride, j.rows, j.cols,
                                    threadIdx.x);
 }
 
 template <int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs,
+__global__ __launch_bounds__(kThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
                                                                 const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ scales,
                                                                 float* __restrict__ out) {
   const QJob j = jobs[blockIdx.x];
+  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+    zero_f32(out, j.base, j.stride, threadIdx.x);
+    return;
+  }
   const int wave = threadIdx.x / kWave;
   if (wave >= j.rows) return;
   const int len = wave == j.rows - 1 ? j.last : j.cols;
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void dequant_flat_kernel(const QJob* __re
                                 len, 1, len, threadIdx.x & (kWave - 1));
 }
 
-// Dequantised values of positions outside every block.
+// Dequantised values of positions outside every block (a plan with no block at all).
 __global__ __launch_bounds__(kThreads) void zero_values_kernel(const QJob* __restrict__ jobs,
                                                                float* __restrict__ out) {
   const QJob j = jobs[blockIdx.x];
@@ -1076,17 +1097,24 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
 
 namespace {
 
+// The zero-range jobs follow the flat groups, which follow the tiles: they ride
+// at the end of the last launch that has blocks, or get their own launch.
 template <bool BF16, int FMT, bool HW>
 void launch_quant_kinds(const rs_plan* p, const void* src, uint8_t* q, float* scales, hipStream_t s) {
   const dim3 block(kThreads);
   const QJob* tiles = p->qjobs;
   const QJob* flats = tiles + p->n_qtile;
-  if (p->n_qtile)
-    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qtile)), block,
-                       0, s, tiles, src, q, scales);
+  const int64_t nz = p->n_qzero;
+  if (p->n_qtile) {
+    const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
+    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(n)), block, 0, s, tiles,
+                       p->n_qtile, src, q, scales);
+  }
   if (p->n_qflat)
-    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat)), block,
-                       0, s, flats, src, q, scales);
+    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), block,
+                       0, s, flats, p->n_qflat, src, q, scales);
+  if (!p->n_qtile && !p->n_qflat && nz)
+    hipLaunchKernelGGL(zero_codes_kernel, dim3(static_cast<unsigned>(nz)), block, 0, s, flats, q);
 }
 
 template <bool BF16>
@@ -1100,9 +1128,6 @@ void launch_quant(const rs_plan* p, const void* src, int fmt, bool hw, uint8_t* 
     launch_quant_kinds<BF16, FMT_I8, false>(p, src, q, scales, s);
   else
     launch_quant_kinds<BF16, FMT_U8, false>(p, src, q, scales, s);
-  if (p->n_qzero)
-    hipLaunchKernelGGL(zero_codes_kernel, dim3(static_cast<unsigned>(p->n_qzero)), dim3(kThreads), 0, s,
-                       p->qjobs + p->n_qtile + p->n_qflat, q);
 }
 
 template <int FMT, bool HW>
@@ -1110,15 +1135,17 @@ void launch_dequant(const rs_plan* p, const uint8_t* q, const float* scales, flo
   const dim3 block(kThreads);
   const QJob* tiles = p->qjobs;
   const QJob* flats = tiles + p->n_qtile;
-  if (p->n_qtile)
-    hipLaunchKernelGGL((dequant_tile_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qtile)), block, 0, s,
-                       tiles, q, scales, out);
+  const int64_t nz = p->n_qzero;
+  if (p->n_qtile) {
+    const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
+    hipLaunchKernelGGL((dequant_tile_kernel<FMT, HW>), dim3(static_cast<unsigned>(n)), block, 0, s, tiles,
+                       p->n_qtile, q, scales, out);
+  }
   if (p->n_qflat)
-    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat)), block, 0, s,
-                       flats, q, scales, out);
-  if (p->n_qzero)
-    hipLaunchKernelGGL(zero_values_kernel, dim3(static_cast<unsigned>(p->n_qzero)), block, 0, s,
-                       flats + p->n_qflat, out);
+    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), block, 0, s,
+                       flats, p->n_qflat, q, scales, out);
+  if (!p->n_qtile && !p->n_qflat && nz)
+    hipLaunchKernelGGL(zero_values_kernel, dim3(static_cast<unsigned>(nz)), block, 0, s, flats, out);
 }
 
 int fmt_of(int32_t q_dt) {

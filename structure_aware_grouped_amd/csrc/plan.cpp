@@ -379,6 +379,14 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
 
     Tables tb;
     lower(t, S, R_mat, &tb);
+    const int64_t longest = std::max({static_cast<int64_t>(tb.unpack.size()), static_cast<int64_t>(tb.tm.size()),
+                                      static_cast<int64_t>(tb.pack.size()), static_cast<int64_t>(tb.qjobs.size()),
+                                      static_cast<int64_t>(tb.gchunks.size()),
+                                      static_cast<int64_t>(tb.gjobs.size())});
+    if (longest > kMaxWorkgroups)
+      return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(longest) +
+                                 " work items in one launch; at most " + std::to_string(kMaxWorkgroups) +
+                                 " fit a dispatch");
 
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess) return fail(RS_EHIP, "rs_plan_load: no HIP device");

@@ -7,8 +7,8 @@
 // lies a multiple of its atomic block size g from the tensor's start, with S
 // as small as possible.
 //
-// Method (same walkthrough, "the planner first fixes a tensor order" and the
-// two paragraphs after it; bud-325 summary, Method (2)):
+// Method (same walkthrough, the planner's tensor-order paragraph and the two
+// paragraphs after it; bud-325 summary, Method (2)):
 //   * three orders: the caller's, block size descending, shape descending;
 //   * for one order and one S, feasibility is decided by placing each tensor
 //     at the first valid start after the previous one (the DP's state f(i, j)

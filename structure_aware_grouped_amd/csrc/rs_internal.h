@@ -28,6 +28,9 @@ constexpr int64_t kUnpackChunk = RS_UNPACK_CHUNK;   // elements per unpack work 
 constexpr int64_t kPackChunk = RS_PACK_CHUNK;       // output elements per pack work item
 constexpr int64_t kZeroChunk = RS_ZERO_CHUNK;       // elements per zero-fill work item
 static_assert(kUnpackChunk % 16 == 0 && kPackChunk % 16 == 0, "work items keep 16-element alignment");
+// Every launch uses 256-thread workgroups, and a dispatch counts its grid in
+// work-items with 32 bits: one list may hold at most this many work items.
+constexpr int64_t kMaxWorkgroups = 0xFFFFFFFFll / 256;
 constexpr int kFlatPerGroup = 4;          // flat quant blocks per 256-thread group (one per wave)
 
 // One tensor of a loaded plan.
