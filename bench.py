@@ -36,7 +36,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
 METRIC = "DBuffer pack/unpack+blockquant GB/s, % HBM peak (Llama-3-8B layer, V=64)"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_llama3_8b_v64.md")
+# committed counter summaries: (workload, mode, tile-major) -> profiles/traffic_<name>.md
+PROFILE_TRAFFIC = {(1, "step", False): "llama3_8b_v64", (1, "step", True): "llama3_8b_v64_tile_major",
+                   (1, "fp8_gather", False): "llama3_8b_v64_fp8_gather", (4, "adam8", False): "adam8_llama3_8b_v64"}
 KERNEL_SOURCES = [os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", f)
                   for f in ("kernels.hip", "rs_internal.h", "plan.cpp")]
 
@@ -122,62 +124,20 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """Measured HBM bytes per launch of `kernel` from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def read_traffic(key, kernel: str):
+    """Measured HBM bytes per launch of bench step `kernel` from the committed counter
+    summary of this configuration, if there is one and it was taken on the current
+    kernel source; else None."""
+    name = PROFILE_TRAFFIC.get(key)
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.md") if name else None
+    if not path or not os.path.exists(path):
         return None
-    text = open(PROFILE_TRAFFIC).read()
+    text = open(path).read()
     m = re.search(r"kernel sources sha256\[:16\]:\s*`?([0-9a-f]{16})", text, re.I)
     if not m or m.group(1) != kernel_hash():
         return None
     m = re.search(rf"^\|\s*{kernel}\s*\|[^\n]*?\|\s*([0-9]+)\s*\|\s*$", text, re.M)
     return int(m.group(1)) if m else None
-
-
-class HipTimer:
-    """HIP timing events recorded on a given stream.
-
-    By default the events are created with hipEventDisableSystemFence: recording
-    one then costs no system-scope cache writeback and invalidation between the
-    kernels it separates (a default event record adds about 10 us of idle GPU
-    time at every boundary of this step). The events are only read after a
-    device-wide synchronisation, which is what that flag requires. The HIP
-    runtime is the one torch loaded."""
-    DISABLE_SYSTEM_FENCE = 0x20000000
-
-    def __init__(self, torch, fenced: bool = False):
-        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
-        hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
-        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
-        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.hip, self.flags, self.events = hip, 0 if fenced else self.DISABLE_SYSTEM_FENCE, []
-
-    @staticmethod
-    def _ok(rc, what):
-        if rc != 0:
-            raise RuntimeError(f"{what} failed with HIP error {rc}")
-
-    def event(self):
-        e = ctypes.c_void_p()
-        self._ok(self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.flags), "hipEventCreateWithFlags")
-        self.events.append(e)
-        return e
-
-    def record(self, e, stream: int):
-        self._ok(self.hip.hipEventRecord(e, ctypes.c_void_p(stream)), "hipEventRecord")
-
-    def ms(self, a, b) -> float:
-        t = ctypes.c_float()
-        self._ok(self.hip.hipEventElapsedTime(ctypes.byref(t), a, b), "hipEventElapsedTime")
-        return t.value
-
-    def close(self):
-        for e in self.events:
-            self.hip.hipEventDestroy(e)
-        self.events = []
 
 
 def cpu_baseline(w, plan, names=None) -> dict:
@@ -410,9 +370,7 @@ def main():
         check = "skipped (the Adam step is checked by tests/test_gpu_adam.py)"
     dom_avg_s = per_kernel[dominant]["avg_ms"] * 1e-3
     achieved = nbytes[dominant] / dom_avg_s / 1e9
-    # the committed counter summary covers the headline workload only
-    headline = args.workload == 1 and args.mode == "step" and not args.tile_major
-    traffic = read_traffic(dominant) if headline else None
+    traffic = read_traffic((args.workload, args.mode, bool(args.tile_major)), dominant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant])}

@@ -33,12 +33,6 @@ constexpr int kWave = 64;
 #ifndef RS_NT
 #define RS_NT 1
 #endif
-#ifndef RS_UNPACK_U
-#define RS_UNPACK_U 8
-#endif
-#ifndef RS_PACK_U
-#define RS_PACK_U 8
-#endif
 // Streamed data is touched once: load and store it with the nontemporal hint
 // so it does not displace anything in L2 / MALL.
 constexpr bool kNT = RS_NT != 0;
@@ -313,66 +307,72 @@ __device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ 
   }
 }
 
-// Zero [base, base + len) of a byte array (codes) with 16-byte stores in the middle.
+// Zero [base, base + len) of a byte array (codes) with 16-byte stores in the
+// middle, by NT threads.
+template <int NT = kThreads>
 __device__ void zero_bytes(uint8_t* q, int64_t base, int64_t len, int tid) {
   const int64_t end = base + len;
   const int64_t a0 = (base + 15) & ~int64_t(15);
   const int64_t a1 = end & ~int64_t(15);
   if (a0 >= a1) {
-    for (int64_t i = base + tid; i < end; i += kThreads) q[i] = 0;
+    for (int64_t i = base + tid; i < end; i += NT) q[i] = 0;
     return;
   }
-  for (int64_t i = base + tid; i < a0; i += kThreads) q[i] = 0;
-  for (int64_t i = a1 + tid; i < end; i += kThreads) q[i] = 0;
+  for (int64_t i = base + tid; i < a0; i += NT) q[i] = 0;
+  for (int64_t i = a1 + tid; i < end; i += NT) q[i] = 0;
   u32x4* v = reinterpret_cast<u32x4*>(q + a0);
   const int64_t nv = (a1 - a0) >> 4;
-  for (int64_t i = tid; i < nv; i += kThreads) stg(v + i, u32x4{0u, 0u, 0u, 0u});
+  for (int64_t i = tid; i < nv; i += NT) stg(v + i, u32x4{0u, 0u, 0u, 0u});
 }
 
-// Zero [base, base + len) of an fp32 array with 16-byte stores in the middle.
+// Zero [base, base + len) of an fp32 array with 16-byte stores in the
+// middle, by NT threads.
+template <int NT = kThreads>
 __device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
   const int64_t end = base + len;
   const int64_t a0 = (base + 3) & ~int64_t(3);
   const int64_t a1 = end & ~int64_t(3);
   if (a0 >= a1) {
-    for (int64_t i = base + tid; i < end; i += kThreads) o[i] = 0.0f;
+    for (int64_t i = base + tid; i < end; i += NT) o[i] = 0.0f;
     return;
   }
-  for (int64_t i = base + tid; i < a0; i += kThreads) o[i] = 0.0f;
-  for (int64_t i = a1 + tid; i < end; i += kThreads) o[i] = 0.0f;
+  for (int64_t i = base + tid; i < a0; i += NT) o[i] = 0.0f;
+  for (int64_t i = a1 + tid; i < end; i += NT) o[i] = 0.0f;
   f32x4* v = reinterpret_cast<f32x4*>(o + a0);
   const int64_t nv = (a1 - a0) >> 2;
-  for (int64_t i = tid; i < nv; i += kThreads) stg(v + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+  for (int64_t i = tid; i < nv; i += NT) stg(v + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 }
 
 // One workgroup per tile. Workgroups from n_main on take the zero-range jobs
 // that follow the tiles in the list and clear code bytes outside every block,
 // so the whole call is one launch.
+// kQuantThreads threads per tile; the register path holds a whole tile of up
+// to 16384 elements (2048 16-byte vectors of bf16, 4096 of fp32).
 template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void quant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
-                                                              const void* __restrict__ src,
-                                                              uint8_t* __restrict__ q,
-                                                              float* __restrict__ scales) {
-  __shared__ uint32_t red[kThreads / kWave];
+__global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                                   const void* __restrict__ src,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ scales) {
+  __shared__ uint32_t red[kQuantThreads / kWave];
   const QJob j = jobs[blockIdx.x];
   if (static_cast<int64_t>(blockIdx.x) >= n_main) {
-    zero_bytes(q, j.base, j.stride, threadIdx.x);
+    zero_bytes<kQuantThreads>(q, j.base, j.stride, threadIdx.x);
     return;
   }
-  quant_block<BF16, FMT, HW, kThreads, BF16 ? 8 : 16>(src, q, scales, j.base, j.stride, j.rows, j.cols,
-                                                       j.scale, threadIdx.x, red);
+  quant_block<BF16, FMT, HW, kQuantThreads, (BF16 ? 2048 : 4096) / kQuantThreads>(
+      src, q, scales, j.base, j.stride, j.rows, j.cols, j.scale, threadIdx.x, red);
 }
 
-// One wave per flat block, up to four blocks per workgroup; zero-range jobs
+// One wave per flat block, kFlatPerGroup blocks per workgroup; zero-range jobs
 // from n_main on, as in the tile kernel.
 template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+__global__ __launch_bounds__(kFlatThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
                                                               const void* __restrict__ src,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ scales) {
   const QJob j = jobs[blockIdx.x];
   if (static_cast<int64_t>(blockIdx.x) >= n_main) {
-    zero_bytes(q, j.base, j.stride, threadIdx.x);
+    zero_bytes<kFlatThreads>(q, j.base, j.stride, threadIdx.x);
     return;
   }
   const int wave = threadIdx.x / kWave;
@@ -432,13 +432,13 @@ __global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __re
 }
 
 template <int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+__global__ __launch_bounds__(kFlatThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
                                                                 const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ scales,
                                                                 float* __restrict__ out) {
   const QJob j = jobs[blockIdx.x];
   if (static_cast<int64_t>(blockIdx.x) >= n_main) {
-    zero_f32(out, j.base, j.stride, threadIdx.x);
+    zero_f32<kFlatThreads>(out, j.base, j.stride, threadIdx.x);
     return;
   }
   const int wave = threadIdx.x / kWave;
@@ -519,36 +519,46 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
   }
 }
 
+// floor(n / d) for n < 2^16 and 1 <= d < 2^16 with m = magic_u16(d) =
+// ceil(2^32 / d): n*m / 2^32 exceeds n/d by less than 2^-16 < 1/d, which
+// never carries past the next integer.
+__device__ __forceinline__ uint32_t magic_u16(uint32_t d) { return d == 1 ? 0u : 0xFFFFFFFFu / d + 1u; }
+__device__ __forceinline__ uint32_t div_u16(uint32_t n, uint32_t d, uint32_t m) {
+  return d == 1 ? n : __umulhi(n, m);
+}
+
 // Contiguous row runs of a quantised tensor (see GatherChunk). Each lane turns
 // VEC codes into one 16-byte store (8 codes -> 8 bf16, 4 codes -> 4 fp32), so
-// the lanes of a wave read and write one contiguous range each; eight vectors
-// in flight per thread. A TILE run's rows share the band's scales: the scale
-// of every column vector is staged in LDS once per workgroup.
+// the lanes of a wave read and write one contiguous range each. Workgroup b
+// takes piece b % split of run b / split: kGatherVec vectors per thread, and
+// again split pieces further on while the run lasts. A run of several rows
+// holds fewer than 2^16 vectors (the lowering keeps it under 16384 elements),
+// so its row and tile-column indices come from div_u16.
 template <int FMT, bool HW, bool BF16OUT>
-__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const GatherChunk* __restrict__ chunks,
-                                                               const uint8_t* __restrict__ q,
-                                                               const float* __restrict__ scales,
-                                                               void* const* __restrict__ dst) {
+__global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(const GatherChunk* __restrict__ chunks,
+                                                                    const uint8_t* __restrict__ q,
+                                                                    const float* __restrict__ scales,
+                                                                    void* const* __restrict__ dst, int split) {
   constexpr int VEC = BF16OUT ? 8 : 4;
-  constexpr int U = 8;
-  __shared__ float col_scale[kGatherMaxCols / 4];
-  const GatherChunk c = chunks[blockIdx.x];
+  constexpr int U = kGatherVec;
+  const int ci = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
+  const int piece = static_cast<int>(blockIdx.x) - ci * split;
+  const GatherChunk c = chunks[ci];
   void* out = dst[c.tensor];
-  const int vpr = c.cols / VEC;
-  const int nvec = c.rows * vpr;
+  const uint32_t vpr = static_cast<uint32_t>(c.cols / VEC);
+  const int nvec = c.rows * static_cast<int>(vpr);
   const uint8_t* qb = q + c.qbase;
   const bool band = c.rstep == 0;
-  if (band) {
-    for (int t = threadIdx.x; t < vpr; t += kThreads) col_scale[t] = scales[c.scale0 + (t * VEC) / c.bc];
-    __syncthreads();
-  }
-  GridWalk w(threadIdx.x, vpr, kThreads);
-  for (int i0 = threadIdx.x; i0 < nvec; i0 += kThreads * U) {
+  const uint32_t mv = magic_u16(vpr);
+  const uint32_t cpt = band ? static_cast<uint32_t>(c.bc / VEC) : 1u;   // vectors per tile column
+  const uint32_t mc = magic_u16(cpt);
+  const int pass = split * static_cast<int>(kGatherPiece);
+  for (int i0 = piece * static_cast<int>(kGatherPiece) + static_cast<int>(threadIdx.x); i0 < nvec; i0 += pass) {
     uint32_t code[U][VEC / 4];
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kThreads;
+      const int i = i0 + u * kGatherThreads;
       if (i < nvec) {
         if constexpr (VEC == 8) {
           const u32x2 t = ldg(reinterpret_cast<const u32x2*>(qb) + i);
@@ -557,13 +567,18 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const GatherChunk
         } else {
           code[u][0] = ldg(reinterpret_cast<const uint32_t*>(qb) + i);
         }
-        sc[u] = band ? col_scale[w.col] : scales[c.scale0 + w.row];
+        const uint32_t row = c.rows == 1 ? 0u : div_u16(static_cast<uint32_t>(i), vpr, mv);
+        if (band) {
+          const uint32_t col = static_cast<uint32_t>(i) - row * vpr;
+          sc[u] = scales[c.scale0 + div_u16(col, cpt, mc)];
+        } else {
+          sc[u] = scales[c.scale0 + row];
+        }
       }
-      w.next();
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * kThreads;
+      const int i = i0 + u * kGatherThreads;
       if (i >= nvec) continue;
       const int64_t e = c.toff + static_cast<int64_t>(i) * VEC;
       float v[VEC];
@@ -597,7 +612,7 @@ __global__ __launch_bounds__(kThreads) void gather_tile_kernel(const QJob* __res
 }
 
 template <int FMT, bool HW, bool BF16OUT>
-__global__ __launch_bounds__(kThreads) void gather_flat_kernel(const QJob* __restrict__ jobs,
+__global__ __launch_bounds__(kFlatThreads) void gather_flat_kernel(const QJob* __restrict__ jobs,
                                                                const uint8_t* __restrict__ q,
                                                                const float* __restrict__ scales,
                                                                void* const* __restrict__ dst) {
@@ -744,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restr
                           threadIdx.x, red, k);
 }
 
-__global__ __launch_bounds__(kThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
+__global__ __launch_bounds__(kFlatThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
                                                              const float* grad, uint8_t* qm, float* sm,
                                                              uint8_t* qv, float* sv, AdamK k) {
   const QJob j = jobs[blockIdx.x];
@@ -757,28 +772,30 @@ __global__ __launch_bounds__(kThreads) void adam_flat_kernel(const QJob* __restr
 
 // ------------------------------------------------------------------ unpack
 
-template <int U>
-__global__ __launch_bounds__(kThreads) void unpack_kernel(const CopyChunk* __restrict__ chunks,
-                                                          const uint8_t* __restrict__ gathered,
-                                                          void* const* __restrict__ dst, int eb) {
-  const CopyChunk c = chunks[blockIdx.x];
+// Workgroup b copies piece b % split (kUnpackPiece vectors) of chunk b / split.
+__global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(const CopyChunk* __restrict__ chunks,
+                                                               const uint8_t* __restrict__ gathered,
+                                                               void* const* __restrict__ dst, int eb,
+                                                               int split) {
+  const int ci = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
+  const int piece = static_cast<int>(blockIdx.x) - ci * split;
+  const CopyChunk c = chunks[ci];
   const uint8_t* s = gathered + c.src * eb;
   uint8_t* d = static_cast<uint8_t*>(dst[c.tensor]) + c.off * eb;
   const int nbytes = c.len * eb;
   const int nvec = nbytes >> 4;
+  const int v0 = piece * static_cast<int>(kUnpackPiece) + static_cast<int>(threadIdx.x);
   const u32x4* s4 = reinterpret_cast<const u32x4*>(s);
   u32x4* d4 = reinterpret_cast<u32x4*>(d);
-  for (int b = threadIdx.x; b < nvec; b += kThreads * U) {
-    u32x4 r[U];
+  u32x4 r[kUnpackVec];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (b + u * kThreads < nvec) r[u] = ldg(s4 + b + u * kThreads);
+  for (int u = 0; u < kUnpackVec; ++u)
+    if (v0 + u * kUnpackThreads < nvec) r[u] = ldg(s4 + v0 + u * kUnpackThreads);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (b + u * kThreads < nvec) stg(d4 + b + u * kThreads, r[u]);
-  }
+  for (int u = 0; u < kUnpackVec; ++u)
+    if (v0 + u * kUnpackThreads < nvec) stg(d4 + v0 + u * kUnpackThreads, r[u]);
   const int tail = nbytes & 15;
-  if (static_cast<int>(threadIdx.x) < tail) d[(nvec << 4) + threadIdx.x] = s[(nvec << 4) + threadIdx.x];
+  if (piece == 0 && static_cast<int>(threadIdx.x) < tail) d[(nvec << 4) + threadIdx.x] = s[(nvec << 4) + threadIdx.x];
 }
 
 // ------------------------------------------------------------------ pack
@@ -803,65 +820,69 @@ __device__ __forceinline__ float load1(const void* p, int64_t e) {
 }
 
 // packed = acc ? prev + src*sigma : src*sigma on tensor data, +0.0 on padding.
-// `prev` may alias `out`: every element is read before it is written, by the
-// same thread.
-template <bool BF16, bool ACC, int U>
-__global__ __launch_bounds__(kThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
-                                                        const void* const* __restrict__ src,
-                                                        const float* prev, float* out, float sigma) {
-  const PackChunk c = chunks[blockIdx.x];
+// Workgroup b writes piece b % kPackSplit (kPackPiece output vectors) of
+// chunk b / kPackSplit. `prev` may alias `out`: every element is read before
+// it is written, by the same thread.
+template <bool BF16, bool ACC>
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
+                                                             const void* const* __restrict__ src,
+                                                             const float* prev, float* out, float sigma) {
+  const int ci = static_cast<int>(blockIdx.x / static_cast<unsigned>(kPackSplit));
+  const int piece = static_cast<int>(blockIdx.x) - ci * static_cast<int>(kPackSplit);
+  const PackChunk c = chunks[ci];
   f32x4* o4 = reinterpret_cast<f32x4*>(out + c.out);
   const int nv = c.n_total >> 2;
+  const int v0 = piece * static_cast<int>(kPackPiece) + static_cast<int>(threadIdx.x);
   if (c.tensor < 0) {
-    for (int i = threadIdx.x; i < nv; i += kThreads) stg(o4 + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+    for (int u = 0; u < kPackVec; ++u)
+      if (v0 + u * kPackThreads < nv) stg(o4 + v0 + u * kPackThreads, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
     return;
   }
   const void* g = src[c.tensor];
   const int nd = c.n_data;
   const f32x4* p4 = reinterpret_cast<const f32x4*>(prev + c.out);
-  for (int b = threadIdx.x; b < nv; b += kThreads * U) {
-    f32x4 gv[U], pv[U];
+  f32x4 gv[kPackVec], pv[kPackVec];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = b + u * kThreads;
-      if (i < nv && 4 * i + 4 <= nd) {
-        gv[u] = load4<BF16>(g, c.off + 4 * i);
-        if constexpr (ACC) pv[u] = ldg(p4 + i);
-      }
+  for (int u = 0; u < kPackVec; ++u) {
+    const int i = v0 + u * kPackThreads;
+    if (i < nv && 4 * i + 4 <= nd) {
+      gv[u] = load4<BF16>(g, c.off + 4 * i);
+      if constexpr (ACC) pv[u] = ldg(p4 + i);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = b + u * kThreads;
-      if (i >= nv) continue;
-      f32x4 y;
-      if (4 * i + 4 <= nd) {
-        y.x = __fmul_rn(gv[u].x, sigma);
-        y.y = __fmul_rn(gv[u].y, sigma);
-        y.z = __fmul_rn(gv[u].z, sigma);
-        y.w = __fmul_rn(gv[u].w, sigma);
-        if constexpr (ACC) {
-          y.x = __fadd_rn(pv[u].x, y.x);
-          y.y = __fadd_rn(pv[u].y, y.y);
-          y.z = __fadd_rn(pv[u].z, y.z);
-          y.w = __fadd_rn(pv[u].w, y.w);
-        }
-      } else {
-        float t[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int e = 4 * i + k;
-          if (e < nd) {
-            float v = __fmul_rn(load1<BF16>(g, c.off + e), sigma);
-            if constexpr (ACC) v = __fadd_rn(prev[c.out + e], v);
-            t[k] = v;
-          } else {
-            t[k] = 0.0f;
-          }
-        }
-        y = f32x4{t[0], t[1], t[2], t[3]};
+  for (int u = 0; u < kPackVec; ++u) {
+    const int i = v0 + u * kPackThreads;
+    if (i >= nv) continue;
+    f32x4 y;
+    if (4 * i + 4 <= nd) {
+      y.x = __fmul_rn(gv[u].x, sigma);
+      y.y = __fmul_rn(gv[u].y, sigma);
+      y.z = __fmul_rn(gv[u].z, sigma);
+      y.w = __fmul_rn(gv[u].w, sigma);
+      if constexpr (ACC) {
+        y.x = __fadd_rn(pv[u].x, y.x);
+        y.y = __fadd_rn(pv[u].y, y.y);
+        y.z = __fadd_rn(pv[u].z, y.z);
+        y.w = __fadd_rn(pv[u].w, y.w);
       }
-      stg(o4 + i, y);
+    } else {
+      float t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * i + k;
+        if (e < nd) {
+          float v = __fmul_rn(load1<BF16>(g, c.off + e), sigma);
+          if constexpr (ACC) v = __fadd_rn(prev[c.out + e], v);
+          t[k] = v;
+        } else {
+          t[k] = 0.0f;
+        }
+      }
+      y = f32x4{t[0], t[1], t[2], t[3]};
     }
+    stg(o4 + i, y);
   }
 }
 
@@ -1033,9 +1054,11 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
   st = sync_table(p, &p->dst, dst, s, who);
   if (st != RS_OK) return st;
   const uint8_t* gb = static_cast<const uint8_t*>(gathered);
-  if (p->n_unpack)
-    hipLaunchKernelGGL(unpack_kernel<RS_UNPACK_U>, dim3(static_cast<unsigned>(p->n_unpack)), dim3(kThreads), 0, s,
-                       p->unpack, gb, p->dst.dev, eb);
+  if (p->n_unpack) {
+    const int64_t split = unpack_split(eb);
+    hipLaunchKernelGGL(unpack_kernel, dim3(static_cast<unsigned>(p->n_unpack * split)), dim3(kUnpackThreads), 0, s,
+                       p->unpack, gb, p->dst.dev, eb, static_cast<int>(split));
+  }
   if (p->n_tm) {
     const dim3 g(static_cast<unsigned>(p->n_tm));
     if (eb == 4) hipLaunchKernelGGL(unpack_tm_kernel<4>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
@@ -1071,15 +1094,15 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_table(p, &p->src, src, s, who);
   if (st != RS_OK) return st;
-  const dim3 grid(static_cast<unsigned>(p->n_pack)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(p->n_pack * kPackSplit)), sblock(kPackThreads), block(kThreads);
   void** tab = p->src.dev;
   if (p->n_pack) {
     if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_kernel<false, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
-      else hipLaunchKernelGGL((pack_kernel<false, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+      if (prev) hipLaunchKernelGGL((pack_kernel<false, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
+      else hipLaunchKernelGGL((pack_kernel<false, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
     } else {
-      if (prev) hipLaunchKernelGGL((pack_kernel<true, true, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
-      else hipLaunchKernelGGL((pack_kernel<true, false, RS_PACK_U>), grid, block, 0, s, p->pack, tab, prev, packed, sigma);
+      if (prev) hipLaunchKernelGGL((pack_kernel<true, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
+      else hipLaunchKernelGGL((pack_kernel<true, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
     }
   }
   if (p->n_tm) {
@@ -1107,11 +1130,11 @@ void launch_quant_kinds(const rs_plan* p, const void* src, uint8_t* q, float* sc
   const int64_t nz = p->n_qzero;
   if (p->n_qtile) {
     const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
-    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(n)), block, 0, s, tiles,
+    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(n)), dim3(kQuantThreads), 0, s, tiles,
                        p->n_qtile, src, q, scales);
   }
   if (p->n_qflat)
-    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), block,
+    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), dim3(kFlatThreads),
                        0, s, flats, p->n_qflat, src, q, scales);
   if (!p->n_qtile && !p->n_qflat && nz)
     hipLaunchKernelGGL(zero_codes_kernel, dim3(static_cast<unsigned>(nz)), block, 0, s, flats, q);
@@ -1142,7 +1165,7 @@ void launch_dequant(const rs_plan* p, const uint8_t* q, const float* scales, flo
                        p->n_qtile, q, scales, out);
   }
   if (p->n_qflat)
-    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), block, 0, s,
+    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), dim3(kFlatThreads), 0, s,
                        flats, p->n_qflat, q, scales, out);
   if (!p->n_qtile && !p->n_qflat && nz)
     hipLaunchKernelGGL(zero_values_kernel, dim3(static_cast<unsigned>(nz)), block, 0, s, flats, out);
@@ -1210,15 +1233,17 @@ void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipS
   const dim3 block(kThreads);
   const QJob* tiles = p->gjobs;
   const QJob* flats = tiles + p->n_gtile;
-  if (p->n_gchunks)
-    hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gchunks)),
-                       block, 0, s, p->gchunks, q, scales, p->gdst.dev);
+  if (p->n_gchunks) {
+    const int64_t split = gather_split(BF16OUT ? 8 : 4);
+    hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gchunks * split)),
+                       dim3(kGatherThreads), 0, s, p->gchunks, q, scales, p->gdst.dev, static_cast<int>(split));
+  }
   if (p->n_gtile)
     hipLaunchKernelGGL((gather_tile_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gtile)),
                        block, 0, s, tiles, q, scales, p->gdst.dev);
   if (p->n_gflat)
     hipLaunchKernelGGL((gather_flat_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gflat)),
-                       block, 0, s, flats, q, scales, p->gdst.dev);
+                       dim3(kFlatThreads), 0, s, flats, q, scales, p->gdst.dev);
 }
 
 template <bool BF16OUT>
@@ -1295,7 +1320,7 @@ extern "C" int rs_adam8_step(rs_plan* p, float* param, const float* grad, void* 
     hipLaunchKernelGGL(adam_tile_kernel, dim3(static_cast<unsigned>(p->n_qtile)), dim3(kThreads), 0, s,
                        p->qjobs, param, grad, qmb, s_m, qvb, s_v, k);
   if (p->n_qflat)
-    hipLaunchKernelGGL(adam_flat_kernel, dim3(static_cast<unsigned>(p->n_qflat)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(adam_flat_kernel, dim3(static_cast<unsigned>(p->n_qflat)), dim3(kFlatThreads), 0, s,
                        p->qjobs + p->n_qtile, param, grad, qmb, s_m, qvb, s_v, k);
   return launched(who);
 }

@@ -383,10 +383,14 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
                                       static_cast<int64_t>(tb.pack.size()), static_cast<int64_t>(tb.qjobs.size()),
                                       static_cast<int64_t>(tb.gchunks.size()),
                                       static_cast<int64_t>(tb.gjobs.size())});
-    if (longest > kMaxWorkgroups)
-      return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(longest) +
-                                 " work items in one launch; at most " + std::to_string(kMaxWorkgroups) +
-                                 " fit a dispatch");
+    const int64_t unpack_items = static_cast<int64_t>(tb.unpack.size()) * unpack_split(4) * kUnpackThreads;
+    const int64_t pack_items = static_cast<int64_t>(tb.pack.size()) * kPackSplit * kPackThreads;
+    const int64_t gather_items = static_cast<int64_t>(tb.gchunks.size()) * gather_split(4) * kGatherThreads;
+    const int64_t threads = std::max({unpack_items, pack_items, gather_items});
+    if (longest > kMaxWorkgroups || threads > kMaxWorkItems)
+      return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(longest) + " work items (" +
+                                 std::to_string(threads) + " threads) in one launch, more than a dispatch "
+                                 "holds");
 
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess) return fail(RS_EHIP, "rs_plan_load: no HIP device");
