@@ -140,6 +140,51 @@ def read_traffic(key, kernel: str):
     return int(m.group(1)) if m else None
 
 
+class HipTimer:
+    """HIP timing events recorded on a given stream.
+
+    By default the events are created with hipEventDisableSystemFence: recording
+    one then costs no system-scope cache writeback and invalidation between the
+    kernels it separates (a default event record adds about 10 us of idle GPU
+    time at every boundary of this step). The events are only read after a
+    device-wide synchronisation, which is what that flag requires. The HIP
+    runtime is the one torch loaded."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch, fenced: bool = False):
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip, self.flags, self.events = hip, 0 if fenced else self.DISABLE_SYSTEM_FENCE, []
+
+    @staticmethod
+    def _ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def event(self):
+        e = ctypes.c_void_p()
+        self._ok(self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.flags), "hipEventCreateWithFlags")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream: int):
+        self._ok(self.hip.hipEventRecord(e, ctypes.c_void_p(stream)), "hipEventRecord")
+
+    def ms(self, a, b) -> float:
+        t = ctypes.c_float()
+        self._ok(self.hip.hipEventElapsedTime(ctypes.byref(t), a, b), "hipEventElapsedTime")
+        return t.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def cpu_baseline(w, plan, names=None) -> dict:
     """The CPU oracle (single-threaded NumPy) on a bounded sample of the workload:
     the tensors named in `names` (default: every tensor, i.e. one whole step),
