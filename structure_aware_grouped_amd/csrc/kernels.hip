@@ -226,6 +226,23 @@ struct GridWalk {
   }
 };
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8). piece_index renumbers them so that G consecutive pieces of
+// the buffer run on one XCD (and share its L2 and TLB), while neighbouring
+// groups still alternate between XCDs. The last partial round keeps the
+// identity order. A permutation of [0, n): correctness never depends on it.
+template <unsigned G>
+__device__ __forceinline__ unsigned piece_index(unsigned b, unsigned n) {
+  if constexpr (G <= 1) {
+    return b;
+  } else {
+    constexpr unsigned kRound = 8u * G;
+    if (b >= n - n % kRound) return b;
+    const unsigned slot = b / 8u, xcd = b % 8u;
+    return (slot / G) * kRound + xcd * G + slot % G;
+  }
+}
+
 // ------------------------------------------------------------------ quant
 
 // One quantisation block: element (r, c) at base + r*stride + c, r < rows,
@@ -541,8 +558,9 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(const Gathe
                                                                     void* const* __restrict__ dst, int split) {
   constexpr int VEC = BF16OUT ? 8 : 4;
   constexpr int U = kGatherVec;
-  const int ci = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
-  const int piece = static_cast<int>(blockIdx.x) - ci * split;
+  const unsigned b = piece_index<kGatherXcdGroup>(blockIdx.x, gridDim.x);
+  const int ci = static_cast<int>(b / static_cast<unsigned>(split));
+  const int piece = static_cast<int>(b) - ci * split;
   const GatherChunk c = chunks[ci];
   void* out = dst[c.tensor];
   const uint32_t vpr = static_cast<uint32_t>(c.cols / VEC);
@@ -777,8 +795,9 @@ __global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(const CopyChunk*
                                                                const uint8_t* __restrict__ gathered,
                                                                void* const* __restrict__ dst, int eb,
                                                                int split) {
-  const int ci = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
-  const int piece = static_cast<int>(blockIdx.x) - ci * split;
+  const unsigned b = piece_index<kUnpackXcdGroup>(blockIdx.x, gridDim.x);
+  const int ci = static_cast<int>(b / static_cast<unsigned>(split));
+  const int piece = static_cast<int>(b) - ci * split;
   const CopyChunk c = chunks[ci];
   const uint8_t* s = gathered + c.src * eb;
   uint8_t* d = static_cast<uint8_t*>(dst[c.tensor]) + c.off * eb;
@@ -827,8 +846,9 @@ template <bool BF16, bool ACC>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
                                                              const void* const* __restrict__ src,
                                                              const float* prev, float* out, float sigma) {
-  const int ci = static_cast<int>(blockIdx.x / static_cast<unsigned>(kPackSplit));
-  const int piece = static_cast<int>(blockIdx.x) - ci * static_cast<int>(kPackSplit);
+  const unsigned b = piece_index<kPackXcdGroup>(blockIdx.x, gridDim.x);
+  const int ci = static_cast<int>(b / static_cast<unsigned>(kPackSplit));
+  const int piece = static_cast<int>(b) - ci * static_cast<int>(kPackSplit);
   const PackChunk c = chunks[ci];
   f32x4* o4 = reinterpret_cast<f32x4*>(out + c.out);
   const int nv = c.n_total >> 2;
