@@ -1004,6 +1004,183 @@ __global__ __launch_bounds__(kThreads) void pack_tm_kernel(const TmJob* __restri
   }
 }
 
+// Direct tile-major reorder, no LDS: workgroup b takes piece b % split of
+// strip b / split, kTmThreads vectors (one per thread). Unpack walks the strip
+// in row-major order: consecutive lanes write one contiguous row segment and
+// read bc-element runs of consecutive tiles (256 bytes for 128 bf16 columns).
+// Pack walks it in buffer order: writes and prev reads are contiguous, grad
+// reads are bc-element row runs. Strips hold at most kTmStage elements, so
+// every index below stays under 2^16 and div_u16 applies.
+template <int EB>
+__global__ __launch_bounds__(kTmThreads) void unpack_tm_direct_kernel(const TmJob* __restrict__ jobs,
+                                                                      const uint8_t* __restrict__ gathered,
+                                                                      void* const* __restrict__ dst, int split) {
+  constexpr int VE = 16 / EB;   // elements per 16-byte vector
+  const int ji = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
+  const int piece = static_cast<int>(blockIdx.x) - ji * split;
+  const TmJob j = jobs[ji];
+  const uint32_t bc = static_cast<uint32_t>(j.bc), width = static_cast<uint32_t>(j.k) * bc;
+  const uint32_t mbc = magic_u16(bc);
+  const uint8_t* src = gathered + j.base * EB;
+  uint8_t* out = static_cast<uint8_t*>(dst[j.tensor]) + j.toff * EB;
+  const int stride = split * kTmThreads;
+  if (bc % VE == 0 && j.cols % VE == 0) {
+    const uint32_t wv = width / VE, mw = magic_u16(wv);
+    const int nvec = j.h * static_cast<int>(wv);
+    for (int v = piece * kTmThreads + static_cast<int>(threadIdx.x); v < nvec; v += stride) {
+      const uint32_t r = div_u16(static_cast<uint32_t>(v), wv, mw);
+      const uint32_t col = (static_cast<uint32_t>(v) - r * wv) * VE;
+      const uint32_t t = div_u16(col, bc, mbc), c = col - t * bc;
+      const u32x4 x = ldg(reinterpret_cast<const u32x4*>(src + (static_cast<int64_t>(t) * j.tile_elems + r * bc + c) * EB));
+      stg(reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(r) * j.cols + col) * EB), x);
+    }
+    return;
+  }
+  const int n = j.h * static_cast<int>(width);
+  const uint32_t mw = magic_u16(width);
+  for (int e = piece * kTmThreads + static_cast<int>(threadIdx.x); e < n; e += stride) {
+    const uint32_t r = div_u16(static_cast<uint32_t>(e), width, mw);
+    const uint32_t col = static_cast<uint32_t>(e) - r * width;
+    const uint32_t t = div_u16(col, bc, mbc), c = col - t * bc;
+    const uint8_t* from = src + (static_cast<int64_t>(t) * j.tile_elems + r * bc + c) * EB;
+    uint8_t* to = out + (static_cast<int64_t>(r) * j.cols + col) * EB;
+    for (int b = 0; b < EB; ++b) to[b] = from[b];
+  }
+}
+
+template <bool BF16, bool ACC>
+__global__ __launch_bounds__(kTmThreads) void pack_tm_direct_kernel(const TmJob* __restrict__ jobs,
+                                                                    const void* const* __restrict__ src,
+                                                                    const float* prev, float* out, float sigma,
+                                                                    int split) {
+  const int ji = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
+  const int piece = static_cast<int>(blockIdx.x) - ji * split;
+  const TmJob j = jobs[ji];
+  const uint32_t bc = static_cast<uint32_t>(j.bc), run = static_cast<uint32_t>(j.h) * bc;
+  const uint32_t mbc = magic_u16(bc);
+  const void* g = src[j.tensor];
+  const int stride = split * kTmThreads;
+  if (bc % 4 == 0 && j.cols % 4 == 0) {
+    const uint32_t rv = run / 4, mr = magic_u16(rv);
+    const int nvec = j.k * static_cast<int>(rv);
+    for (int o = piece * kTmThreads + static_cast<int>(threadIdx.x); o < nvec; o += stride) {
+      const uint32_t t = div_u16(static_cast<uint32_t>(o), rv, mr);
+      const uint32_t e = (static_cast<uint32_t>(o) - t * rv) * 4;
+      const uint32_t r = div_u16(e, bc, mbc), c = e - r * bc;
+      const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
+      const f32x4 x = load4<BF16>(g, j.toff + static_cast<int64_t>(r) * j.cols + t * bc + c);
+      f32x4 y{__fmul_rn(x.x, sigma), __fmul_rn(x.y, sigma), __fmul_rn(x.z, sigma), __fmul_rn(x.w, sigma)};
+      if constexpr (ACC) {
+        const f32x4 pv = ldg(reinterpret_cast<const f32x4*>(prev + pos));
+        y = f32x4{__fadd_rn(pv.x, y.x), __fadd_rn(pv.y, y.y), __fadd_rn(pv.z, y.z), __fadd_rn(pv.w, y.w)};
+      }
+      stg(reinterpret_cast<f32x4*>(out + pos), y);
+    }
+    return;
+  }
+  const int n = j.k * static_cast<int>(run);
+  const uint32_t mr = magic_u16(run);
+  for (int o = piece * kTmThreads + static_cast<int>(threadIdx.x); o < n; o += stride) {
+    const uint32_t t = div_u16(static_cast<uint32_t>(o), run, mr);
+    const uint32_t e = static_cast<uint32_t>(o) - t * run;
+    const uint32_t r = div_u16(e, bc, mbc), c = e - r * bc;
+    const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
+    float y = __fmul_rn(load1<BF16>(g, j.toff + static_cast<int64_t>(r) * j.cols + t * bc + c), sigma);
+    if constexpr (ACC) y = __fadd_rn(prev[pos], y);
+    out[pos] = y;
+  }
+}
+
+// Gather side of a tile-major tensor, over the same strips: each lane turns
+// VEC codes of one tile row into one 16-byte store of the row-major tensor
+// (8 codes -> 8 bf16, 4 -> 4 fp32), kGatherVec vectors per thread; tile t of
+// the strip uses scale scale0 + t.
+template <int FMT, bool HW, bool BF16OUT>
+__global__ __launch_bounds__(kGatherThreads) void gather_tm_kernel(const TmJob* __restrict__ jobs,
+                                                                  const uint8_t* __restrict__ q,
+                                                                  const float* __restrict__ scales,
+                                                                  void* const* __restrict__ dst, int split) {
+  constexpr int VEC = BF16OUT ? 8 : 4;
+  constexpr int U = kGatherVec;
+  const int ji = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
+  const int piece = static_cast<int>(blockIdx.x) - ji * split;
+  const TmJob j = jobs[ji];
+  const uint32_t bc = static_cast<uint32_t>(j.bc), width = static_cast<uint32_t>(j.k) * bc;
+  const uint32_t mbc = magic_u16(bc);
+  const uint8_t* qb = q + j.base;
+  void* out = dst[j.tensor];
+  const int pass = split * static_cast<int>(kGatherPiece);
+  if (bc % VEC == 0 && j.cols % VEC == 0) {
+    const uint32_t wv = width / VEC, mw = magic_u16(wv);
+    const int nvec = j.h * static_cast<int>(wv);
+    for (int i0 = piece * static_cast<int>(kGatherPiece) + static_cast<int>(threadIdx.x); i0 < nvec; i0 += pass) {
+      uint32_t code[U][VEC / 4];
+      float sc[U];
+      int64_t dpos[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kGatherThreads;
+        if (i < nvec) {
+          const uint32_t r = div_u16(static_cast<uint32_t>(i), wv, mw);
+          const uint32_t col = (static_cast<uint32_t>(i) - r * wv) * VEC;
+          const uint32_t t = div_u16(col, bc, mbc), c = col - t * bc;
+          const uint8_t* from = qb + static_cast<int64_t>(t) * j.tile_elems + r * bc + c;
+          if constexpr (VEC == 8) {
+            const u32x2 w = ldg(reinterpret_cast<const u32x2*>(from));
+            code[u][0] = w.x;
+            code[u][1] = w.y;
+          } else {
+            code[u][0] = ldg(reinterpret_cast<const uint32_t*>(from));
+          }
+          sc[u] = scales[j.scale0 + t];
+          dpos[u] = j.toff + static_cast<int64_t>(r) * j.cols + col;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i0 + u * kGatherThreads >= nvec) continue;
+        float v[VEC];
+#pragma unroll
+        for (int h = 0; h < VEC / 4; ++h) {
+          const f32x4 d = decode4<FMT, HW>(code[u][h]);
+          v[4 * h] = __fmul_rn(d.x, sc[u]);
+          v[4 * h + 1] = __fmul_rn(d.y, sc[u]);
+          v[4 * h + 2] = __fmul_rn(d.z, sc[u]);
+          v[4 * h + 3] = __fmul_rn(d.w, sc[u]);
+        }
+        if constexpr (BF16OUT) {
+          stg(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + dpos[u]),
+              u32x4{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
+                    bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)});
+        } else {
+          stg(reinterpret_cast<f32x4*>(static_cast<float*>(out) + dpos[u]), f32x4{v[0], v[1], v[2], v[3]});
+        }
+      }
+    }
+    return;
+  }
+  // element path: a piece is kGatherPiece elements, U per thread
+  const int n = j.h * static_cast<int>(width);
+  const uint32_t mw = magic_u16(width);
+  for (int e0 = piece * static_cast<int>(kGatherPiece) + static_cast<int>(threadIdx.x); e0 < n; e0 += pass) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * kGatherThreads;
+      if (e >= n) break;
+      const uint32_t r = div_u16(static_cast<uint32_t>(e), width, mw);
+      const uint32_t col = static_cast<uint32_t>(e) - r * width;
+      const uint32_t t = div_u16(col, bc, mbc), c = col - t * bc;
+      const float v = __fmul_rn(decode1<FMT, HW>(qb[static_cast<int64_t>(t) * j.tile_elems + r * bc + c]),
+                                scales[j.scale0 + t]);
+      const int64_t d = j.toff + static_cast<int64_t>(r) * j.cols + col;
+      if constexpr (BF16OUT)
+        static_cast<uint16_t*>(out)[d] = static_cast<uint16_t>(bf16_rne(v));
+      else
+        static_cast<float*>(out)[d] = v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1079,7 +1256,14 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
     hipLaunchKernelGGL(unpack_kernel, dim3(static_cast<unsigned>(p->n_unpack * split)), dim3(kUnpackThreads), 0, s,
                        p->unpack, gb, p->dst.dev, eb, static_cast<int>(split));
   }
-  if (p->n_tm) {
+  if (p->n_tm && !p->tm_lds) {
+    const int64_t split = tm_split(16 / eb);
+    const dim3 g(static_cast<unsigned>(p->n_tm * split)), b(kTmThreads);
+    const int sp = static_cast<int>(split);
+    if (eb == 4) hipLaunchKernelGGL(unpack_tm_direct_kernel<4>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp);
+    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_direct_kernel<2>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp);
+    else hipLaunchKernelGGL(unpack_tm_direct_kernel<1>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp);
+  } else if (p->n_tm) {
     const dim3 g(static_cast<unsigned>(p->n_tm));
     if (eb == 4) hipLaunchKernelGGL(unpack_tm_kernel<4>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
     else if (eb == 2) hipLaunchKernelGGL(unpack_tm_kernel<2>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
@@ -1125,7 +1309,18 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
       else hipLaunchKernelGGL((pack_kernel<true, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
     }
   }
-  if (p->n_tm) {
+  if (p->n_tm && !p->tm_lds) {
+    const int64_t split = tm_split(4);
+    const dim3 g(static_cast<unsigned>(p->n_tm * split)), b(kTmThreads);
+    const int sp = static_cast<int>(split);
+    if (src_dt == RS_F32) {
+      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<false, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
+      else hipLaunchKernelGGL((pack_tm_direct_kernel<false, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
+    } else {
+      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<true, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
+      else hipLaunchKernelGGL((pack_tm_direct_kernel<true, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
+    }
+  } else if (p->n_tm) {
     const dim3 g(static_cast<unsigned>(p->n_tm));
     if (src_dt == RS_F32) {
       if (prev) hipLaunchKernelGGL((pack_tm_kernel<false, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
@@ -1264,6 +1459,11 @@ void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipS
   if (p->n_gflat)
     hipLaunchKernelGGL((gather_flat_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gflat)),
                        dim3(kFlatThreads), 0, s, flats, q, scales, p->gdst.dev);
+  if (p->n_tm) {
+    const int64_t split = tm_gather_split(BF16OUT ? 8 : 4);
+    hipLaunchKernelGGL((gather_tm_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_tm * split)),
+                       dim3(kGatherThreads), 0, s, p->tmjobs, q, scales, p->gdst.dev, static_cast<int>(split));
+  }
 }
 
 template <bool BF16OUT>
@@ -1296,7 +1496,7 @@ extern "C" int rs_unpack_dequant(rs_plan* p, const void* q, int32_t q_dt, const 
     if (!dst[i]) return fail(RS_EINVAL, std::string(who) + ": null destination " + std::to_string(i));
     if (!aligned16(dst[i])) return fail(RS_EALIGN, std::string(who) + ": destination " + std::to_string(i) + " not 16-byte aligned");
   }
-  if (p->n_gchunks + p->n_gtile + p->n_gflat == 0) return RS_OK;
+  if (p->n_gchunks + p->n_gtile + p->n_gflat + p->n_tm == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_table(p, &p->gdst, dst, s, who);
   if (st != RS_OK) return st;

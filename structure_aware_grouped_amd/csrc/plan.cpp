@@ -4,6 +4,7 @@
 // address mapping: "veScale-FSDP: flexible, structure-aware sharding at
 // 10K-GPU scale", feynmanwiki walkthrough, DBuffer paragraphs).
 #include <algorithm>
+#include <cassert>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -90,8 +91,20 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   const int64_t top = R_mat * S;
   const int64_t n = static_cast<int64_t>(t.size());
 
+  // first scale index of every tensor (tensors in order; tiles row-major, flat blocks in order)
+  std::vector<int64_t> first_scale(n + 1, 0);
+  for (int64_t i = 0; i < n; ++i) {
+    const Tensor& x = t[i];
+    int64_t nb = 0;
+    if (x.kind == RS_TILE) nb = ((x.rows + x.p0 - 1) / x.p0) * ((x.cols + x.p1 - 1) / x.p1);
+    else if (x.kind == RS_TILEMAJOR) nb = x.n / (x.p0 * x.p1);
+    else if (x.kind == RS_FLAT) nb = (x.n + x.p0 - 1) / x.p0;
+    first_scale[i + 1] = first_scale[i] + nb;
+  }
+
   // unpack: every row-major tensor in chunks; TILEMAJOR tensors in strips of
-  // rows across up to k tiles of one tile row (unpack and pack share them)
+  // rows across up to k tiles of one tile row (unpack, pack and the gather side
+  // share them)
   for (int64_t i = 0; i < n; ++i) {
     const Tensor& x = t[i];
     if (x.kind == RS_TILEMAJOR) {
@@ -106,6 +119,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
             j.toff = (tr * br + r0) * x.cols + tc0 * bc;
             j.cols = x.cols;
             j.tile_elems = br * bc;
+            j.scale0 = first_scale[i] + tr * ntc + tc0;
             j.tensor = static_cast<int32_t>(i);
             j.k = static_cast<int32_t>(std::min(k, ntc - tc0));
             j.h = static_cast<int32_t>(std::min(h, br - r0));
@@ -213,6 +227,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     }
   }
   tb->n_qblocks = q;
+  assert(q == first_scale[n]);
   std::vector<std::pair<int64_t, int64_t>> qiv;
   for (const Tensor& x : t)
     if (x.kind == RS_TILE || x.kind == RS_FLAT || x.kind == RS_TILEMAJOR) qiv.push_back({x.start, x.start + x.n});
@@ -249,7 +264,8 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     tile_vec[ti] = t[ti].kind == RS_TILE && t[ti].cols % 16 == 0 && t[ti].p1 % 16 == 0 &&
                    t[ti].cols <= kGatherMaxCols;
   for (const QJob& j : tb->qjobs)
-    if (j.kind == QJOB_TILE && !tile_vec[j.tensor]) tb->gjobs.push_back(j);   // incl. TILEMAJOR tiles
+    if (j.kind == QJOB_TILE && !tile_vec[j.tensor] && t[j.tensor].kind != RS_TILEMAJOR)
+      tb->gjobs.push_back(j);   // TILEMAJOR tensors use the tile-major strips
   q = 0;
   for (int64_t ti = 0; ti < n; ++ti) {
     const Tensor& x = t[ti];
@@ -386,7 +402,8 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     const int64_t unpack_items = static_cast<int64_t>(tb.unpack.size()) * unpack_split(4) * kUnpackThreads;
     const int64_t pack_items = static_cast<int64_t>(tb.pack.size()) * kPackSplit * kPackThreads;
     const int64_t gather_items = static_cast<int64_t>(tb.gchunks.size()) * gather_split(4) * kGatherThreads;
-    const int64_t threads = std::max({unpack_items, pack_items, gather_items});
+    const int64_t tm_items = static_cast<int64_t>(tb.tm.size()) * tm_split(4) * kTmThreads;
+    const int64_t threads = std::max({unpack_items, pack_items, gather_items, tm_items});
     if (longest > kMaxWorkgroups || threads > kMaxWorkItems)
       return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(longest) + " work items (" +
                                  std::to_string(threads) + " threads) in one launch, more than a dispatch "
@@ -421,6 +438,10 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     // RS_E4M3_ENCODER=sw selects the integer encoder, which gives the same codes.
     const char* enc = std::getenv("RS_E4M3_ENCODER");
     p->e4m3_hw = !(enc && std::strcmp(enc, "sw") == 0);
+    // Tile-major unpack / pack: direct kernels by default; RS_TM_KERNEL=lds
+    // selects the LDS-staged ones (same results).
+    const char* tmk = std::getenv("RS_TM_KERNEL");
+    p->tm_lds = tmk && std::strcmp(tmk, "lds") == 0;
 
     const int64_t bytes = align_up(sizeof(TmJob) * std::max<int64_t>(p->n_tm, 1), 256) +
                           align_up(sizeof(CopyChunk) * std::max<int64_t>(p->n_unpack, 1), 256) +

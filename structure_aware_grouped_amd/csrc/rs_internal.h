@@ -149,13 +149,23 @@ struct TmJob {
   int64_t toff;        // row-major offset of element (tr*br + r0, tc0*bc)
   int64_t cols;        // tensor columns (row stride of the tensor)
   int64_t tile_elems;  // br * bc
+  int64_t scale0;      // scale index of tile (tr, tc0); tile t of the job uses scale0 + t
   int32_t tensor;
   int32_t k;
   int32_t h;
   int32_t bc;
 };
 
-constexpr int64_t kTmStage = 8192;   // elements staged in LDS per tile-major job (32 KiB as fp32)
+constexpr int64_t kTmStage = 8192;   // elements per tile-major job (staged in LDS: 32 KiB as fp32)
+// Tile-major reorder: direct (each lane maps its own 16-byte vector between the
+// two layouts, small split workgroups; the default) or staged through LDS (one
+// 256-thread workgroup per job; RS_TM_KERNEL=lds at rs_plan_load).
+#ifndef RS_TM_THREADS
+#define RS_TM_THREADS 64
+#endif
+constexpr int kTmThreads = RS_TM_THREADS;
+// pieces per job for vectors of vec elements (direct kernels)
+constexpr int64_t tm_split(int64_t vec) { return (kTmStage / vec + kTmThreads - 1) / kTmThreads; }
 
 // Gather-side work item: a contiguous run of whole rows of one quantised
 // tensor, inside one band of tiles (TILE) or made of whole flat blocks (FLAT,
@@ -193,6 +203,8 @@ constexpr int kGatherThreads = RS_GATHER_THREADS, kGatherVec = RS_GATHER_VEC;
 constexpr int64_t kGatherPiece = int64_t(kGatherThreads) * kGatherVec;
 // pieces per run for VEC codes per vector; longer runs loop
 constexpr int64_t gather_split(int64_t vec) { return (kGatherChunk / vec + kGatherPiece - 1) / kGatherPiece; }
+// pieces per tile-major gather job (a strip of at most kTmStage elements)
+constexpr int64_t tm_gather_split(int64_t vec) { return (kTmStage / vec + kGatherPiece - 1) / kGatherPiece; }
 
 // Device copy of a per-tensor pointer table plus the host state that decides
 // when it must be uploaded again.
@@ -242,4 +254,5 @@ struct rs_plan {
   rs::PtrTable src;   // pack sources
   rs::PtrTable gdst;  // unpack-dequant destinations
   bool e4m3_hw = false;  // use gfx950's FP8 conversion instructions
+  bool tm_lds = false;   // tile-major unpack / pack staged through LDS instead of the direct kernels
 };

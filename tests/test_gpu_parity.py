@@ -210,10 +210,12 @@ TILE_MAJOR = [
 
 @pytest.mark.parametrize("V", [1, 3, 8])
 @pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
-def test_tile_major_group(gpu_lib, V, pdtype):
-    """Tile-major tensors through unpack / pack (LDS reorder), quant, dequant and the
-    fused unpack-dequant, next to row-major ones."""
+@pytest.mark.parametrize("tm_kernel", ["direct", "lds"])
+def test_tile_major_group(gpu_lib, V, pdtype, tm_kernel, monkeypatch):
+    """Tile-major tensors through unpack / pack (direct reorder, or staged through LDS),
+    quant, dequant and the fused unpack-dequant, next to row-major ones."""
     import structure_aware_grouped_amd as rs
+    monkeypatch.setenv("RS_TM_KERNEL", tm_kernel)
     _full_check(rs, TILE_MAJOR, V, pdtype, 40 + V)
 
 
