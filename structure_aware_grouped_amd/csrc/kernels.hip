@@ -371,8 +371,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* _
                                                                    uint8_t* __restrict__ q,
                                                                    float* __restrict__ scales) {
   __shared__ uint32_t red[kQuantThreads / kWave];
-  const QJob j = jobs[blockIdx.x];
-  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+  const unsigned b = piece_index<kTileXcdGroup>(blockIdx.x, gridDim.x);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
     zero_bytes<kQuantThreads>(q, j.base, j.stride, threadIdx.x);
     return;
   }
@@ -387,8 +388,9 @@ __global__ __launch_bounds__(kFlatThreads) void quant_flat_kernel(const QJob* __
                                                               const void* __restrict__ src,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ scales) {
-  const QJob j = jobs[blockIdx.x];
-  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+  const unsigned b = piece_index<kFlatXcdGroup>(blockIdx.x, gridDim.x);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
     zero_bytes<kFlatThreads>(q, j.base, j.stride, threadIdx.x);
     return;
   }
@@ -439,8 +441,9 @@ __global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __re
                                                                 const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ scales,
                                                                 float* __restrict__ out) {
-  const QJob j = jobs[blockIdx.x];
-  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+  const unsigned b = piece_index<kTileXcdGroup>(blockIdx.x, gridDim.x);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
     zero_f32(out, j.base, j.stride, threadIdx.x);
     return;
   }
@@ -453,8 +456,9 @@ __global__ __launch_bounds__(kFlatThreads) void dequant_flat_kernel(const QJob* 
                                                                 const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ scales,
                                                                 float* __restrict__ out) {
-  const QJob j = jobs[blockIdx.x];
-  if (static_cast<int64_t>(blockIdx.x) >= n_main) {
+  const unsigned b = piece_index<kFlatXcdGroup>(blockIdx.x, gridDim.x);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
     zero_f32<kFlatThreads>(out, j.base, j.stride, threadIdx.x);
     return;
   }
@@ -772,7 +776,8 @@ __global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restr
                                                              const float* grad, uint8_t* qm, float* sm,
                                                              uint8_t* qv, float* sv, AdamK k) {
   __shared__ uint32_t red[2 * kThreads / kWave];
-  const QJob j = jobs[blockIdx.x];
+  const unsigned b = piece_index<kTileXcdGroup>(blockIdx.x, gridDim.x);
+  const QJob j = jobs[b];
   adam_block<kThreads, 4>(param, grad, qm, sm, qv, sv, j.base, j.stride, j.rows, j.cols, j.scale,
                           threadIdx.x, red, k);
 }
@@ -780,7 +785,8 @@ __global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restr
 __global__ __launch_bounds__(kFlatThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
                                                              const float* grad, uint8_t* qm, float* sm,
                                                              uint8_t* qv, float* sv, AdamK k) {
-  const QJob j = jobs[blockIdx.x];
+  const unsigned b = piece_index<kFlatXcdGroup>(blockIdx.x, gridDim.x);
+  const QJob j = jobs[b];
   const int wave = threadIdx.x / kWave;
   if (wave >= j.rows) return;
   const int len = wave == j.rows - 1 ? j.last : j.cols;
