@@ -219,6 +219,29 @@ def test_tile_major_group(gpu_lib, V, pdtype, tm_kernel, monkeypatch):
     _full_check(rs, TILE_MAJOR, V, pdtype, 40 + V)
 
 
+# Big enough that each split or XCD-grouped launch runs whole rounds plus a
+# ragged tail. Pack: more than 2048 pieces of 512 outputs. Row-run gather: more
+# than 1024 pieces. Tile kernels: more than 32 tiles. It also holds partial
+# tiles on unaligned columns, a partial flat block and tile-major tiles.
+MID = [
+    TensorSpec("tiles32", 1024, 1024, "TILE", 32, 32),
+    TensorSpec("tiles64_ragged", 300, 1000, "TILE", 64, 64),
+    TensorSpec("flat2048", 1, 300001, "FLAT", 2048),
+    TensorSpec("tm32x64", 256, 512, "TILEMAJOR", 32, 64),
+    TensorSpec("rows3", 777, 33, "ROWS", 3),
+    TensorSpec("elem", 5000, 1, "ELEM"),
+]
+
+
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_mid_size_group(gpu_lib, pdtype):
+    import structure_aware_grouped_amd as rs
+    S, _, _, _ = rs.rs_plan_build(MID, 7)
+    pieces = 7 * S // 4096 * 8                  # pack pieces: a whole round of 2048 and a tail
+    assert pieces > 2048 and pieces % 2048 != 0
+    _full_check(rs, MID, 7, pdtype, 77)
+
+
 def test_trailing_padding_ranks(gpu_lib):
     """R_mat > R_used: ranks holding only padding come out zero."""
     import structure_aware_grouped_amd as rs
