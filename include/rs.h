@@ -142,9 +142,13 @@ int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t ali
  * Checks (RS_EPLAN unless noted): S > 0 and S % 16 == 0 and every
  * s_i % 16 == 0 (RS_EALIGN); intervals disjoint and inside [0, V*S); no
  * rank boundary inside a tensor except at a multiple of g_i from s_i;
- * R_mat in [R_used, V] (RS_ERANGE); V*S fits int64 (RS_ERANGE); no
- * kernel launch of the plan needs more than (2^32 - 1) / 256 work items
- * (RS_ERANGE: about 2^37 elements of R_mat*S, beyond one device's memory).
+ * R_mat in [R_used, V] (RS_ERANGE); V*S fits int64 (RS_ERANGE);
+ * R_mat*S <= 2^39 elements and fewer than 2^32 work items per launch
+ * (RS_ERANGE; neither limit is reached by a group one device can hold).
+ * Environment read here, once per plan: RS_E4M3_ENCODER=sw selects the
+ * integer E4M3 encoder instead of gfx950's conversion instruction;
+ * RS_TM_KERNEL=lds stages the tile-major reorder of unpack / pack through
+ * LDS instead of the direct kernels. Both give identical results.
  * On success *out owns host memory and one device allocation, released by
  * rs_plan_free. Errors: the above, RS_ENOMEM, RS_EHIP. */
 int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,

@@ -2,12 +2,16 @@
 // RaggedShard / DBuffer layout library.
 //
 // Every kernel is HBM-bound streaming work over plan-indexed work lists made
-// once by rs_plan_load: 16-byte vector loads and stores, one 256-thread
-// workgroup per work item, several independent vectors in flight per thread.
-// Quantisation keeps a whole tile (or, one wave per block, a whole flat
-// block) in registers, so each input byte is read from HBM once; the block
-// absmax is a wave shuffle reduction plus, for tiles, a 4-entry LDS combine.
-// No MFMA: nothing here is a dense contraction.
+// once by rs_plan_load, with 16-byte nontemporal vector loads and stores.
+// The streaming transforms (unpack, pack, the row-run gather, the tile-major
+// reorder) split each work item over small, short-lived workgroups (64-128
+// threads, one or two vectors each), which keep more independent streams in
+// flight on gfx950 than one large workgroup per item; piece_index can keep
+// runs of consecutive pieces on one XCD. Quantisation keeps a whole tile
+// (512 threads) or a whole flat block (one wave) in registers, so each input
+// byte is read from HBM once; the block absmax is a wave shuffle reduction
+// plus, for tiles, an LDS combine over the waves. No MFMA: nothing here is a
+// dense contraction.
 //
 // Arithmetic follows "veScale-FSDP: flexible, structure-aware sharding at
 // 10K-GPU scale" (feynmanwiki walkthrough, DBuffer paragraph on fused add /
@@ -16,6 +20,7 @@
 // (__fmul_rn, __fadd_rn, __fdiv_rn) and no contraction into FMA.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
@@ -366,12 +371,12 @@ __device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
 // kQuantThreads threads per tile; the register path holds a whole tile of up
 // to 16384 elements (2048 16-byte vectors of bf16, 4096 of fp32).
 template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+__device__ __forceinline__ void quant_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
                                                                    const void* __restrict__ src,
                                                                    uint8_t* __restrict__ q,
                                                                    float* __restrict__ scales) {
   __shared__ uint32_t red[kQuantThreads / kWave];
-  const unsigned b = piece_index<kTileXcdGroup>(blockIdx.x, gridDim.x);
+  const unsigned b = piece_index<kTileXcdGroup>(jb, n_jobs);
   const QJob j = jobs[b];
   if (static_cast<int64_t>(b) >= n_main) {
     zero_bytes<kQuantThreads>(q, j.base, j.stride, threadIdx.x);
@@ -381,14 +386,25 @@ __global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* _
       src, q, scales, j.base, j.stride, j.rows, j.cols, j.scale, threadIdx.x, red);
 }
 
+template <bool BF16, int FMT, bool HW>
+__global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                                   const void* __restrict__ src,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ scales, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    quant_tile_kernel_job<BF16, FMT, HW>(jb, n_jobs, jobs, n_main, src, q, scales);
+    __syncthreads();   // the next job reuses this workgroup's LDS
+  }
+}
+
 // One wave per flat block, kFlatPerGroup blocks per workgroup; zero-range jobs
 // from n_main on, as in the tile kernel.
 template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kFlatThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+__device__ __forceinline__ void quant_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
                                                               const void* __restrict__ src,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ scales) {
-  const unsigned b = piece_index<kFlatXcdGroup>(blockIdx.x, gridDim.x);
+  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
   const QJob j = jobs[b];
   if (static_cast<int64_t>(b) >= n_main) {
     zero_bytes<kFlatThreads>(q, j.base, j.stride, threadIdx.x);
@@ -401,11 +417,28 @@ __global__ __launch_bounds__(kFlatThreads) void quant_flat_kernel(const QJob* __
                                        1, len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr);
 }
 
+template <bool BF16, int FMT, bool HW>
+__global__ __launch_bounds__(kFlatThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                              const void* __restrict__ src,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    quant_flat_kernel_job<BF16, FMT, HW>(jb, n_jobs, jobs, n_main, src, q, scales);
+  }
+}
+
 // Code bytes of positions outside every block (a plan with no block at all).
-__global__ __launch_bounds__(kThreads) void zero_codes_kernel(const QJob* __restrict__ jobs,
+__device__ __forceinline__ void zero_codes_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs,
                                                               uint8_t* __restrict__ q) {
-  const QJob j = jobs[blockIdx.x];
+  const QJob j = jobs[jb];
   zero_bytes(q, j.base, j.stride, threadIdx.x);
+}
+
+__global__ __launch_bounds__(kThreads) void zero_codes_kernel(const QJob* __restrict__ jobs,
+                                                              uint8_t* __restrict__ q, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    zero_codes_kernel_job(jb, n_jobs, jobs, q);
+  }
 }
 
 // ------------------------------------------------------------------ dequant
@@ -437,11 +470,11 @@ __device__ void dequant_block(const uint8_t* __restrict__ q, float* __restrict__
 // Workgroups from n_main on clear the values outside every block (zero-range
 // jobs), as in the quant kernels.
 template <int FMT, bool HW>
-__global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+__device__ __forceinline__ void dequant_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
                                                                 const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ scales,
                                                                 float* __restrict__ out) {
-  const unsigned b = piece_index<kTileXcdGroup>(blockIdx.x, gridDim.x);
+  const unsigned b = piece_index<kTileXcdGroup>(jb, n_jobs);
   const QJob j = jobs[b];
   if (static_cast<int64_t>(b) >= n_main) {
     zero_f32(out, j.base, j.stride, threadIdx.x);
@@ -452,11 +485,21 @@ __global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __re
 }
 
 template <int FMT, bool HW>
-__global__ __launch_bounds__(kFlatThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+__global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    dequant_tile_kernel_job<FMT, HW>(jb, n_jobs, jobs, n_main, q, scales, out);
+  }
+}
+
+template <int FMT, bool HW>
+__device__ __forceinline__ void dequant_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
                                                                 const uint8_t* __restrict__ q,
                                                                 const float* __restrict__ scales,
                                                                 float* __restrict__ out) {
-  const unsigned b = piece_index<kFlatXcdGroup>(blockIdx.x, gridDim.x);
+  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
   const QJob j = jobs[b];
   if (static_cast<int64_t>(b) >= n_main) {
     zero_f32<kFlatThreads>(out, j.base, j.stride, threadIdx.x);
@@ -469,11 +512,28 @@ __global__ __launch_bounds__(kFlatThreads) void dequant_flat_kernel(const QJob* 
                                 len, 1, len, threadIdx.x & (kWave - 1));
 }
 
+template <int FMT, bool HW>
+__global__ __launch_bounds__(kFlatThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    dequant_flat_kernel_job<FMT, HW>(jb, n_jobs, jobs, n_main, q, scales, out);
+  }
+}
+
 // Dequantised values of positions outside every block (a plan with no block at all).
-__global__ __launch_bounds__(kThreads) void zero_values_kernel(const QJob* __restrict__ jobs,
+__device__ __forceinline__ void zero_values_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs,
                                                                float* __restrict__ out) {
-  const QJob j = jobs[blockIdx.x];
+  const QJob j = jobs[jb];
   zero_f32(out, j.base, j.stride, threadIdx.x);
+}
+
+__global__ __launch_bounds__(kThreads) void zero_values_kernel(const QJob* __restrict__ jobs,
+                                                               float* __restrict__ out, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    zero_values_kernel_job(jb, n_jobs, jobs, out);
+  }
 }
 
 // ------------------------------------------------------------------ gather side
@@ -556,15 +616,15 @@ __device__ __forceinline__ uint32_t div_u16(uint32_t n, uint32_t d, uint32_t m) 
 // holds fewer than 2^16 vectors (the lowering keeps it under 16384 elements),
 // so its row and tile-column indices come from div_u16.
 template <int FMT, bool HW, bool BF16OUT>
-__global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(const GatherChunk* __restrict__ chunks,
+__device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const GatherChunk* __restrict__ chunks,
                                                                     const uint8_t* __restrict__ q,
                                                                     const float* __restrict__ scales,
                                                                     void* const* __restrict__ dst, int split) {
   constexpr int VEC = BF16OUT ? 8 : 4;
   constexpr int U = kGatherVec;
-  const unsigned b = piece_index<kGatherXcdGroup>(blockIdx.x, gridDim.x);
-  const int ci = static_cast<int>(b / static_cast<unsigned>(split));
-  const int piece = static_cast<int>(b) - ci * split;
+  const unsigned cu = b / static_cast<unsigned>(split);
+  const int ci = static_cast<int>(cu);
+  const int piece = static_cast<int>(b - cu * static_cast<unsigned>(split));
   const GatherChunk c = chunks[ci];
   void* out = dst[c.tensor];
   const uint32_t vpr = static_cast<uint32_t>(c.cols / VEC);
@@ -624,27 +684,56 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(const Gathe
 }
 
 template <int FMT, bool HW, bool BF16OUT>
-__global__ __launch_bounds__(kThreads) void gather_tile_kernel(const QJob* __restrict__ jobs,
+__global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(const GatherChunk* __restrict__ chunks,
+                                                                    const uint8_t* __restrict__ q,
+                                                                    const float* __restrict__ scales,
+                                                                    void* const* __restrict__ dst, int split, unsigned n_pieces) {
+  for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
+    gather_rows_kernel_piece<FMT, HW, BF16OUT>(piece_index<kGatherXcdGroup>(p, n_pieces), chunks, q, scales, dst, split);
+}
+
+template <int FMT, bool HW, bool BF16OUT>
+__device__ __forceinline__ void gather_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs,
                                                                const uint8_t* __restrict__ q,
                                                                const float* __restrict__ scales,
                                                                void* const* __restrict__ dst) {
-  const QJob j = jobs[blockIdx.x];
+  const QJob j = jobs[jb];
   gather_block<FMT, HW, BF16OUT, kThreads>(q, dst[j.tensor], scales[j.scale], j.base, j.toff, j.stride,
                                            j.tstride, j.rows, j.cols, threadIdx.x);
 }
 
 template <int FMT, bool HW, bool BF16OUT>
-__global__ __launch_bounds__(kFlatThreads) void gather_flat_kernel(const QJob* __restrict__ jobs,
+__global__ __launch_bounds__(kThreads) void gather_tile_kernel(const QJob* __restrict__ jobs,
+                                                               const uint8_t* __restrict__ q,
+                                                               const float* __restrict__ scales,
+                                                               void* const* __restrict__ dst, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    gather_tile_kernel_job<FMT, HW, BF16OUT>(jb, n_jobs, jobs, q, scales, dst);
+  }
+}
+
+template <int FMT, bool HW, bool BF16OUT>
+__device__ __forceinline__ void gather_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs,
                                                                const uint8_t* __restrict__ q,
                                                                const float* __restrict__ scales,
                                                                void* const* __restrict__ dst) {
-  const QJob j = jobs[blockIdx.x];
+  const QJob j = jobs[jb];
   const int wave = threadIdx.x / kWave;
   if (wave >= j.rows) return;
   const int len = wave == j.rows - 1 ? j.last : j.cols;
   const int64_t step = static_cast<int64_t>(wave) * j.cols;
   gather_block<FMT, HW, BF16OUT, kWave>(q, dst[j.tensor], scales[j.scale + wave], j.base + step,
                                         j.toff + step, len, len, 1, len, threadIdx.x & (kWave - 1));
+}
+
+template <int FMT, bool HW, bool BF16OUT>
+__global__ __launch_bounds__(kFlatThreads) void gather_flat_kernel(const QJob* __restrict__ jobs,
+                                                               const uint8_t* __restrict__ q,
+                                                               const float* __restrict__ scales,
+                                                               void* const* __restrict__ dst, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    gather_flat_kernel_job<FMT, HW, BF16OUT>(jb, n_jobs, jobs, q, scales, dst);
+  }
 }
 
 // ------------------------------------------------------------------ 8-bit Adam step
@@ -772,20 +861,29 @@ __device__ void adam_block(float* __restrict__ param, const float* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restrict__ jobs, float* param,
+__device__ __forceinline__ void adam_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, float* param,
                                                              const float* grad, uint8_t* qm, float* sm,
                                                              uint8_t* qv, float* sv, AdamK k) {
   __shared__ uint32_t red[2 * kThreads / kWave];
-  const unsigned b = piece_index<kTileXcdGroup>(blockIdx.x, gridDim.x);
+  const unsigned b = piece_index<kTileXcdGroup>(jb, n_jobs);
   const QJob j = jobs[b];
   adam_block<kThreads, 4>(param, grad, qm, sm, qv, sv, j.base, j.stride, j.rows, j.cols, j.scale,
                           threadIdx.x, red, k);
 }
 
-__global__ __launch_bounds__(kFlatThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
+__global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restrict__ jobs, float* param,
+                                                             const float* grad, uint8_t* qm, float* sm,
+                                                             uint8_t* qv, float* sv, AdamK k, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    adam_tile_kernel_job(jb, n_jobs, jobs, param, grad, qm, sm, qv, sv, k);
+    __syncthreads();   // the next job reuses this workgroup's LDS
+  }
+}
+
+__device__ __forceinline__ void adam_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, float* param,
                                                              const float* grad, uint8_t* qm, float* sm,
                                                              uint8_t* qv, float* sv, AdamK k) {
-  const unsigned b = piece_index<kFlatXcdGroup>(blockIdx.x, gridDim.x);
+  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
   const QJob j = jobs[b];
   const int wave = threadIdx.x / kWave;
   if (wave >= j.rows) return;
@@ -794,16 +892,24 @@ __global__ __launch_bounds__(kFlatThreads) void adam_flat_kernel(const QJob* __r
                        len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr, k);
 }
 
+__global__ __launch_bounds__(kFlatThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
+                                                             const float* grad, uint8_t* qm, float* sm,
+                                                             uint8_t* qv, float* sv, AdamK k, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    adam_flat_kernel_job(jb, n_jobs, jobs, param, grad, qm, sm, qv, sv, k);
+  }
+}
+
 // ------------------------------------------------------------------ unpack
 
 // Workgroup b copies piece b % split (kUnpackPiece vectors) of chunk b / split.
-__global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(const CopyChunk* __restrict__ chunks,
+__device__ __forceinline__ void unpack_kernel_piece(unsigned b, const CopyChunk* __restrict__ chunks,
                                                                const uint8_t* __restrict__ gathered,
                                                                void* const* __restrict__ dst, int eb,
                                                                int split) {
-  const unsigned b = piece_index<kUnpackXcdGroup>(blockIdx.x, gridDim.x);
-  const int ci = static_cast<int>(b / static_cast<unsigned>(split));
-  const int piece = static_cast<int>(b) - ci * split;
+  const unsigned cu = b / static_cast<unsigned>(split);
+  const int ci = static_cast<int>(cu);
+  const int piece = static_cast<int>(b - cu * static_cast<unsigned>(split));
   const CopyChunk c = chunks[ci];
   const uint8_t* s = gathered + c.src * eb;
   uint8_t* d = static_cast<uint8_t*>(dst[c.tensor]) + c.off * eb;
@@ -821,6 +927,14 @@ __global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(const CopyChunk*
     if (v0 + u * kUnpackThreads < nvec) stg(d4 + v0 + u * kUnpackThreads, r[u]);
   const int tail = nbytes & 15;
   if (piece == 0 && static_cast<int>(threadIdx.x) < tail) d[(nvec << 4) + threadIdx.x] = s[(nvec << 4) + threadIdx.x];
+}
+
+__global__ __launch_bounds__(kUnpackThreads) void unpack_kernel(const CopyChunk* __restrict__ chunks,
+                                                               const uint8_t* __restrict__ gathered,
+                                                               void* const* __restrict__ dst, int eb,
+                                                               int split, unsigned n_pieces) {
+  for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
+    unpack_kernel_piece(piece_index<kUnpackXcdGroup>(p, n_pieces), chunks, gathered, dst, eb, split);
 }
 
 // ------------------------------------------------------------------ pack
@@ -849,12 +963,12 @@ __device__ __forceinline__ float load1(const void* p, int64_t e) {
 // chunk b / kPackSplit. `prev` may alias `out`: every element is read before
 // it is written, by the same thread.
 template <bool BF16, bool ACC>
-__global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
+__device__ __forceinline__ void pack_kernel_piece(unsigned b, const PackChunk* __restrict__ chunks,
                                                              const void* const* __restrict__ src,
                                                              const float* prev, float* out, float sigma) {
-  const unsigned b = piece_index<kPackXcdGroup>(blockIdx.x, gridDim.x);
-  const int ci = static_cast<int>(b / static_cast<unsigned>(kPackSplit));
-  const int piece = static_cast<int>(b) - ci * static_cast<int>(kPackSplit);
+  const unsigned cu = b / static_cast<unsigned>(kPackSplit);
+  const int ci = static_cast<int>(cu);
+  const int piece = static_cast<int>(b - cu * static_cast<unsigned>(kPackSplit));
   const PackChunk c = chunks[ci];
   f32x4* o4 = reinterpret_cast<f32x4*>(out + c.out);
   const int nv = c.n_total >> 2;
@@ -912,6 +1026,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __r
   }
 }
 
+template <bool BF16, bool ACC>
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
+                                                             const void* const* __restrict__ src,
+                                                             const float* prev, float* out, float sigma, unsigned n_pieces) {
+  for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
+    pack_kernel_piece<BF16, ACC>(piece_index<kPackXcdGroup>(p, n_pieces), chunks, src, prev, out, sigma);
+}
+
 // ------------------------------------------------------------------ tile-major layout
 
 // Tile-major -> row-major (unpack of a TILEMAJOR tensor), one TmJob per
@@ -920,11 +1042,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __r
 // written as h contiguous row segments of the tensor. Both global sides move
 // long contiguous ranges; the reorder happens in LDS.
 template <int EB>
-__global__ __launch_bounds__(kThreads) void unpack_tm_kernel(const TmJob* __restrict__ jobs,
+__device__ __forceinline__ void unpack_tm_kernel_job(unsigned jb, unsigned n_jobs, const TmJob* __restrict__ jobs,
                                                              const uint8_t* __restrict__ gathered,
                                                              void* const* __restrict__ dst) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kTmStage * 4];
-  const TmJob j = jobs[blockIdx.x];
+  const TmJob j = jobs[jb];
   const int bc = j.bc, h = j.h, k = j.k, tid = threadIdx.x;
   const int run = h * bc, width = k * bc;
   const uint8_t* src = gathered + j.base * EB;
@@ -961,17 +1083,27 @@ __global__ __launch_bounds__(kThreads) void unpack_tm_kernel(const TmJob* __rest
   }
 }
 
+template <int EB>
+__global__ __launch_bounds__(kThreads) void unpack_tm_kernel(const TmJob* __restrict__ jobs,
+                                                             const uint8_t* __restrict__ gathered,
+                                                             void* const* __restrict__ dst, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    unpack_tm_kernel_job<EB>(jb, n_jobs, jobs, gathered, dst);
+    __syncthreads();   // the next job reuses this workgroup's LDS
+  }
+}
+
 // Row-major -> tile-major with the pack arithmetic (pack of a TILEMAJOR
 // tensor): h rows of k*bc gradients are staged in LDS as fp32, then each
 // tile's run of h*bc elements is written contiguously as
 // [prev +] fl32(g * sigma). `prev` may alias `out` (each element is read and
 // written by the same thread).
 template <bool BF16, bool ACC>
-__global__ __launch_bounds__(kThreads) void pack_tm_kernel(const TmJob* __restrict__ jobs,
+__device__ __forceinline__ void pack_tm_kernel_job(unsigned jb, unsigned n_jobs, const TmJob* __restrict__ jobs,
                                                            const void* const* __restrict__ src,
                                                            const float* prev, float* out, float sigma) {
   __shared__ __attribute__((aligned(16))) float stage[kTmStage];
-  const TmJob j = jobs[blockIdx.x];
+  const TmJob j = jobs[jb];
   const int bc = j.bc, h = j.h, k = j.k, tid = threadIdx.x;
   const int run = h * bc, width = k * bc;
   const void* g = src[j.tensor];
@@ -1010,6 +1142,16 @@ __global__ __launch_bounds__(kThreads) void pack_tm_kernel(const TmJob* __restri
   }
 }
 
+template <bool BF16, bool ACC>
+__global__ __launch_bounds__(kThreads) void pack_tm_kernel(const TmJob* __restrict__ jobs,
+                                                           const void* const* __restrict__ src,
+                                                           const float* prev, float* out, float sigma, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    pack_tm_kernel_job<BF16, ACC>(jb, n_jobs, jobs, src, prev, out, sigma);
+    __syncthreads();   // the next job reuses this workgroup's LDS
+  }
+}
+
 // Direct tile-major reorder, no LDS: workgroup b takes piece b % split of
 // strip b / split, kTmThreads vectors (one per thread). Unpack walks the strip
 // in row-major order: consecutive lanes write one contiguous row segment and
@@ -1018,12 +1160,13 @@ __global__ __launch_bounds__(kThreads) void pack_tm_kernel(const TmJob* __restri
 // reads are bc-element row runs. Strips hold at most kTmStage elements, so
 // every index below stays under 2^16 and div_u16 applies.
 template <int EB>
-__global__ __launch_bounds__(kTmThreads) void unpack_tm_direct_kernel(const TmJob* __restrict__ jobs,
+__device__ __forceinline__ void unpack_tm_direct_kernel_piece(unsigned b, const TmJob* __restrict__ jobs,
                                                                       const uint8_t* __restrict__ gathered,
                                                                       void* const* __restrict__ dst, int split) {
   constexpr int VE = 16 / EB;   // elements per 16-byte vector
-  const int ji = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
-  const int piece = static_cast<int>(blockIdx.x) - ji * split;
+  const unsigned ju = b / static_cast<unsigned>(split);
+  const int ji = static_cast<int>(ju);
+  const int piece = static_cast<int>(b - ju * static_cast<unsigned>(split));
   const TmJob j = jobs[ji];
   const uint32_t bc = static_cast<uint32_t>(j.bc), width = static_cast<uint32_t>(j.k) * bc;
   const uint32_t mbc = magic_u16(bc);
@@ -1054,13 +1197,22 @@ __global__ __launch_bounds__(kTmThreads) void unpack_tm_direct_kernel(const TmJo
   }
 }
 
+template <int EB>
+__global__ __launch_bounds__(kTmThreads) void unpack_tm_direct_kernel(const TmJob* __restrict__ jobs,
+                                                                      const uint8_t* __restrict__ gathered,
+                                                                      void* const* __restrict__ dst, int split, unsigned n_pieces) {
+  for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
+    unpack_tm_direct_kernel_piece<EB>(p, jobs, gathered, dst, split);
+}
+
 template <bool BF16, bool ACC>
-__global__ __launch_bounds__(kTmThreads) void pack_tm_direct_kernel(const TmJob* __restrict__ jobs,
+__device__ __forceinline__ void pack_tm_direct_kernel_piece(unsigned b, const TmJob* __restrict__ jobs,
                                                                     const void* const* __restrict__ src,
                                                                     const float* prev, float* out, float sigma,
                                                                     int split) {
-  const int ji = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
-  const int piece = static_cast<int>(blockIdx.x) - ji * split;
+  const unsigned ju = b / static_cast<unsigned>(split);
+  const int ji = static_cast<int>(ju);
+  const int piece = static_cast<int>(b - ju * static_cast<unsigned>(split));
   const TmJob j = jobs[ji];
   const uint32_t bc = static_cast<uint32_t>(j.bc), run = static_cast<uint32_t>(j.h) * bc;
   const uint32_t mbc = magic_u16(bc);
@@ -1097,19 +1249,29 @@ __global__ __launch_bounds__(kTmThreads) void pack_tm_direct_kernel(const TmJob*
   }
 }
 
+template <bool BF16, bool ACC>
+__global__ __launch_bounds__(kTmThreads) void pack_tm_direct_kernel(const TmJob* __restrict__ jobs,
+                                                                    const void* const* __restrict__ src,
+                                                                    const float* prev, float* out, float sigma,
+                                                                    int split, unsigned n_pieces) {
+  for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
+    pack_tm_direct_kernel_piece<BF16, ACC>(p, jobs, src, prev, out, sigma, split);
+}
+
 // Gather side of a tile-major tensor, over the same strips: each lane turns
 // VEC codes of one tile row into one 16-byte store of the row-major tensor
 // (8 codes -> 8 bf16, 4 -> 4 fp32), kGatherVec vectors per thread; tile t of
 // the strip uses scale scale0 + t.
 template <int FMT, bool HW, bool BF16OUT>
-__global__ __launch_bounds__(kGatherThreads) void gather_tm_kernel(const TmJob* __restrict__ jobs,
+__device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* __restrict__ jobs,
                                                                   const uint8_t* __restrict__ q,
                                                                   const float* __restrict__ scales,
                                                                   void* const* __restrict__ dst, int split) {
   constexpr int VEC = BF16OUT ? 8 : 4;
   constexpr int U = kGatherVec;
-  const int ji = static_cast<int>(blockIdx.x / static_cast<unsigned>(split));
-  const int piece = static_cast<int>(blockIdx.x) - ji * split;
+  const unsigned ju = b / static_cast<unsigned>(split);
+  const int ji = static_cast<int>(ju);
+  const int piece = static_cast<int>(b - ju * static_cast<unsigned>(split));
   const TmJob j = jobs[ji];
   const uint32_t bc = static_cast<uint32_t>(j.bc), width = static_cast<uint32_t>(j.k) * bc;
   const uint32_t mbc = magic_u16(bc);
@@ -1187,7 +1349,24 @@ __global__ __launch_bounds__(kGatherThreads) void gather_tm_kernel(const TmJob* 
   }
 }
 
+template <int FMT, bool HW, bool BF16OUT>
+__global__ __launch_bounds__(kGatherThreads) void gather_tm_kernel(const TmJob* __restrict__ jobs,
+                                                                  const uint8_t* __restrict__ q,
+                                                                  const float* __restrict__ scales,
+                                                                  void* const* __restrict__ dst, int split, unsigned n_pieces) {
+  for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
+    gather_tm_kernel_piece<FMT, HW, BF16OUT>(p, jobs, q, scales, dst, split);
+}
+
 // ------------------------------------------------------------------ host side
+
+// Grid of a launch: one workgroup per work item up to the plan's max_grid
+// (kMaxGrid unless RS_MAX_GRID lowers it), beyond which every workgroup loops
+// over items p, p + grid, ... (max_grid is a multiple of 8, so item p still
+// runs on XCD p % 8).
+dim3 grid_of(const rs_plan* p, int64_t n_items) {
+  return dim3(static_cast<unsigned>(std::min<int64_t>(n_items, p->max_grid)));
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -1259,21 +1438,25 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
   const uint8_t* gb = static_cast<const uint8_t*>(gathered);
   if (p->n_unpack) {
     const int64_t split = unpack_split(eb);
-    hipLaunchKernelGGL(unpack_kernel, dim3(static_cast<unsigned>(p->n_unpack * split)), dim3(kUnpackThreads), 0, s,
-                       p->unpack, gb, p->dst.dev, eb, static_cast<int>(split));
+    const int64_t n = p->n_unpack * split;
+    hipLaunchKernelGGL(unpack_kernel, grid_of(p, n), dim3(kUnpackThreads), 0, s, p->unpack, gb, p->dst.dev, eb,
+                       static_cast<int>(split), static_cast<unsigned>(n));
   }
   if (p->n_tm && !p->tm_lds) {
     const int64_t split = tm_split(16 / eb);
-    const dim3 g(static_cast<unsigned>(p->n_tm * split)), b(kTmThreads);
+    const int64_t n = p->n_tm * split;
+    const dim3 g = grid_of(p, n), b(kTmThreads);
     const int sp = static_cast<int>(split);
-    if (eb == 4) hipLaunchKernelGGL(unpack_tm_direct_kernel<4>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp);
-    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_direct_kernel<2>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp);
-    else hipLaunchKernelGGL(unpack_tm_direct_kernel<1>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp);
+    const unsigned np = static_cast<unsigned>(n);
+    if (eb == 4) hipLaunchKernelGGL(unpack_tm_direct_kernel<4>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp, np);
+    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_direct_kernel<2>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp, np);
+    else hipLaunchKernelGGL(unpack_tm_direct_kernel<1>, g, b, 0, s, p->tmjobs, gb, p->dst.dev, sp, np);
   } else if (p->n_tm) {
-    const dim3 g(static_cast<unsigned>(p->n_tm));
-    if (eb == 4) hipLaunchKernelGGL(unpack_tm_kernel<4>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
-    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_kernel<2>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
-    else hipLaunchKernelGGL(unpack_tm_kernel<1>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev);
+    const dim3 g = grid_of(p, p->n_tm);
+    const unsigned nj = static_cast<unsigned>(p->n_tm);
+    if (eb == 4) hipLaunchKernelGGL(unpack_tm_kernel<4>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev, nj);
+    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_kernel<2>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev, nj);
+    else hipLaunchKernelGGL(unpack_tm_kernel<1>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev, nj);
   }
   return launched(who);
 }
@@ -1304,36 +1487,41 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_table(p, &p->src, src, s, who);
   if (st != RS_OK) return st;
-  const dim3 grid(static_cast<unsigned>(p->n_pack * kPackSplit)), sblock(kPackThreads), block(kThreads);
+  const int64_t n_pieces = p->n_pack * kPackSplit;
+  const unsigned np = static_cast<unsigned>(n_pieces);
+  const dim3 grid = grid_of(p, n_pieces), sblock(kPackThreads), block(kThreads);
   void** tab = p->src.dev;
   if (p->n_pack) {
     if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_kernel<false, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
-      else hipLaunchKernelGGL((pack_kernel<false, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
+      if (prev) hipLaunchKernelGGL((pack_kernel<false, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
+      else hipLaunchKernelGGL((pack_kernel<false, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
     } else {
-      if (prev) hipLaunchKernelGGL((pack_kernel<true, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
-      else hipLaunchKernelGGL((pack_kernel<true, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma);
+      if (prev) hipLaunchKernelGGL((pack_kernel<true, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
+      else hipLaunchKernelGGL((pack_kernel<true, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
     }
   }
   if (p->n_tm && !p->tm_lds) {
     const int64_t split = tm_split(4);
-    const dim3 g(static_cast<unsigned>(p->n_tm * split)), b(kTmThreads);
+    const int64_t n = p->n_tm * split;
+    const dim3 g = grid_of(p, n), b(kTmThreads);
     const int sp = static_cast<int>(split);
+    const unsigned ntp = static_cast<unsigned>(n);
     if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<false, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
-      else hipLaunchKernelGGL((pack_tm_direct_kernel<false, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
+      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<false, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
+      else hipLaunchKernelGGL((pack_tm_direct_kernel<false, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
     } else {
-      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<true, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
-      else hipLaunchKernelGGL((pack_tm_direct_kernel<true, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp);
+      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<true, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
+      else hipLaunchKernelGGL((pack_tm_direct_kernel<true, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
     }
   } else if (p->n_tm) {
-    const dim3 g(static_cast<unsigned>(p->n_tm));
+    const dim3 g = grid_of(p, p->n_tm);
+    const unsigned nj = static_cast<unsigned>(p->n_tm);
     if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_tm_kernel<false, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
-      else hipLaunchKernelGGL((pack_tm_kernel<false, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
+      if (prev) hipLaunchKernelGGL((pack_tm_kernel<false, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
+      else hipLaunchKernelGGL((pack_tm_kernel<false, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
     } else {
-      if (prev) hipLaunchKernelGGL((pack_tm_kernel<true, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
-      else hipLaunchKernelGGL((pack_tm_kernel<true, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma);
+      if (prev) hipLaunchKernelGGL((pack_tm_kernel<true, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
+      else hipLaunchKernelGGL((pack_tm_kernel<true, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
     }
   }
   return launched(who);
@@ -1351,14 +1539,14 @@ void launch_quant_kinds(const rs_plan* p, const void* src, uint8_t* q, float* sc
   const int64_t nz = p->n_qzero;
   if (p->n_qtile) {
     const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
-    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(n)), dim3(kQuantThreads), 0, s, tiles,
-                       p->n_qtile, src, q, scales);
+    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), grid_of(p, n), dim3(kQuantThreads), 0, s, tiles,
+                       p->n_qtile, src, q, scales, static_cast<unsigned>(n));
   }
   if (p->n_qflat)
-    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), dim3(kFlatThreads),
-                       0, s, flats, p->n_qflat, src, q, scales);
+    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), grid_of(p, p->n_qflat + nz), dim3(kFlatThreads), 0, s, flats,
+                       p->n_qflat, src, q, scales, static_cast<unsigned>(p->n_qflat + nz));
   if (!p->n_qtile && !p->n_qflat && nz)
-    hipLaunchKernelGGL(zero_codes_kernel, dim3(static_cast<unsigned>(nz)), block, 0, s, flats, q);
+    hipLaunchKernelGGL(zero_codes_kernel, grid_of(p, nz), block, 0, s, flats, q, static_cast<unsigned>(nz));
 }
 
 template <bool BF16>
@@ -1382,14 +1570,14 @@ void launch_dequant(const rs_plan* p, const uint8_t* q, const float* scales, flo
   const int64_t nz = p->n_qzero;
   if (p->n_qtile) {
     const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
-    hipLaunchKernelGGL((dequant_tile_kernel<FMT, HW>), dim3(static_cast<unsigned>(n)), block, 0, s, tiles,
-                       p->n_qtile, q, scales, out);
+    hipLaunchKernelGGL((dequant_tile_kernel<FMT, HW>), grid_of(p, n), block, 0, s, tiles, p->n_qtile, q, scales, out,
+                       static_cast<unsigned>(n));
   }
   if (p->n_qflat)
-    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), dim3(static_cast<unsigned>(p->n_qflat + nz)), dim3(kFlatThreads), 0, s,
-                       flats, p->n_qflat, q, scales, out);
+    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), grid_of(p, p->n_qflat + nz), dim3(kFlatThreads), 0, s, flats,
+                       p->n_qflat, q, scales, out, static_cast<unsigned>(p->n_qflat + nz));
   if (!p->n_qtile && !p->n_qflat && nz)
-    hipLaunchKernelGGL(zero_values_kernel, dim3(static_cast<unsigned>(nz)), block, 0, s, flats, out);
+    hipLaunchKernelGGL(zero_values_kernel, grid_of(p, nz), block, 0, s, flats, out, static_cast<unsigned>(nz));
 }
 
 int fmt_of(int32_t q_dt) {
@@ -1456,19 +1644,21 @@ void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipS
   const QJob* flats = tiles + p->n_gtile;
   if (p->n_gchunks) {
     const int64_t split = gather_split(BF16OUT ? 8 : 4);
-    hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gchunks * split)),
-                       dim3(kGatherThreads), 0, s, p->gchunks, q, scales, p->gdst.dev, static_cast<int>(split));
+    const int64_t n = p->n_gchunks * split;
+    hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT>), grid_of(p, n), dim3(kGatherThreads), 0, s, p->gchunks, q,
+                       scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));
   }
   if (p->n_gtile)
-    hipLaunchKernelGGL((gather_tile_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gtile)),
-                       block, 0, s, tiles, q, scales, p->gdst.dev);
+    hipLaunchKernelGGL((gather_tile_kernel<FMT, HW, BF16OUT>), grid_of(p, p->n_gtile), block, 0, s, tiles, q, scales,
+                       p->gdst.dev, static_cast<unsigned>(p->n_gtile));
   if (p->n_gflat)
-    hipLaunchKernelGGL((gather_flat_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_gflat)),
-                       dim3(kFlatThreads), 0, s, flats, q, scales, p->gdst.dev);
+    hipLaunchKernelGGL((gather_flat_kernel<FMT, HW, BF16OUT>), grid_of(p, p->n_gflat), dim3(kFlatThreads), 0, s, flats, q,
+                       scales, p->gdst.dev, static_cast<unsigned>(p->n_gflat));
   if (p->n_tm) {
     const int64_t split = tm_gather_split(BF16OUT ? 8 : 4);
-    hipLaunchKernelGGL((gather_tm_kernel<FMT, HW, BF16OUT>), dim3(static_cast<unsigned>(p->n_tm * split)),
-                       dim3(kGatherThreads), 0, s, p->tmjobs, q, scales, p->gdst.dev, static_cast<int>(split));
+    const int64_t n = p->n_tm * split;
+    hipLaunchKernelGGL((gather_tm_kernel<FMT, HW, BF16OUT>), grid_of(p, n), dim3(kGatherThreads), 0, s, p->tmjobs, q,
+                       scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));
   }
 }
 
@@ -1543,10 +1733,10 @@ extern "C" int rs_adam8_step(rs_plan* p, float* param, const float* grad, void* 
   uint8_t* qmb = static_cast<uint8_t*>(q_m);
   uint8_t* qvb = static_cast<uint8_t*>(q_v);
   if (p->n_qtile)
-    hipLaunchKernelGGL(adam_tile_kernel, dim3(static_cast<unsigned>(p->n_qtile)), dim3(kThreads), 0, s,
-                       p->qjobs, param, grad, qmb, s_m, qvb, s_v, k);
+    hipLaunchKernelGGL(adam_tile_kernel, grid_of(p, p->n_qtile), dim3(kThreads), 0, s, p->qjobs, param, grad, qmb, s_m,
+                       qvb, s_v, k, static_cast<unsigned>(p->n_qtile));
   if (p->n_qflat)
-    hipLaunchKernelGGL(adam_flat_kernel, dim3(static_cast<unsigned>(p->n_qflat)), dim3(kFlatThreads), 0, s,
-                       p->qjobs + p->n_qtile, param, grad, qmb, s_m, qvb, s_v, k);
+    hipLaunchKernelGGL(adam_flat_kernel, grid_of(p, p->n_qflat), dim3(kFlatThreads), 0, s, p->qjobs + p->n_qtile, param,
+                       grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(p->n_qflat));
   return launched(who);
 }

@@ -70,6 +70,8 @@ int validate(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S, const
   if (R_mat < *R_used || R_mat > V)
     return fail(RS_ERANGE, "rs_plan_load: R_mat must lie in [R_used, V] (R_used = " +
                                std::to_string(*R_used) + ")");
+  if (R_mat > kMaxElems / S)
+    return fail(RS_ERANGE, "rs_plan_load: R_mat * S exceeds 2^39 elements, more than one device holds");
   return RS_OK;
 }
 
@@ -395,19 +397,17 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
 
     Tables tb;
     lower(t, S, R_mat, &tb);
-    const int64_t longest = std::max({static_cast<int64_t>(tb.unpack.size()), static_cast<int64_t>(tb.tm.size()),
-                                      static_cast<int64_t>(tb.pack.size()), static_cast<int64_t>(tb.qjobs.size()),
-                                      static_cast<int64_t>(tb.gchunks.size()),
-                                      static_cast<int64_t>(tb.gjobs.size())});
-    const int64_t unpack_items = static_cast<int64_t>(tb.unpack.size()) * unpack_split(4) * kUnpackThreads;
-    const int64_t pack_items = static_cast<int64_t>(tb.pack.size()) * kPackSplit * kPackThreads;
-    const int64_t gather_items = static_cast<int64_t>(tb.gchunks.size()) * gather_split(4) * kGatherThreads;
-    const int64_t tm_items = static_cast<int64_t>(tb.tm.size()) * tm_split(4) * kTmThreads;
-    const int64_t threads = std::max({unpack_items, pack_items, gather_items, tm_items});
-    if (longest > kMaxWorkgroups || threads > kMaxWorkItems)
-      return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(longest) + " work items (" +
-                                 std::to_string(threads) + " threads) in one launch, more than a dispatch "
-                                 "holds");
+    // Every launch loops over its work items beyond kMaxGrid workgroups; item
+    // and piece indices are 32-bit. Under the 2^39-element limit this holds
+    // for any plan but one made of tiny tiles.
+    const int64_t items = std::max({static_cast<int64_t>(tb.unpack.size()) * unpack_split(4),
+                                    static_cast<int64_t>(tb.pack.size()) * kPackSplit,
+                                    static_cast<int64_t>(tb.gchunks.size()) * gather_split(4),
+                                    static_cast<int64_t>(tb.tm.size()) * tm_split(4),
+                                    static_cast<int64_t>(tb.qjobs.size()), static_cast<int64_t>(tb.gjobs.size())});
+    if (items > 0xFFFFFFFFll)
+      return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(items) +
+                                 " work items in one launch; indices are 32-bit");
 
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess) return fail(RS_EHIP, "rs_plan_load: no HIP device");
@@ -442,6 +442,13 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     // selects the LDS-staged ones (same results).
     const char* tmk = std::getenv("RS_TM_KERNEL");
     p->tm_lds = tmk && std::strcmp(tmk, "lds") == 0;
+    // RS_MAX_GRID=n caps every launch at n workgroups (rounded down to a
+    // multiple of 8, at least 8), so the workgroups loop over work items; the
+    // results do not change.
+    if (const char* mg = std::getenv("RS_MAX_GRID")) {
+      const long long v = std::strtoll(mg, nullptr, 10);
+      p->max_grid = std::max<int64_t>(8, std::min<int64_t>(kMaxGrid, v) / 8 * 8);
+    }
 
     const int64_t bytes = align_up(sizeof(TmJob) * std::max<int64_t>(p->n_tm, 1), 256) +
                           align_up(sizeof(CopyChunk) * std::max<int64_t>(p->n_unpack, 1), 256) +

@@ -87,11 +87,12 @@ constexpr unsigned kFlatXcdGroup = RS_FLAT_XCD_GROUP;
 #endif
 constexpr int kQuantThreads = RS_QUANT_THREADS;
 static_assert(kQuantThreads % 64 == 0 && 2048 % kQuantThreads == 0, "tile quant thread count");
-// A dispatch counts its grid in work-items with 32 bits.
-constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
-// Other launches use workgroups of at most max(256, kQuantThreads) threads:
-// one list may hold at most this many work items.
-constexpr int64_t kMaxWorkgroups = kMaxWorkItems / (kQuantThreads > 256 ? kQuantThreads : 256);
+// Split launches use at most kMaxGrid workgroups and loop over further pieces
+// (a multiple of 8: one round of the XCD dispatch).
+constexpr int64_t kMaxGrid = int64_t(1) << 24;
+// Largest materialised buffer, R_mat * S elements (4 TiB of fp32, far beyond
+// one device); it keeps every work-item index within 32 bits.
+constexpr int64_t kMaxElems = int64_t(1) << 39;
 // Flat quantisation blocks per workgroup, one 64-lane wave each.
 #ifndef RS_FLAT_PER_GROUP
 #define RS_FLAT_PER_GROUP 2
@@ -267,4 +268,5 @@ struct rs_plan {
   rs::PtrTable gdst;  // unpack-dequant destinations
   bool e4m3_hw = false;  // use gfx950's FP8 conversion instructions
   bool tm_lds = false;   // tile-major unpack / pack staged through LDS instead of the direct kernels
+  int64_t max_grid = rs::kMaxGrid;   // workgroups per launch; beyond it workgroups loop over items
 };

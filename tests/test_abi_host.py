@@ -150,10 +150,10 @@ def test_host_planner_matches_oracle_on_tile_major_groups(rs, seed):
     assert (S, starts, name) == (ref.S, [int(s) for s in ref.starts], ref.order_name)
 
 
-def test_plan_too_large_for_one_dispatch_is_rejected(rs):
-    """A launch counts its grid in 32-bit work-items: a plan whose pack needs more
-    than (2^32 - 1) / 256 workgroups is refused on the host, before any device call."""
+def test_plan_larger_than_any_device_is_rejected(rs):
+    """R_mat * S above 2^39 elements is refused on the host before any lowering
+    (launches loop over their work items, so only the 32-bit indices bound a plan)."""
     from structure_aware_grouped_amd import binding as b
-    big = [TensorSpec("big", 1 << 20, 1 << 17, "ELEM")]      # 2^37 elements, 2^25 pack items
-    assert _status(lambda: rs.rs_plan_load(big, 1, 1 << 37, [0])) == b.RS_ERANGE
-    assert "work items" in b.load().rs_last_error().decode()
+    big = [TensorSpec("big", 1 << 20, 1 << 19, "ELEM")]      # 2^39 elements
+    assert _status(lambda: rs.rs_plan_load(big, 2, 1 << 39, [0], R_mat=2)) == b.RS_ERANGE
+    assert "2^39" in b.load().rs_last_error().decode()

@@ -50,9 +50,13 @@ def test_chained_steps_on_a_ragged_group(gpu_lib, V):
     plan.close()
 
 
-def test_two_steps_on_the_mid_size_group(gpu_lib):
-    """More than 32 tiles, so the XCD-grouped tile order runs whole rounds and a tail."""
+@pytest.mark.parametrize("max_grid", [None, "16"])
+def test_two_steps_on_the_mid_size_group(gpu_lib, max_grid, monkeypatch):
+    """More than 32 tiles, so the XCD-grouped tile order runs whole rounds and a tail;
+    with RS_MAX_GRID=16 every workgroup also loops over many blocks."""
     import structure_aware_grouped_amd as rs
+    if max_grid:
+        monkeypatch.setenv("RS_MAX_GRID", max_grid)
     specs, V = MID, 7
     S, starts, _, _ = rs.rs_plan_build(specs, V)
     plan = rs.rs_plan_load(specs, V, S, starts, V, 0)

@@ -242,6 +242,18 @@ def test_mid_size_group(gpu_lib, pdtype):
     _full_check(rs, MID, 7, pdtype, 77)
 
 
+@pytest.mark.parametrize("tm_kernel", ["direct", "lds"])
+def test_launches_that_loop_over_work_items(gpu_lib, tm_kernel, monkeypatch):
+    """RS_MAX_GRID=24 caps every launch at 24 workgroups, so each workgroup loops
+    over many work items (and reuses its LDS between tiles): the results must not
+    change."""
+    import structure_aware_grouped_amd as rs
+    monkeypatch.setenv("RS_MAX_GRID", "24")
+    monkeypatch.setenv("RS_TM_KERNEL", tm_kernel)
+    _full_check(rs, MID, 7, torch.bfloat16, 78)
+    _full_check(rs, TILE_MAJOR, 3, torch.float32, 79)
+
+
 def test_trailing_padding_ranks(gpu_lib):
     """R_mat > R_used: ranks holding only padding come out zero."""
     import structure_aware_grouped_amd as rs
