@@ -9,7 +9,7 @@ import torch
 
 from oracle import adam as OA, plan as OP, transform as OT
 from tests.gpu_util import tensor_bits
-from tests.test_gpu_parity import MID, RAGGED
+from tests.test_gpu_parity import BIG_BLOCKS, MID, RAGGED
 from workloads import TensorSpec, workload
 import workloads as W
 
@@ -68,6 +68,29 @@ def test_two_steps_on_the_mid_size_group(gpu_lib, max_grid, monkeypatch):
     qm, sm = OT.block_quant(m, specs, starts, S, V, "i8")
     qv, sv = OT.block_quant(v, specs, starts, S, V, "u8")
     for h in HYPERS[:2]:
+        grad = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+        want = OA.adam8_step(param, grad, qm, sm, qv, sv, specs, starts, h)
+        got = _run(rs, plan, (param, grad, qm, sm, qv.astype(np.uint8), sv), h)
+        for g, wv, name in zip(got, want, ("param", "q_m", "s_m", "q_v", "s_v")):
+            assert np.array_equal(tensor_bits(g), np.asarray(wv).view(tensor_bits(g).dtype)), (name, h.step)
+        param, qm, sm, qv, sv = want
+    plan.close()
+
+
+def test_steps_on_blocks_beyond_the_register_paths(gpu_lib):
+    """Tiles of 32768 elements and 6000-element flat blocks take the two-pass path."""
+    import structure_aware_grouped_amd as rs
+    specs, V = BIG_BLOCKS, 3
+    S, starts, _, _ = rs.rs_plan_build(specs, V)
+    plan = rs.rs_plan_load(specs, V, S, starts, V, 0)
+    rng = np.random.default_rng(11)
+    total = V * S
+    param = rng.standard_normal(total).astype(np.float32)
+    m = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(total) * 1e-3) ** 2).astype(np.float32)
+    qm, sm = OT.block_quant(m, specs, starts, S, V, "i8")
+    qv, sv = OT.block_quant(v, specs, starts, S, V, "u8")
+    for h in HYPERS:
         grad = (rng.standard_normal(total) * 1e-3).astype(np.float32)
         want = OA.adam8_step(param, grad, qm, sm, qv, sv, specs, starts, h)
         got = _run(rs, plan, (param, grad, qm, sm, qv.astype(np.uint8), sv), h)

@@ -242,6 +242,26 @@ def test_mid_size_group(gpu_lib, pdtype):
     _full_check(rs, MID, 7, pdtype, 77)
 
 
+# Blocks larger than the register paths hold (a tile of more than 16384
+# elements, a flat block of more than 2048 fp32 / 4096 bf16 elements), so the
+# kernels take their two-pass element paths; plus a flat block size that is not
+# a multiple of 16 (per-block gather) and tile-major tiles of 32768 elements.
+BIG_BLOCKS = [
+    TensorSpec("tile_big", 300, 520, "TILE", 256, 128),
+    TensorSpec("flat_big", 1, 20000, "FLAT", 6000),
+    TensorSpec("tm_big", 512, 256, "TILEMAJOR", 256, 128),
+    TensorSpec("flat_odd", 1, 3001, "FLAT", 1000),
+    TensorSpec("norm", 300, 1, "ROWS", 1),
+]
+
+
+@pytest.mark.parametrize("V", [1, 3])
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_blocks_beyond_the_register_paths(gpu_lib, V, pdtype):
+    import structure_aware_grouped_amd as rs
+    _full_check(rs, BIG_BLOCKS, V, pdtype, 90 + V)
+
+
 @pytest.mark.parametrize("tm_kernel", ["direct", "lds"])
 def test_launches_that_loop_over_work_items(gpu_lib, tm_kernel, monkeypatch):
     """RS_MAX_GRID=24 caps every launch at 24 workgroups, so each workgroup loops
