@@ -113,6 +113,11 @@ def _full_check(rs, specs, V, pdtype, seed, fmts=("e4m3", "i8", "u8"), R_mat=Non
         wd = OT.block_dequant(wq, ws, specs, plan.starts, S, R, fmt)
         assert np.array_equal(tensor_bits(out), wd.view(np.uint32)), fmt
         assert guard_intact(owhole, total)
+        # unpack of a 1-byte buffer: the gathered codes, tensor by tensor
+        cdst = [garbage(sp.rows * sp.cols, torch.uint8, DEV, 0x99).view(sp.rows, sp.cols) for sp in specs]
+        rs.rs_unpack_gathered(plan, q, cdst)
+        for d, wv in zip(cdst, OT.unpack(wq, specs, plan.starts)):
+            assert np.array_equal(tensor_bits(d), wv), fmt
         # gather side: gathered codes + scales -> the quantised full tensors
         for out_dt, tag in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
             quantised = [sp.kind in ("TILE", "TILEMAJOR", "FLAT") for sp in specs]
