@@ -38,7 +38,9 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
 METRIC = "DBuffer pack/unpack+blockquant GB/s, % HBM peak (Llama-3-8B layer, V=64)"
 # committed counter summaries: (workload, mode, tile-major) -> profiles/traffic_<name>.md
 PROFILE_TRAFFIC = {(1, "step", False): "llama3_8b_v64", (1, "step", True): "llama3_8b_v64_tile_major",
-                   (1, "fp8_gather", False): "llama3_8b_v64_fp8_gather", (4, "adam8", False): "adam8_llama3_8b_v64"}
+                   (1, "fp8_gather", False): "llama3_8b_v64_fp8_gather", (4, "adam8", False): "adam8_llama3_8b_v64",
+                   (2, "step", False): "llama3_70b_v1024", (3, "step", False): "moe128_v256",
+                   (4, "step", False): "adam_states_llama3_8b_v64"}
 KERNEL_SOURCES = [os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", f)
                   for f in ("kernels.hip", "rs_internal.h", "plan.cpp")]
 
