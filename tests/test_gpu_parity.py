@@ -390,6 +390,33 @@ def test_pointer_table_refresh(gpu_lib):
     plan.close()
 
 
+def test_calls_on_a_side_stream(gpu_lib):
+    """Every call runs on torch's current stream: on a side stream (default
+    priority) the results, including a changed pointer table, arrive in order."""
+    import structure_aware_grouped_amd as rs
+    specs = RAGGED
+    plan = _plan(rs, specs, 3)
+    rng = _rng(21)
+    G, Gh, xs = _flat_input(rng, plan, torch.bfloat16)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        for k in range(2):   # the second round brings new tensors, so a new pointer table
+            outs = [garbage(sp.rows * sp.cols, torch.bfloat16, DEV).view(sp.rows, sp.cols) for sp in specs]
+            rs.rs_unpack_gathered(plan, G, outs)
+            q = garbage(plan.R_mat * plan.S, torch.uint8, DEV)
+            scales = garbage(max(plan.n_qblocks, 1), torch.float32, DEV)
+            rs.rs_block_quant(plan, G, q, "e4m3", scales)
+    side.synchronize()
+    want = OT.unpack(tensor_bits(G), specs, plan.starts)
+    for o, wv in zip(outs, want):
+        assert np.array_equal(tensor_bits(o), wv)
+    wq, ws = OT.block_quant(Gh, specs, plan.starts, plan.S, plan.R_mat, "e4m3")
+    assert np.array_equal(tensor_bits(q), wq)
+    assert np.array_equal(tensor_bits(scales)[: plan.n_qblocks], ws.view(np.uint32))
+    plan.close()
+
+
 def test_bad_arguments_launch_nothing(gpu_lib):
     import structure_aware_grouped_amd as rs
     from structure_aware_grouped_amd import binding as b
