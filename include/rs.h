@@ -86,7 +86,7 @@ typedef enum rs_dtype {
  *                  distributed asymmetrically)           g = br * bc
  *                  Needs rows % br == 0, cols % bc == 0, br*bc % 16 == 0 and
  *                  bc <= 8192. Unpack and pack reorder between this layout and
- *                  the row-major tensor (through LDS on the GPU).
+ *                  the row-major tensor (staged through LDS on the GPU).
  * The last block of a tensor may be partial. TILE, TILEMAJOR and FLAT
  * tensors are the ones rs_block_quant quantises (tiles / flat blocks); the
  * others are not. */
@@ -147,8 +147,9 @@ int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t ali
  * (RS_ERANGE; neither limit is reached by a group one device can hold).
  * Environment read here, once per plan: RS_E4M3_ENCODER=sw selects the
  * integer E4M3 encoder instead of gfx950's conversion instruction;
- * RS_TM_KERNEL=lds stages the tile-major reorder of unpack / pack through
- * LDS instead of the direct kernels. Both give identical results.
+ * RS_TM_KERNEL=direct runs the tile-major reorder of unpack / pack with
+ * direct per-lane kernels instead of staging it through LDS. Both give
+ * identical results.
  * On success *out owns host memory and one device allocation, released by
  * rs_plan_free. Errors: the above, RS_ENOMEM, RS_EHIP. */
 int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,

@@ -1045,7 +1045,8 @@ template <int EB>
 __device__ __forceinline__ void unpack_tm_kernel_job(unsigned jb, unsigned n_jobs, const TmJob* __restrict__ jobs,
                                                              const uint8_t* __restrict__ gathered,
                                                              void* const* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kTmStage * 4];
+  extern __shared__ __attribute__((aligned(16))) uint8_t tm_stage_bytes[];   // the plan's largest strip
+  uint8_t* stage = tm_stage_bytes;
   const TmJob j = jobs[jb];
   const int bc = j.bc, h = j.h, k = j.k, tid = threadIdx.x;
   const int run = h * bc, width = k * bc;
@@ -1054,28 +1055,28 @@ __device__ __forceinline__ void unpack_tm_kernel_job(unsigned jb, unsigned n_job
   if ((bc * EB) % 16 == 0 && (j.cols * EB) % 16 == 0) {
     constexpr int VE = 16 / EB;
     const int rv = run / VE, total = k * rv;
-    for (int v = tid; v < total; v += kThreads) {
+    for (int v = tid; v < total; v += kTmLdsThreads) {
       const int t = v / rv, e = (v - t * rv) * VE, r = e / bc, c = e - r * bc;
       *reinterpret_cast<u32x4*>(stage + (r * width + t * bc + c) * EB) =
           ldg(reinterpret_cast<const u32x4*>(src + (static_cast<int64_t>(t) * j.tile_elems + e) * EB));
     }
     __syncthreads();
     const int wv = width / VE, total2 = h * wv;
-    for (int v = tid; v < total2; v += kThreads) {
+    for (int v = tid; v < total2; v += kTmLdsThreads) {
       const int r = v / wv, w = v - r * wv;
       stg(reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(r) * j.cols + w * VE) * EB),
           *reinterpret_cast<const u32x4*>(stage + (r * width + w * VE) * EB));
     }
     return;
   }
-  for (int v = tid; v < k * run; v += kThreads) {
+  for (int v = tid; v < k * run; v += kTmLdsThreads) {
     const int t = v / run, e = v - t * run, r = e / bc, c = e - r * bc;
     const uint8_t* from = src + (static_cast<int64_t>(t) * j.tile_elems + e) * EB;
     uint8_t* to = stage + (r * width + t * bc + c) * EB;
     for (int b = 0; b < EB; ++b) to[b] = from[b];
   }
   __syncthreads();
-  for (int v = tid; v < h * width; v += kThreads) {
+  for (int v = tid; v < h * width; v += kTmLdsThreads) {
     const int r = v / width, w = v - r * width;
     uint8_t* to = out + (static_cast<int64_t>(r) * j.cols + w) * EB;
     const uint8_t* from = stage + v * EB;
@@ -1084,7 +1085,7 @@ __device__ __forceinline__ void unpack_tm_kernel_job(unsigned jb, unsigned n_job
 }
 
 template <int EB>
-__global__ __launch_bounds__(kThreads) void unpack_tm_kernel(const TmJob* __restrict__ jobs,
+__global__ __launch_bounds__(kTmLdsThreads) void unpack_tm_kernel(const TmJob* __restrict__ jobs,
                                                              const uint8_t* __restrict__ gathered,
                                                              void* const* __restrict__ dst, unsigned n_jobs) {
   for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
@@ -1102,20 +1103,21 @@ template <bool BF16, bool ACC>
 __device__ __forceinline__ void pack_tm_kernel_job(unsigned jb, unsigned n_jobs, const TmJob* __restrict__ jobs,
                                                            const void* const* __restrict__ src,
                                                            const float* prev, float* out, float sigma) {
-  __shared__ __attribute__((aligned(16))) float stage[kTmStage];
+  extern __shared__ __attribute__((aligned(16))) float tm_stage_f32[];   // the plan's largest strip
+  float* stage = tm_stage_f32;
   const TmJob j = jobs[jb];
   const int bc = j.bc, h = j.h, k = j.k, tid = threadIdx.x;
   const int run = h * bc, width = k * bc;
   const void* g = src[j.tensor];
   if (bc % 4 == 0 && j.cols % 4 == 0) {
     const int wv = width / 4, total = h * wv;
-    for (int v = tid; v < total; v += kThreads) {
+    for (int v = tid; v < total; v += kTmLdsThreads) {
       const int r = v / wv, w = v - r * wv;
       *reinterpret_cast<f32x4*>(stage + r * width + 4 * w) = load4<BF16>(g, j.toff + static_cast<int64_t>(r) * j.cols + 4 * w);
     }
     __syncthreads();
     const int rv = run / 4, total2 = k * rv;
-    for (int v = tid; v < total2; v += kThreads) {
+    for (int v = tid; v < total2; v += kTmLdsThreads) {
       const int t = v / rv, e = (v - t * rv) * 4, r = e / bc, c = e - r * bc;
       const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
       const f32x4 x = *reinterpret_cast<const f32x4*>(stage + r * width + t * bc + c);
@@ -1128,12 +1130,12 @@ __device__ __forceinline__ void pack_tm_kernel_job(unsigned jb, unsigned n_jobs,
     }
     return;
   }
-  for (int v = tid; v < h * width; v += kThreads) {
+  for (int v = tid; v < h * width; v += kTmLdsThreads) {
     const int r = v / width, w = v - r * width;
     stage[v] = load1<BF16>(g, j.toff + static_cast<int64_t>(r) * j.cols + w);
   }
   __syncthreads();
-  for (int v = tid; v < k * run; v += kThreads) {
+  for (int v = tid; v < k * run; v += kTmLdsThreads) {
     const int t = v / run, e = v - t * run, r = e / bc, c = e - r * bc;
     const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
     float y = __fmul_rn(stage[r * width + t * bc + c], sigma);
@@ -1143,7 +1145,7 @@ __device__ __forceinline__ void pack_tm_kernel_job(unsigned jb, unsigned n_jobs,
 }
 
 template <bool BF16, bool ACC>
-__global__ __launch_bounds__(kThreads) void pack_tm_kernel(const TmJob* __restrict__ jobs,
+__global__ __launch_bounds__(kTmLdsThreads) void pack_tm_kernel(const TmJob* __restrict__ jobs,
                                                            const void* const* __restrict__ src,
                                                            const float* prev, float* out, float sigma, unsigned n_jobs) {
   for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
@@ -1442,8 +1444,8 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
     hipLaunchKernelGGL(unpack_kernel, grid_of(p, n), dim3(kUnpackThreads), 0, s, p->unpack, gb, p->dst.dev, eb,
                        static_cast<int>(split), static_cast<unsigned>(n));
   }
-  if (p->n_tm && !p->tm_lds) {
-    const int64_t split = tm_split(16 / eb);
+  if (p->n_tm && !p->tm_unpack_lds) {
+    const int64_t split = tm_pieces(p->tm_max_strip, 16 / eb, kTmThreads);
     const int64_t n = p->n_tm * split;
     const dim3 g = grid_of(p, n), b(kTmThreads);
     const int sp = static_cast<int>(split);
@@ -1454,9 +1456,10 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
   } else if (p->n_tm) {
     const dim3 g = grid_of(p, p->n_tm);
     const unsigned nj = static_cast<unsigned>(p->n_tm);
-    if (eb == 4) hipLaunchKernelGGL(unpack_tm_kernel<4>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev, nj);
-    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_kernel<2>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev, nj);
-    else hipLaunchKernelGGL(unpack_tm_kernel<1>, g, dim3(kThreads), 0, s, p->tmjobs, gb, p->dst.dev, nj);
+    const unsigned lds = static_cast<unsigned>(p->tm_max_strip * eb);
+    if (eb == 4) hipLaunchKernelGGL(unpack_tm_kernel<4>, g, dim3(kTmLdsThreads), lds, s, p->tmjobs, gb, p->dst.dev, nj);
+    else if (eb == 2) hipLaunchKernelGGL(unpack_tm_kernel<2>, g, dim3(kTmLdsThreads), lds, s, p->tmjobs, gb, p->dst.dev, nj);
+    else hipLaunchKernelGGL(unpack_tm_kernel<1>, g, dim3(kTmLdsThreads), lds, s, p->tmjobs, gb, p->dst.dev, nj);
   }
   return launched(who);
 }
@@ -1489,7 +1492,7 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
   if (st != RS_OK) return st;
   const int64_t n_pieces = p->n_pack * kPackSplit;
   const unsigned np = static_cast<unsigned>(n_pieces);
-  const dim3 grid = grid_of(p, n_pieces), sblock(kPackThreads), block(kThreads);
+  const dim3 grid = grid_of(p, n_pieces), sblock(kPackThreads);
   void** tab = p->src.dev;
   if (p->n_pack) {
     if (src_dt == RS_F32) {
@@ -1500,8 +1503,8 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
       else hipLaunchKernelGGL((pack_kernel<true, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
     }
   }
-  if (p->n_tm && !p->tm_lds) {
-    const int64_t split = tm_split(4);
+  if (p->n_tm && !p->tm_pack_lds) {
+    const int64_t split = tm_pieces(p->tm_max_strip, 4, kTmThreads);
     const int64_t n = p->n_tm * split;
     const dim3 g = grid_of(p, n), b(kTmThreads);
     const int sp = static_cast<int>(split);
@@ -1516,12 +1519,13 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
   } else if (p->n_tm) {
     const dim3 g = grid_of(p, p->n_tm);
     const unsigned nj = static_cast<unsigned>(p->n_tm);
+    const unsigned lds = static_cast<unsigned>(p->tm_max_strip * 4);
     if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_tm_kernel<false, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
-      else hipLaunchKernelGGL((pack_tm_kernel<false, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
+      if (prev) hipLaunchKernelGGL((pack_tm_kernel<false, true>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
+      else hipLaunchKernelGGL((pack_tm_kernel<false, false>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
     } else {
-      if (prev) hipLaunchKernelGGL((pack_tm_kernel<true, true>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
-      else hipLaunchKernelGGL((pack_tm_kernel<true, false>), g, block, 0, s, p->tmjobs, tab, prev, packed, sigma, nj);
+      if (prev) hipLaunchKernelGGL((pack_tm_kernel<true, true>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
+      else hipLaunchKernelGGL((pack_tm_kernel<true, false>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
     }
   }
   return launched(who);
@@ -1655,7 +1659,7 @@ void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipS
     hipLaunchKernelGGL((gather_flat_kernel<FMT, HW, BF16OUT>), grid_of(p, p->n_gflat), dim3(kFlatThreads), 0, s, flats, q,
                        scales, p->gdst.dev, static_cast<unsigned>(p->n_gflat));
   if (p->n_tm) {
-    const int64_t split = tm_gather_split(BF16OUT ? 8 : 4);
+    const int64_t split = tm_pieces(p->tm_max_strip, BF16OUT ? 8 : 4, kGatherPiece);
     const int64_t n = p->n_tm * split;
     hipLaunchKernelGGL((gather_tm_kernel<FMT, HW, BF16OUT>), grid_of(p, n), dim3(kGatherThreads), 0, s, p->tmjobs, q,
                        scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));

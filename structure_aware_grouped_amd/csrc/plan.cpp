@@ -81,6 +81,7 @@ struct Tables {
   std::vector<PackChunk> pack;
   std::vector<QJob> qjobs;          // sorted by kind: tiles, flat groups, zero ranges
   int64_t n_qtile = 0, n_qflat = 0, n_qzero = 0;
+  int64_t tm_max_strip = 0;
   std::vector<GatherChunk> gchunks;
   std::vector<QJob> gjobs;          // tiles, then flat groups
   int64_t n_gtile = 0, n_gflat = 0;
@@ -111,8 +112,9 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     const Tensor& x = t[i];
     if (x.kind == RS_TILEMAJOR) {
       const int64_t br = x.p0, bc = x.p1, ntc = x.cols / bc;
-      const int64_t h = std::min<int64_t>(br, std::max<int64_t>(1, std::min<int64_t>(8, kTmStage / bc)));
-      const int64_t k = std::max<int64_t>(1, std::min(ntc, kTmStage / (h * bc)));
+      const int64_t h = std::min<int64_t>(br, std::max<int64_t>(1, std::min<int64_t>(kTmRows, kTmStrip / bc)));
+      const int64_t k = std::max<int64_t>(1, std::min(ntc, kTmStrip / (h * bc)));
+      tb->tm_max_strip = std::max(tb->tm_max_strip, h * k * bc);   // <= max(kTmStrip, bc) <= kTmStage
       for (int64_t tr = 0; tr < x.rows / br; ++tr)
         for (int64_t tc0 = 0; tc0 < ntc; tc0 += k)
           for (int64_t r0 = 0; r0 < br; r0 += h) {
@@ -403,7 +405,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     const int64_t items = std::max({static_cast<int64_t>(tb.unpack.size()) * unpack_split(4),
                                     static_cast<int64_t>(tb.pack.size()) * kPackSplit,
                                     static_cast<int64_t>(tb.gchunks.size()) * gather_split(4),
-                                    static_cast<int64_t>(tb.tm.size()) * tm_split(4),
+                                    static_cast<int64_t>(tb.tm.size()) * tm_pieces(tb.tm_max_strip, 4, kTmThreads),
                                     static_cast<int64_t>(tb.qjobs.size()), static_cast<int64_t>(tb.gjobs.size())});
     if (items > 0xFFFFFFFFll)
       return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(items) +
@@ -430,6 +432,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->n_qtile = tb.n_qtile;
     p->n_qflat = tb.n_qflat;
     p->n_qzero = tb.n_qzero;
+    p->tm_max_strip = tb.tm_max_strip;
     p->n_gchunks = static_cast<int64_t>(tb.gchunks.size());
     p->n_gtile = tb.n_gtile;
     p->n_gflat = tb.n_gflat;
@@ -438,10 +441,13 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     // RS_E4M3_ENCODER=sw selects the integer encoder, which gives the same codes.
     const char* enc = std::getenv("RS_E4M3_ENCODER");
     p->e4m3_hw = !(enc && std::strcmp(enc, "sw") == 0);
-    // Tile-major unpack / pack: direct kernels by default; RS_TM_KERNEL=lds
-    // selects the LDS-staged ones (same results).
-    const char* tmk = std::getenv("RS_TM_KERNEL");
-    p->tm_lds = tmk && std::strcmp(tmk, "lds") == 0;
+    // Tile-major reorder: staged through LDS by default; RS_TM_KERNEL=direct
+    // selects the direct kernels (=lds the staged ones) for unpack and pack.
+    // Both give the same results.
+    if (const char* tmk = std::getenv("RS_TM_KERNEL")) {
+      if (std::strcmp(tmk, "lds") == 0) p->tm_unpack_lds = p->tm_pack_lds = true;
+      if (std::strcmp(tmk, "direct") == 0) p->tm_unpack_lds = p->tm_pack_lds = false;
+    }
     // RS_MAX_GRID=n caps every launch at n workgroups (rounded down to a
     // multiple of 8, at least 8), so the workgroups loop over work items; the
     // results do not change.

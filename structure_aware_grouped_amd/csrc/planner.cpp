@@ -72,7 +72,7 @@ bool spec_ok(const rs_tensor_spec& s, std::string* why) {
       break;
     case RS_TILEMAJOR:
       if (s.p0 < 1 || s.p1 < 1) return bad("TILEMAJOR needs p0, p1 >= 1");
-      if (s.p0 > (int64_t(1) << 24) || s.p1 > 8192 || s.p0 * s.p1 > (int64_t(1) << 24))
+      if (s.p0 > (int64_t(1) << 24) || s.p1 > 8192 || s.p1 > kTmStage || s.p0 * s.p1 > (int64_t(1) << 24))
         return bad("TILEMAJOR tiles hold at most 2^24 elements and 8192 columns");
       if (s.rows % s.p0 != 0 || s.cols % s.p1 != 0) return bad("TILEMAJOR tiles must cover the tensor exactly");
       if ((s.p0 * s.p1) % 16 != 0) return bad("TILEMAJOR tile size must be a multiple of 16 elements");

@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+
 #include "rs.h"
 
 namespace rs {
@@ -169,16 +171,36 @@ struct TmJob {
   int32_t bc;
 };
 
-constexpr int64_t kTmStage = 8192;   // elements per tile-major job (staged in LDS: 32 KiB as fp32)
-// Tile-major reorder: direct (each lane maps its own 16-byte vector between the
-// two layouts, small split workgroups; the default) or staged through LDS (one
-// 256-thread workgroup per job; RS_TM_KERNEL=lds at rs_plan_load).
+#ifndef RS_TM_STRIP
+#define RS_TM_STRIP 2048
+#endif
+#ifndef RS_TM_ROWS
+#define RS_TM_ROWS 2
+#endif
+#ifndef RS_TM_LDS_THREADS
+#define RS_TM_LDS_THREADS 128
+#endif
+// A tile-major job is a strip of up to kTmRows rows of consecutive tiles of
+// one tile row, about kTmStrip elements; a single row of the widest allowed
+// tile (8192 columns) is the largest strip.
+constexpr int64_t kTmStrip = RS_TM_STRIP;
+constexpr int64_t kTmStage = 8192;          // largest strip, in elements
+constexpr int64_t kTmRows = RS_TM_ROWS;
+constexpr int kTmLdsThreads = RS_TM_LDS_THREADS;
+static_assert(kTmStrip <= kTmStage && kTmStage <= 16384, "tile-major strips: indices stay under 2^16");
+// Tile-major reorder: staged through LDS (one kTmLdsThreads workgroup per
+// strip; the default) or direct (each lane maps its own 16-byte vector between
+// the two layouts, on small split workgroups; RS_TM_KERNEL=direct at
+// rs_plan_load). Both give the same results.
 #ifndef RS_TM_THREADS
 #define RS_TM_THREADS 64
 #endif
 constexpr int kTmThreads = RS_TM_THREADS;
 // pieces per job for vectors of vec elements (direct kernels)
-constexpr int64_t tm_split(int64_t vec) { return (kTmStage / vec + kTmThreads - 1) / kTmThreads; }
+// pieces per job: the plan's largest strip in vectors of vec elements, per_piece vectors each
+inline int64_t tm_pieces(int64_t max_strip, int64_t vec, int64_t per_piece) {
+  return std::max<int64_t>(1, (max_strip / vec + per_piece - 1) / per_piece);
+}
 
 // Gather-side work item: a contiguous run of whole rows of one quantised
 // tensor, inside one band of tiles (TILE) or made of whole flat blocks (FLAT,
@@ -216,8 +238,7 @@ constexpr int kGatherThreads = RS_GATHER_THREADS, kGatherVec = RS_GATHER_VEC;
 constexpr int64_t kGatherPiece = int64_t(kGatherThreads) * kGatherVec;
 // pieces per run for VEC codes per vector; longer runs loop
 constexpr int64_t gather_split(int64_t vec) { return (kGatherChunk / vec + kGatherPiece - 1) / kGatherPiece; }
-// pieces per tile-major gather job (a strip of at most kTmStage elements)
-constexpr int64_t tm_gather_split(int64_t vec) { return (kTmStage / vec + kGatherPiece - 1) / kGatherPiece; }
+
 
 // Device copy of a per-tensor pointer table plus the host state that decides
 // when it must be uploaded again.
@@ -267,6 +288,8 @@ struct rs_plan {
   rs::PtrTable src;   // pack sources
   rs::PtrTable gdst;  // unpack-dequant destinations
   bool e4m3_hw = false;  // use gfx950's FP8 conversion instructions
-  bool tm_lds = false;   // tile-major unpack / pack staged through LDS instead of the direct kernels
+  int64_t tm_max_strip = 0;    // elements of the largest tile-major job (LDS stage, piece count)
+  bool tm_unpack_lds = true;   // tile-major unpack staged through LDS (else the direct kernel)
+  bool tm_pack_lds = true;     // tile-major pack staged through LDS (else the direct kernel)
   int64_t max_grid = rs::kMaxGrid;   // workgroups per launch; beyond it workgroups loop over items
 };
