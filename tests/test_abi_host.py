@@ -157,3 +157,28 @@ def test_plan_larger_than_any_device_is_rejected(rs):
     big = [TensorSpec("big", 1 << 20, 1 << 19, "ELEM")]      # 2^39 elements
     assert _status(lambda: rs.rs_plan_load(big, 2, 1 << 39, [0], R_mat=2)) == b.RS_ERANGE
     assert "2^39" in b.load().rs_last_error().decode()
+
+
+def test_empty_group_and_null_outputs_are_rejected(rs):
+    from structure_aware_grouped_amd import binding as b
+    assert _status(lambda: rs.rs_plan_build([], 4)) == b.RS_EINVAL
+    lib = b.load()
+    spec = b.specs_array([TensorSpec("a", 4, 4, "ROWS", 1)])
+    S = b.ctypes.c_int64()
+    assert lib.rs_plan_build(spec, 1, 4, 16, 0, None, None, None, None) == b.RS_EINVAL
+    assert lib.rs_plan_build(spec, 1, 4, 16, 0, b.ctypes.byref(S), None, None, None) == b.RS_EINVAL
+    assert lib.rs_plan_build(spec, 1, 4, 16, 7, b.ctypes.byref(S), (b.ctypes.c_int64 * 1)(), None, None) \
+        == b.RS_EINVAL                                            # unknown order policy
+
+
+def test_largest_tensor_plans_on_the_host(rs):
+    """A single tensor of 2^40 elements (the spec limit) plans without overflow; one
+    more row is rejected."""
+    from structure_aware_grouped_amd import binding as b
+    big = TensorSpec("big", 1 << 20, 1 << 20, "ROWS", 1)
+    S, starts, _, _ = rs.rs_plan_build([big], 64)
+    assert starts == [0] and S == (1 << 40) // 64 and S % 16 == 0
+    ref = OP.plan([big], 64)
+    assert (S, starts) == (ref.S, [int(x) for x in ref.starts])
+    assert _status(lambda: rs.rs_plan_build([TensorSpec("big", (1 << 20) + 1, 1 << 20, "ROWS", 1)], 64)) \
+        == b.RS_EINVAL
