@@ -250,13 +250,15 @@ def test_mid_size_group(gpu_lib, pdtype):
 # Blocks larger than the register paths hold (a tile of more than 16384
 # elements, a flat block of more than 2048 fp32 / 4096 bf16 elements), so the
 # kernels take their two-pass element paths; plus a flat block size that is not
-# a multiple of 16 (per-block gather) and tile-major tiles of 32768 elements.
+# a multiple of 16 (per-block gather), tile-major tiles of 32768 elements and
+# tile-major tiles of the widest allowed shape (8192 columns).
 BIG_BLOCKS = [
     TensorSpec("tile_big", 300, 520, "TILE", 256, 128),
     TensorSpec("flat_big", 1, 20000, "FLAT", 6000),
     TensorSpec("tm_big", 512, 256, "TILEMAJOR", 256, 128),
     TensorSpec("flat_odd", 1, 3001, "FLAT", 1000),
     TensorSpec("norm", 300, 1, "ROWS", 1),
+    TensorSpec("tm_widest", 4, 16384, "TILEMAJOR", 2, 8192),   # 8192-column tiles: one-row strips
 ]
 
 
