@@ -182,3 +182,14 @@ def test_largest_tensor_plans_on_the_host(rs):
     assert (S, starts) == (ref.S, [int(x) for x in ref.starts])
     assert _status(lambda: rs.rs_plan_build([TensorSpec("big", (1 << 20) + 1, 1 << 20, "ROWS", 1)], 64)) \
         == b.RS_EINVAL
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No CPU fallback: opening a library that is not there raises, naming the build."""
+    import subprocess
+    import sys
+    code = ("import structure_aware_grouped_amd.binding as b\n"
+            f"try:\n    b.load({str(tmp_path / 'librs_hip.so')!r})\n"
+            "except RuntimeError as e:\n    print('raised:', e)\nelse:\n    print('loaded')\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert "raised:" in out.stdout and "no CPU fallback" in out.stdout, out.stdout + out.stderr
