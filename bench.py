@@ -42,7 +42,8 @@ PROFILE_TRAFFIC = {(1, "step", False): "llama3_8b_v64", (1, "step", True): "llam
                    (2, "step", False): "llama3_70b_v1024", (3, "step", False): "moe128_v256",
                    (4, "step", False): "adam_states_llama3_8b_v64"}
 KERNEL_SOURCES = [os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", f)
-                  for f in ("kernels.hip", "rs_internal.h", "plan.cpp")]
+                  for f in ("device_common.h", "host_common.h", "transform.hip", "quant.hip", "gather.hip",
+                            "adam.hip", "rs_internal.h", "plan.cpp")]
 
 
 def parse():

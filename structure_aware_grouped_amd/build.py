@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librs_hip.so")
-SOURCES = ["planner.cpp", "plan.cpp", "kernels.hip"]
+SOURCES = ["planner.cpp", "plan.cpp", "transform.hip", "quant.hip", "gather.hip", "adam.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

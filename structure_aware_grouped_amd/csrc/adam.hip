@@ -1,0 +1,219 @@
+// One AdamW step on block-quantised 8-bit state on gfx950: kernels and the
+// rs_adam8_step entry point.
+//
+// Per quantisation block: dequantise int8 m and uint8 v, update them and the
+// fp32 parameters with the packed gradient, requantise m and v with fresh
+// block scales ("veScale-FSDP: flexible, structure-aware sharding at 10K-GPU
+// scale", feynmanwiki walkthrough, 8-bit Adam paragraph: each device
+// quantises its own whole blocks). Every operation is one IEEE fp32 rounding.
+#include "host_common.h"
+
+namespace rs {
+namespace {
+
+// ------------------------------------------------------------------ 8-bit Adam step
+
+struct AdamK {
+  float b1, b2, c1, c2, eps, step_size, inv_bc2_sqrt, decay;
+};
+
+// m1, v1 and the new parameter of one element (every operation rounded).
+// The square root is __builtin_sqrtf, which this build (correctly rounded
+// divide and sqrt) lowers to a correctly rounded sequence; __fsqrt_rn is not
+// correctly rounded on this toolchain (about 15% of inputs differ by an ulp).
+__device__ __forceinline__ void adam_elem(float p, float g, float m0, float v0, const AdamK& k,
+                                          float& p1, float& m1, float& v1) {
+  m1 = __fadd_rn(__fmul_rn(k.b1, m0), __fmul_rn(k.c1, g));
+  v1 = __fadd_rn(__fmul_rn(k.b2, v0), __fmul_rn(k.c2, __fmul_rn(g, g)));
+  const float den = __fadd_rn(__fmul_rn(__builtin_sqrtf(v1), k.inv_bc2_sqrt), k.eps);
+  p1 = __fsub_rn(__fmul_rn(p, k.decay), __fmul_rn(k.step_size, __fdiv_rn(m1, den)));
+}
+
+// Scale and reciprocal of a block with absmax `amax` for code range Q.
+__device__ __forceinline__ void block_scale(float amax, float Q, float& scale, float& r) {
+  const bool zero = amax == 0.0f;
+  scale = zero ? 1.0f : __fdiv_rn(amax, Q);
+  r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
+}
+
+// One quantisation block (element (r, c) at base + r*stride + c) handled by
+// NT threads. The old scales are read before the block's max is reduced and
+// the new ones written after it. Fast path: 4-element vectors, every updated
+// m and v kept in registers; otherwise two passes (the second recomputes m1
+// and v1 from the old codes, which it then overwrites).
+template <int NT, int MAXV>
+__device__ void adam_block(float* __restrict__ param, const float* __restrict__ grad,
+                           uint8_t* __restrict__ qm, float* __restrict__ sm, uint8_t* __restrict__ qv,
+                           float* __restrict__ sv, int64_t base, int64_t stride, int rows, int cols,
+                           int64_t sidx, int tid, uint32_t* red, const AdamK& k) {
+  const float sm0 = sm[sidx], sv0 = sv[sidx];
+  const int vpr = cols / 4;
+  const int nvec = rows * vpr;
+  if ((base % 4 == 0) && (stride % 4 == 0) && (cols % 4 == 0) && nvec <= NT * MAXV) {
+    f32x4 m1[MAXV], v1[MAXV];
+    uint32_t am = 0, av = 0;
+    GridWalk w(tid, vpr, NT);
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      if (tid + j * NT < nvec) {
+        const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 4;
+        const f32x4 p = ldg(reinterpret_cast<const f32x4*>(param + e));
+        const f32x4 g = ldg(reinterpret_cast<const f32x4*>(grad + e));
+        const uint32_t cm = ldg(reinterpret_cast<const uint32_t*>(qm + e));
+        const uint32_t cv = ldg(reinterpret_cast<const uint32_t*>(qv + e));
+        const f32x4 dm = decode4<FMT_I8, false>(cm), dv = decode4<FMT_U8, false>(cv);
+        const float pin[4] = {p.x, p.y, p.z, p.w}, gin[4] = {g.x, g.y, g.z, g.w};
+        const float dmi[4] = {dm.x, dm.y, dm.z, dm.w}, dvi[4] = {dv.x, dv.y, dv.z, dv.w};
+        float po[4], mo[4], vo[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          adam_elem(pin[h], gin[h], __fmul_rn(dmi[h], sm0), __fmul_rn(dvi[h], sv0), k, po[h], mo[h], vo[h]);
+        m1[j] = f32x4{mo[0], mo[1], mo[2], mo[3]};
+        v1[j] = f32x4{vo[0], vo[1], vo[2], vo[3]};
+        stg(reinterpret_cast<f32x4*>(param + e), f32x4{po[0], po[1], po[2], po[3]});
+        am = max(am, max(max(__float_as_uint(m1[j].x) & 0x7fffffffu, __float_as_uint(m1[j].y) & 0x7fffffffu),
+                         max(__float_as_uint(m1[j].z) & 0x7fffffffu, __float_as_uint(m1[j].w) & 0x7fffffffu)));
+        av = max(av, max(max(__float_as_uint(v1[j].x) & 0x7fffffffu, __float_as_uint(v1[j].y) & 0x7fffffffu),
+                         max(__float_as_uint(v1[j].z) & 0x7fffffffu, __float_as_uint(v1[j].w) & 0x7fffffffu)));
+      }
+      w.next();
+    }
+    const float amax_m = __uint_as_float(group_max<NT>(am, tid, red));
+    const float amax_v = __uint_as_float(group_max<NT>(av, tid, NT > kWave ? red + NT / kWave : nullptr));
+    float scm, rm, scv, rv;
+    block_scale(amax_m, 127.0f, scm, rm);
+    block_scale(amax_v, 255.0f, scv, rv);
+    if (tid == 0) {
+      sm[sidx] = scm;
+      sv[sidx] = scv;
+    }
+    GridWalk w2(tid, vpr, NT);
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      if (tid + j * NT < nvec) {
+        const int64_t e = base + static_cast<int64_t>(w2.row) * stride + static_cast<int64_t>(w2.col) * 4;
+        const uint32_t cm = amax_m == 0.0f ? 0u
+            : encode4<FMT_I8, false>(__fmul_rn(m1[j].x, rm), __fmul_rn(m1[j].y, rm), __fmul_rn(m1[j].z, rm), __fmul_rn(m1[j].w, rm));
+        const uint32_t cv = amax_v == 0.0f ? 0u
+            : encode4<FMT_U8, false>(__fmul_rn(v1[j].x, rv), __fmul_rn(v1[j].y, rv), __fmul_rn(v1[j].z, rv), __fmul_rn(v1[j].w, rv));
+        stg(reinterpret_cast<uint32_t*>(qm + e), cm);
+        stg(reinterpret_cast<uint32_t*>(qv + e), cv);
+      }
+      w2.next();
+    }
+    return;
+  }
+  // general path
+  const int64_t total = static_cast<int64_t>(rows) * cols;
+  uint32_t am = 0, av = 0;
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    const int64_t e = base + rr * stride + cc;
+    float p1, m1, v1;
+    adam_elem(param[e], grad[e], __fmul_rn(decode1<FMT_I8, false>(qm[e]), sm0),
+              __fmul_rn(decode1<FMT_U8, false>(qv[e]), sv0), k, p1, m1, v1);
+    param[e] = p1;
+    am = max(am, __float_as_uint(m1) & 0x7fffffffu);
+    av = max(av, __float_as_uint(v1) & 0x7fffffffu);
+  }
+  const float amax_m = __uint_as_float(group_max<NT>(am, tid, red));
+  const float amax_v = __uint_as_float(group_max<NT>(av, tid, NT > kWave ? red + NT / kWave : nullptr));
+  float scm, rm, scv, rv;
+  block_scale(amax_m, 127.0f, scm, rm);
+  block_scale(amax_v, 255.0f, scv, rv);
+  if (tid == 0) {
+    sm[sidx] = scm;
+    sv[sidx] = scv;
+  }
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    const int64_t e = base + rr * stride + cc;
+    float p1, m1, v1;  // m1 and v1 again, from the old codes (p1 is discarded)
+    adam_elem(0.0f, grad[e], __fmul_rn(decode1<FMT_I8, false>(qm[e]), sm0),
+              __fmul_rn(decode1<FMT_U8, false>(qv[e]), sv0), k, p1, m1, v1);
+    qm[e] = amax_m == 0.0f ? 0 : static_cast<uint8_t>(encode1<FMT_I8, false>(__fmul_rn(m1, rm)));
+    qv[e] = amax_v == 0.0f ? 0 : static_cast<uint8_t>(encode1<FMT_U8, false>(__fmul_rn(v1, rv)));
+  }
+}
+
+__device__ __forceinline__ void adam_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, float* param,
+                                                             const float* grad, uint8_t* qm, float* sm,
+                                                             uint8_t* qv, float* sv, AdamK k) {
+  __shared__ uint32_t red[2 * kThreads / kWave];
+  const unsigned b = piece_index<kTileXcdGroup>(jb, n_jobs);
+  const QJob j = jobs[b];
+  adam_block<kThreads, 4>(param, grad, qm, sm, qv, sv, j.base, j.stride, j.rows, j.cols, j.scale,
+                          threadIdx.x, red, k);
+}
+
+__global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restrict__ jobs, float* param,
+                                                             const float* grad, uint8_t* qm, float* sm,
+                                                             uint8_t* qv, float* sv, AdamK k, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    adam_tile_kernel_job(jb, n_jobs, jobs, param, grad, qm, sm, qv, sv, k);
+    __syncthreads();   // the next job reuses this workgroup's LDS
+  }
+}
+
+__device__ __forceinline__ void adam_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, float* param,
+                                                             const float* grad, uint8_t* qm, float* sm,
+                                                             uint8_t* qv, float* sv, AdamK k) {
+  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
+  const QJob j = jobs[b];
+  const int wave = threadIdx.x / kWave;
+  if (wave >= j.rows) return;
+  const int len = wave == j.rows - 1 ? j.last : j.cols;
+  adam_block<kWave, 8>(param, grad, qm, sm, qv, sv, j.base + static_cast<int64_t>(wave) * j.cols, len, 1,
+                       len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr, k);
+}
+
+__global__ __launch_bounds__(kFlatThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
+                                                             const float* grad, uint8_t* qm, float* sm,
+                                                             uint8_t* qv, float* sv, AdamK k, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    adam_flat_kernel_job(jb, n_jobs, jobs, param, grad, qm, sm, qv, sv, k);
+  }
+}
+
+}  // namespace
+}  // namespace rs
+
+using namespace rs;
+
+extern "C" int rs_adam8_step(rs_plan* p, float* param, const float* grad, void* q_m, float* s_m,
+                             void* q_v, float* s_v, const rs_adam_hparams* hp, void* stream) {
+  const char* who = "rs_adam8_step";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  if (!param || !grad || !q_m || !q_v || !hp || (p->n_qblocks > 0 && (!s_m || !s_v)))
+    return fail(RS_EINVAL, std::string(who) + ": null argument");
+  if (hp->step < 1 || !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) ||
+      !(hp->eps >= 0.0f) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay) || hp->reserved != 0)
+    return fail(RS_EINVAL, std::string(who) + ": bad hyper-parameters");
+  if (!aligned16(param) || !aligned16(grad) || !aligned16(q_m) || !aligned16(q_v))
+    return fail(RS_EALIGN, std::string(who) + ": buffers must be 16-byte aligned");
+  const double b1 = hp->beta1, b2 = hp->beta2, lr = hp->lr, wd = hp->weight_decay;
+  const double t = static_cast<double>(hp->step);
+  AdamK k;
+  k.b1 = hp->beta1;
+  k.b2 = hp->beta2;
+  k.eps = hp->eps;
+  k.c1 = static_cast<float>(1.0 - b1);
+  k.c2 = static_cast<float>(1.0 - b2);
+  k.step_size = static_cast<float>(lr / (1.0 - std::pow(b1, t)));
+  k.inv_bc2_sqrt = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(b2, t)));
+  k.decay = static_cast<float>(1.0 - lr * wd);
+  if (p->n_qtile + p->n_qflat == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* qmb = static_cast<uint8_t*>(q_m);
+  uint8_t* qvb = static_cast<uint8_t*>(q_v);
+  if (p->n_qtile)
+    hipLaunchKernelGGL(adam_tile_kernel, grid_of(p, p->n_qtile), dim3(kThreads), 0, s, p->qjobs, param, grad, qmb, s_m,
+                       qvb, s_v, k, static_cast<unsigned>(p->n_qtile));
+  if (p->n_qflat)
+    hipLaunchKernelGGL(adam_flat_kernel, grid_of(p, p->n_qflat), dim3(kFlatThreads), 0, s, p->qjobs + p->n_qtile, param,
+                       grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(p->n_qflat));
+  return launched(who);
+}
+

@@ -1,0 +1,407 @@
+// Block quantisation and dequantisation of the flat buffer on gfx950: kernels
+// and the rs_block_quant / rs_block_dequant entry points.
+//
+// Every locally whole block (a tile, or a flat block) is quantised by its own
+// absmax: scale = fl32(amax / Q), codes of fl32(x * fl32(Q / amax))
+// ("veScale-FSDP: flexible, structure-aware sharding at 10K-GPU scale",
+// feynmanwiki walkthrough, the block-quantisation and 8-bit Adam paragraphs).
+// A tile stays in the registers of one 512-thread workgroup, a flat block in
+// one wave, so each input byte is read once; the absmax is a wave shuffle
+// reduction plus, for tiles, an LDS combine over the waves.
+#include "host_common.h"
+
+namespace rs {
+namespace {
+
+// ------------------------------------------------------------------ quant
+
+// One quantisation block: element (r, c) at base + r*stride + c, r < rows,
+// c < cols, handled by NT threads (tid in [0, NT)). Fast path: every vector
+// of the block stays in registers (at most NT*MAXV 16-byte vectors, rows and
+// base aligned to a vector). Otherwise: two passes over memory, element by
+// element.
+template <bool BF16, int FMT, bool HW, int NT, int MAXV>
+__device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ q,
+                            float* __restrict__ scales, int64_t base, int64_t stride, int rows,
+                            int cols, int64_t sidx, int tid, uint32_t* red) {
+  using I = In<BF16>;
+  constexpr int VE = I::VE;
+  constexpr float Q = QMax<FMT>::v;
+  const int vpr = cols / VE;
+  const int nvec = rows * vpr;
+  const bool fast = (base % VE == 0) && (stride % VE == 0) && (cols % VE == 0) && nvec <= NT * MAXV;
+  const char* sb = static_cast<const char*>(src);
+
+  if (fast) {
+    u32x4 raw[MAXV];
+    uint32_t m = 0;
+    {
+      GridWalk w(tid, vpr, NT);
+#pragma unroll
+      for (int k = 0; k < MAXV; ++k) {
+        if (tid + k * NT < nvec) {
+          const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * VE;
+          raw[k] = ldg(reinterpret_cast<const u32x4*>(sb + e * I::EB));
+          m = max(m, I::absmax(raw[k]));
+        }
+        w.next();
+      }
+    }
+    const float amax = __uint_as_float(group_max<NT>(m, tid, red));
+    const bool zero = amax == 0.0f;
+    const float r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
+    if (tid == 0) scales[sidx] = zero ? 1.0f : __fdiv_rn(amax, Q);
+    GridWalk w(tid, vpr, NT);
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+      if (tid + k * NT < nvec) {
+        const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * VE;
+        float x[VE];
+        I::widen(raw[k], x);
+        uint32_t words[VE / 4];
+#pragma unroll
+        for (int h = 0; h < VE / 4; ++h) {
+          words[h] = zero ? 0u
+                          : encode4<FMT, HW>(__fmul_rn(x[4 * h], r), __fmul_rn(x[4 * h + 1], r),
+                                             __fmul_rn(x[4 * h + 2], r), __fmul_rn(x[4 * h + 3], r));
+        }
+        if constexpr (VE == 8) {
+          stg(reinterpret_cast<u32x2*>(q + e), u32x2{words[0], words[1]});
+        } else {
+          stg(reinterpret_cast<uint32_t*>(q + e), words[0]);
+        }
+      }
+      w.next();
+    }
+    return;
+  }
+
+  // general path: any alignment, any block size
+  const int64_t total = static_cast<int64_t>(rows) * cols;
+  uint32_t m = 0;
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    m = max(m, __float_as_uint(I::elem(src, base + rr * stride + cc)) & 0x7fffffffu);
+  }
+  const float amax = __uint_as_float(group_max<NT>(m, tid, red));
+  const bool zero = amax == 0.0f;
+  const float r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
+  if (tid == 0) scales[sidx] = zero ? 1.0f : __fdiv_rn(amax, Q);
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    const int64_t e = base + rr * stride + cc;
+    q[e] = zero ? 0 : static_cast<uint8_t>(encode1<FMT, HW>(__fmul_rn(I::elem(src, e), r)));
+  }
+}
+
+// Zero [base, base + len) of a byte array (codes) with 16-byte stores in the
+// middle, by NT threads.
+template <int NT = kThreads>
+__device__ void zero_bytes(uint8_t* q, int64_t base, int64_t len, int tid) {
+  const int64_t end = base + len;
+  const int64_t a0 = (base + 15) & ~int64_t(15);
+  const int64_t a1 = end & ~int64_t(15);
+  if (a0 >= a1) {
+    for (int64_t i = base + tid; i < end; i += NT) q[i] = 0;
+    return;
+  }
+  for (int64_t i = base + tid; i < a0; i += NT) q[i] = 0;
+  for (int64_t i = a1 + tid; i < end; i += NT) q[i] = 0;
+  u32x4* v = reinterpret_cast<u32x4*>(q + a0);
+  const int64_t nv = (a1 - a0) >> 4;
+  for (int64_t i = tid; i < nv; i += NT) stg(v + i, u32x4{0u, 0u, 0u, 0u});
+}
+
+// Zero [base, base + len) of an fp32 array with 16-byte stores in the
+// middle, by NT threads.
+template <int NT = kThreads>
+__device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
+  const int64_t end = base + len;
+  const int64_t a0 = (base + 3) & ~int64_t(3);
+  const int64_t a1 = end & ~int64_t(3);
+  if (a0 >= a1) {
+    for (int64_t i = base + tid; i < end; i += NT) o[i] = 0.0f;
+    return;
+  }
+  for (int64_t i = base + tid; i < a0; i += NT) o[i] = 0.0f;
+  for (int64_t i = a1 + tid; i < end; i += NT) o[i] = 0.0f;
+  f32x4* v = reinterpret_cast<f32x4*>(o + a0);
+  const int64_t nv = (a1 - a0) >> 2;
+  for (int64_t i = tid; i < nv; i += NT) stg(v + i, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+}
+
+// One workgroup per tile. Workgroups from n_main on take the zero-range jobs
+// that follow the tiles in the list and clear code bytes outside every block,
+// so the whole call is one launch.
+// kQuantThreads threads per tile; the register path holds a whole tile of up
+// to 16384 elements (2048 16-byte vectors of bf16, 4096 of fp32).
+template <bool BF16, int FMT, bool HW>
+__device__ __forceinline__ void quant_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
+                                                                   const void* __restrict__ src,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ scales) {
+  __shared__ uint32_t red[kQuantThreads / kWave];
+  const unsigned b = piece_index<kTileXcdGroup>(jb, n_jobs);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
+    zero_bytes<kQuantThreads>(q, j.base, j.stride, threadIdx.x);
+    return;
+  }
+  quant_block<BF16, FMT, HW, kQuantThreads, (BF16 ? 2048 : 4096) / kQuantThreads>(
+      src, q, scales, j.base, j.stride, j.rows, j.cols, j.scale, threadIdx.x, red);
+}
+
+template <bool BF16, int FMT, bool HW>
+__global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                                   const void* __restrict__ src,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ scales, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    quant_tile_kernel_job<BF16, FMT, HW>(jb, n_jobs, jobs, n_main, src, q, scales);
+    __syncthreads();   // the next job reuses this workgroup's LDS
+  }
+}
+
+// One wave per flat block, kFlatPerGroup blocks per workgroup; zero-range jobs
+// from n_main on, as in the tile kernel.
+template <bool BF16, int FMT, bool HW>
+__device__ __forceinline__ void quant_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
+                                                              const void* __restrict__ src,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales) {
+  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
+    zero_bytes<kFlatThreads>(q, j.base, j.stride, threadIdx.x);
+    return;
+  }
+  const int wave = threadIdx.x / kWave;
+  if (wave >= j.rows) return;
+  const int len = wave == j.rows - 1 ? j.last : j.cols;
+  quant_block<BF16, FMT, HW, kWave, 8>(src, q, scales, j.base + static_cast<int64_t>(wave) * j.cols, len,
+                                       1, len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr);
+}
+
+template <bool BF16, int FMT, bool HW>
+__global__ __launch_bounds__(kFlatThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                              const void* __restrict__ src,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    quant_flat_kernel_job<BF16, FMT, HW>(jb, n_jobs, jobs, n_main, src, q, scales);
+  }
+}
+
+// Code bytes of positions outside every block (a plan with no block at all).
+__device__ __forceinline__ void zero_codes_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs,
+                                                              uint8_t* __restrict__ q) {
+  const QJob j = jobs[jb];
+  zero_bytes(q, j.base, j.stride, threadIdx.x);
+}
+
+__global__ __launch_bounds__(kThreads) void zero_codes_kernel(const QJob* __restrict__ jobs,
+                                                              uint8_t* __restrict__ q, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    zero_codes_kernel_job(jb, n_jobs, jobs, q);
+  }
+}
+
+// ------------------------------------------------------------------ dequant
+
+template <int FMT, bool HW, int NT>
+__device__ void dequant_block(const uint8_t* __restrict__ q, float* __restrict__ out, float s,
+                              int64_t base, int64_t stride, int rows, int cols, int tid) {
+  if ((base % 4 == 0) && (stride % 4 == 0) && (cols % 4 == 0)) {
+    const int vpr = cols / 4;
+    const int nvec = rows * vpr;
+    GridWalk w(tid, vpr, NT);
+    for (int i = tid; i < nvec; i += NT) {
+      const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 4;
+      const f32x4 d = decode4<FMT, HW>(ldg(reinterpret_cast<const uint32_t*>(q + e)));
+      stg(reinterpret_cast<f32x4*>(out + e),
+          f32x4{__fmul_rn(d.x, s), __fmul_rn(d.y, s), __fmul_rn(d.z, s), __fmul_rn(d.w, s)});
+      w.next();
+    }
+    return;
+  }
+  const int64_t total = static_cast<int64_t>(rows) * cols;
+  for (int64_t i = tid; i < total; i += NT) {
+    const int64_t rr = i / cols, cc = i - rr * cols;
+    const int64_t e = base + rr * stride + cc;
+    out[e] = __fmul_rn(decode1<FMT, HW>(q[e]), s);
+  }
+}
+
+// Workgroups from n_main on clear the values outside every block (zero-range
+// jobs), as in the quant kernels.
+template <int FMT, bool HW>
+__device__ __forceinline__ void dequant_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out) {
+  const unsigned b = piece_index<kTileXcdGroup>(jb, n_jobs);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
+    zero_f32(out, j.base, j.stride, threadIdx.x);
+    return;
+  }
+  dequant_block<FMT, HW, kThreads>(q, out, scales[j.scale], j.base, j.stride, j.rows, j.cols,
+                                   threadIdx.x);
+}
+
+template <int FMT, bool HW>
+__global__ __launch_bounds__(kThreads) void dequant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    dequant_tile_kernel_job<FMT, HW>(jb, n_jobs, jobs, n_main, q, scales, out);
+  }
+}
+
+template <int FMT, bool HW>
+__device__ __forceinline__ void dequant_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out) {
+  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
+  const QJob j = jobs[b];
+  if (static_cast<int64_t>(b) >= n_main) {
+    zero_f32<kFlatThreads>(out, j.base, j.stride, threadIdx.x);
+    return;
+  }
+  const int wave = threadIdx.x / kWave;
+  if (wave >= j.rows) return;
+  const int len = wave == j.rows - 1 ? j.last : j.cols;
+  dequant_block<FMT, HW, kWave>(q, out, scales[j.scale + wave], j.base + static_cast<int64_t>(wave) * j.cols,
+                                len, 1, len, threadIdx.x & (kWave - 1));
+}
+
+template <int FMT, bool HW>
+__global__ __launch_bounds__(kFlatThreads) void dequant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
+                                                                const uint8_t* __restrict__ q,
+                                                                const float* __restrict__ scales,
+                                                                float* __restrict__ out, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    dequant_flat_kernel_job<FMT, HW>(jb, n_jobs, jobs, n_main, q, scales, out);
+  }
+}
+
+// Dequantised values of positions outside every block (a plan with no block at all).
+__device__ __forceinline__ void zero_values_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs,
+                                                               float* __restrict__ out) {
+  const QJob j = jobs[jb];
+  zero_f32(out, j.base, j.stride, threadIdx.x);
+}
+
+__global__ __launch_bounds__(kThreads) void zero_values_kernel(const QJob* __restrict__ jobs,
+                                                               float* __restrict__ out, unsigned n_jobs) {
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    zero_values_kernel_job(jb, n_jobs, jobs, out);
+  }
+}
+
+}  // namespace
+}  // namespace rs
+
+using namespace rs;
+
+namespace {
+
+// The zero-range jobs follow the flat groups, which follow the tiles: they ride
+// at the end of the last launch that has blocks, or get their own launch.
+template <bool BF16, int FMT, bool HW>
+void launch_quant_kinds(const rs_plan* p, const void* src, uint8_t* q, float* scales, hipStream_t s) {
+  const dim3 block(kThreads);
+  const QJob* tiles = p->qjobs;
+  const QJob* flats = tiles + p->n_qtile;
+  const int64_t nz = p->n_qzero;
+  if (p->n_qtile) {
+    const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
+    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), grid_of(p, n), dim3(kQuantThreads), 0, s, tiles,
+                       p->n_qtile, src, q, scales, static_cast<unsigned>(n));
+  }
+  if (p->n_qflat)
+    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), grid_of(p, p->n_qflat + nz), dim3(kFlatThreads), 0, s, flats,
+                       p->n_qflat, src, q, scales, static_cast<unsigned>(p->n_qflat + nz));
+  if (!p->n_qtile && !p->n_qflat && nz)
+    hipLaunchKernelGGL(zero_codes_kernel, grid_of(p, nz), block, 0, s, flats, q, static_cast<unsigned>(nz));
+}
+
+template <bool BF16>
+void launch_quant(const rs_plan* p, const void* src, int fmt, bool hw, uint8_t* q, float* scales,
+                  hipStream_t s) {
+  if (fmt == FMT_E4M3 && hw)
+    launch_quant_kinds<BF16, FMT_E4M3, true>(p, src, q, scales, s);
+  else if (fmt == FMT_E4M3)
+    launch_quant_kinds<BF16, FMT_E4M3, false>(p, src, q, scales, s);
+  else if (fmt == FMT_I8)
+    launch_quant_kinds<BF16, FMT_I8, false>(p, src, q, scales, s);
+  else
+    launch_quant_kinds<BF16, FMT_U8, false>(p, src, q, scales, s);
+}
+
+template <int FMT, bool HW>
+void launch_dequant(const rs_plan* p, const uint8_t* q, const float* scales, float* out, hipStream_t s) {
+  const dim3 block(kThreads);
+  const QJob* tiles = p->qjobs;
+  const QJob* flats = tiles + p->n_qtile;
+  const int64_t nz = p->n_qzero;
+  if (p->n_qtile) {
+    const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
+    hipLaunchKernelGGL((dequant_tile_kernel<FMT, HW>), grid_of(p, n), block, 0, s, tiles, p->n_qtile, q, scales, out,
+                       static_cast<unsigned>(n));
+  }
+  if (p->n_qflat)
+    hipLaunchKernelGGL((dequant_flat_kernel<FMT, HW>), grid_of(p, p->n_qflat + nz), dim3(kFlatThreads), 0, s, flats,
+                       p->n_qflat, q, scales, out, static_cast<unsigned>(p->n_qflat + nz));
+  if (!p->n_qtile && !p->n_qflat && nz)
+    hipLaunchKernelGGL(zero_values_kernel, grid_of(p, nz), block, 0, s, flats, out, static_cast<unsigned>(nz));
+}
+
+
+}  // namespace
+
+extern "C" int rs_block_quant(rs_plan* p, const void* src, int32_t src_dt, void* q, int32_t q_dt,
+                              float* scales, void* stream) {
+  const char* who = "rs_block_quant";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  if (src_dt != RS_F32 && src_dt != RS_BF16) return fail(RS_EDTYPE, std::string(who) + ": src must be fp32 or bf16");
+  const int fmt = fmt_of(q_dt);
+  if (fmt < 0) return fail(RS_EDTYPE, std::string(who) + ": code format must be E4M3, I8 or U8");
+  if (!src || !q || (!scales && p->n_qblocks > 0)) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (!aligned16(src) || !aligned16(q)) return fail(RS_EALIGN, std::string(who) + ": src / q not 16-byte aligned");
+  if (p->n_qjobs == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (src_dt == RS_BF16)
+    launch_quant<true>(p, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
+  else
+    launch_quant<false>(p, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
+  return launched(who);
+}
+
+extern "C" int rs_block_dequant(rs_plan* p, const void* q, int32_t q_dt, const float* scales,
+                                float* out, void* stream) {
+  const char* who = "rs_block_dequant";
+  clear_error();
+  int st = check_call(p, who);
+  if (st != RS_OK) return st;
+  const int fmt = fmt_of(q_dt);
+  if (fmt < 0) return fail(RS_EDTYPE, std::string(who) + ": code format must be E4M3, I8 or U8");
+  if (!q || !out || (!scales && p->n_qblocks > 0)) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (!aligned16(q) || !aligned16(out)) return fail(RS_EALIGN, std::string(who) + ": q / out not 16-byte aligned");
+  if (p->n_qjobs == 0) return RS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  if (fmt == FMT_E4M3 && p->e4m3_hw)
+    launch_dequant<FMT_E4M3, true>(p, qb, scales, out, s);
+  else if (fmt == FMT_E4M3)
+    launch_dequant<FMT_E4M3, false>(p, qb, scales, out, s);
+  else if (fmt == FMT_I8)
+    launch_dequant<FMT_I8, false>(p, qb, scales, out, s);
+  else
+    launch_dequant<FMT_U8, false>(p, qb, scales, out, s);
+  return launched(who);
+}
