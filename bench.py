@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
+                    help="0 is the tiny three-tensor group: launch-bound, a parity case more than a bandwidth one")
     ap.add_argument("--mode", default="step", choices=["step", "fp8_gather", "adam8"],
                     help="step: the workload's steps; fp8_gather: block quant of the rank slices, then "
                          "the fused unpack-dequant of the codes into the bf16 tensors; adam8 (workload 4): "
@@ -469,7 +470,9 @@ def main():
     if args.cpu_sample and not w.adam_states and args.mode == "step":
         cpu = cpu_baseline(w, plan)
 
-    names = {1: "Llama-3-8B layer (bf16, 128x128 tiles%s), V=64: unpack + pack(1/V, accumulate) + e4m3 tile quant"
+    names = {0: "tiny group (64x48 1-row blocks, 100x32 16x16 tiles, 7x130 elements; fp32), V=4: unpack + "
+                "pack(1/V, accumulate)",
+             1: "Llama-3-8B layer (bf16, 128x128 tiles%s), V=64: unpack + pack(1/V, accumulate) + e4m3 tile quant"
                 % (" stored tile-major" if args.tile_major else ""),
              2: "Llama-3-70B layer (bf16, whole-matrix blocks), V=1024, 4 ranks materialised: unpack + pack",
              3: "MoE layer (128 experts, bf16, 128x128 tiles), V=256: unpack + pack + e4m3 tile quant",
@@ -501,8 +504,9 @@ def main():
                    "order": order_name, "padding_frac": round(plan.padding / (R * S), 5),
                    "S_over_avg_load": round(S / max(avg_load, 1), 4), "plan_ms": round(plan_ms, 2),
                    "bytes_per_step": int(step_bytes), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "storage": "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales"
-                   if args.workload != 4 else "fp32 m/v, int8/uint8 codes + fp32 scales",
+                   "storage": {0: "fp32 params, grads, prev and packed", 2: "bf16 params, fp32 grads/prev/packed",
+                               4: "fp32 m/v, int8/uint8 codes + fp32 scales"}.get(
+                       args.workload, "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales"),
                    "e4m3_encoder": "sw" if os.environ.get("RS_E4M3_ENCODER") == "sw" else "hw"},
         "kernels": per_kernel,
         "cold_cache": cold,
