@@ -70,7 +70,10 @@ inline int elem_bytes(int32_t dt) {
   }
 }
 
-inline int fmt_of(int32_t q_dt) {
+namespace {
+
+// Code format of an rs_dtype (the device side's Fmt, which is local to each file).
+[[maybe_unused]] int fmt_of(int32_t q_dt) {
   switch (q_dt) {
     case RS_E4M3: return FMT_E4M3;
     case RS_I8: return FMT_I8;
@@ -79,4 +82,5 @@ inline int fmt_of(int32_t q_dt) {
   }
 }
 
+}  // namespace
 }  // namespace rs
