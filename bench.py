@@ -457,6 +457,26 @@ def main():
             sf = scales.float()
             assert bool(torch.isfinite(sf).all()) and bool((sf > 0).all()), "scales"
         check = f"ok ({specs[i].name} unpacks to its weights; padding and codes outside blocks are zero)"
+    elif not args.no_check and args.mode == "step":
+        # Adam-state layer, again without the oracle: the second tensor's m and v pack bit
+        # for bit (sigma = 1, no accumulate), their dequantised values lie within half a
+        # code step of the packed ones (plus the rounding of the fp32 product), and every
+        # position outside the tensors is 0 in the packed, code and dequantised buffers
+        i = 1
+        s0, n1, b = int(starts[i]), specs[i].numel, specs[i].p0
+        first = sum(-(-sp.numel // sp.p0) for sp in specs[:i])
+        nb = -(-n1 // b)
+        for name, src, pk, sc, dq in (("m", m, pm, sm, dm), ("v", v, pv, sv, dv)):
+            x = pk[s0:s0 + n1]
+            assert torch.equal(x.view(torch.int32), src[i].reshape(-1).view(torch.int32)), f"pack_{name}"
+            s = sc[first:first + nb].double().repeat_interleave(b)[:n1]
+            err = (dq[s0:s0 + n1].double() - x.double()).abs()
+            assert bool((err <= 0.5 * s + 2.0 ** -20 * x.double().abs()).all()), f"dequant_{name}"
+        pads = padding_ranges(specs, starts, S, R)
+        for buf in (pm.view(torch.int32), pv.view(torch.int32), dm.view(torch.int32), dv.view(torch.int32), qm, qv):
+            assert all(bool((buf[b0:e0] == 0).all()) for b0, e0 in pads), "outside the tensors"
+        check = (f"ok ({specs[i].name}: m and v pack bit for bit and dequantise within half a code step; "
+                 f"padding, codes and values outside the tensors are zero)")
     if not args.no_check and args.mode == "adam8":
         check = "skipped (the Adam step is checked by tests/test_gpu_adam.py)"
     dom_avg_s = float(np.mean(dom_ms)) * 1e-3   # the dominant kernel inside the timed region
