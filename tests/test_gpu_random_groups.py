@@ -3,7 +3,8 @@ one group, shapes with ragged tiles, flat blocks and tails, rank counts 1-64,
 both parameter dtypes, and sometimes only the ranks that hold data
 materialised. Each group goes through the whole check of the parity suite
 (unpack, pack with and without accumulation and in place, quant and dequant
-in the three code formats, 1-byte unpack, the fused gather side)."""
+in the three code formats, 1-byte unpack, the fused gather side), and two
+chained 8-bit Adam steps run on it."""
 import random
 
 import pytest
@@ -56,3 +57,33 @@ def test_random_group(gpu_lib, seed):
         R_mat = -(-max(s + sp.numel for s, sp in zip(starts, specs)) // S)
     print(f"seed {seed}: V={V} {pdtype} R_mat={R_mat} specs={specs}", flush=True)
     _full_check(rs, specs, V, pdtype, 300 + seed, R_mat=R_mat)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_adam_steps_on_a_random_group(gpu_lib, seed):
+    """Two chained rs_adam8_step calls; params, codes and scales bit for bit after each."""
+    import numpy as np
+    from oracle import adam as OA, transform as OT
+    from tests.gpu_util import tensor_bits
+    from tests.test_gpu_adam import HYPERS, _run
+    import structure_aware_grouped_amd as rs
+    specs, V, _, only_used = random_group(seed)
+    S, starts, _, _ = rs.rs_plan_build(specs, V)
+    R = -(-max(s + sp.numel for s, sp in zip(starts, specs)) // S) if only_used else V
+    print(f"seed {seed}: V={V} R_mat={R} specs={specs}", flush=True)
+    plan = rs.rs_plan_load(specs, V, S, starts, R, 0)
+    rng = np.random.default_rng(600 + seed)
+    total = R * S
+    param = rng.standard_normal(total).astype(np.float32)
+    m = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(total) * 1e-3) ** 2).astype(np.float32)
+    qm, sm = OT.block_quant(m, specs, starts, S, R, "i8")
+    qv, sv = OT.block_quant(v, specs, starts, S, R, "u8")
+    for h in HYPERS[:2]:
+        grad = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+        want = OA.adam8_step(param, grad, qm, sm, qv, sv, specs, starts, h)
+        got = _run(rs, plan, (param, grad, qm, sm, qv.astype(np.uint8), sv), h)
+        for g, wv, name in zip(got, want, ("param", "q_m", "s_m", "q_v", "s_v")):
+            assert np.array_equal(tensor_bits(g), np.asarray(wv).view(tensor_bits(g).dtype)), (name, h.step)
+        param, qm, sm, qv, sv = want
+    plan.close()
