@@ -256,7 +256,10 @@ def main():
     plan_ms = (time.perf_counter() - t0) * 1e3
     R_used = -(-max(s + sp.numel for s, sp in zip(starts, specs)) // S)
     R = w.V if w.materialize_all_ranks else R_used
-    plan = rs.rs_plan_load(specs, w.V, S, starts, R, 0)
+    t0 = time.perf_counter()
+    plan = rs.rs_plan_load(specs, w.V, S, starts, R, 0)   # validate, lower, upload the work lists (once)
+    torch.cuda.synchronize()
+    load_ms = (time.perf_counter() - t0) * 1e3
     inp = Inputs(w, S, starts, R, device=dev)
     nbytes = algorithmic_bytes(w, plan)
     avg_load = -(-sum(plan.numels) // w.V)
@@ -523,6 +526,7 @@ def main():
         "config": {"workload": names[args.workload], "V": w.V, "S": S, "R_mat": R,
                    "order": order_name, "padding_frac": round(plan.padding / (R * S), 5),
                    "S_over_avg_load": round(S / max(avg_load, 1), 4), "plan_ms": round(plan_ms, 2),
+                   "load_ms": round(load_ms, 1),
                    "bytes_per_step": int(step_bytes), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "storage": {0: "fp32 params, grads, prev and packed", 2: "bf16 params, fp32 grads/prev/packed",
                                4: "fp32 m/v, int8/uint8 codes + fp32 scales"}.get(
