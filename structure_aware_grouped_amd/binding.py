@@ -177,6 +177,12 @@ def rs_plan_load(specs, V: int, S: int, starts: Sequence[int], R_mat: Optional[i
 
 # ---------------------------------------------------------------- transforms
 
+def _count_check(plan: Plan, items, what: str):
+    """The C calls read exactly one pointer per tensor of the plan."""
+    if len(items) != len(plan.numels):
+        raise ValueError(f"{what}: {len(items)} entries for a plan of {len(plan.numels)} tensors")
+
+
 def _dev_check(plan: Plan, *tensors):
     for t in tensors:
         if t is None:
@@ -189,6 +195,7 @@ def _dev_check(plan: Plan, *tensors):
 
 def rs_unpack_gathered(plan: Plan, gathered: torch.Tensor, dsts: List[torch.Tensor]):
     """dst_i <- gathered[s_i : s_i + n_i] for every tensor (same dtype)."""
+    _count_check(plan, dsts, "dsts")
     _dev_check(plan, gathered, *dsts)
     if gathered.numel() < plan.R_mat * plan.S:
         raise ValueError("gathered buffer shorter than R_mat * S")
@@ -202,6 +209,7 @@ def rs_unpack_gathered(plan: Plan, gathered: torch.Tensor, dsts: List[torch.Tens
 def rs_pack_scatter(plan: Plan, srcs: List[torch.Tensor], packed: torch.Tensor,
                     prev: Optional[torch.Tensor] = None, scale: Optional[float] = None):
     """packed <- [prev +] src * sigma on tensors, +0.0 on padding; sigma = fl32(1/V) unless given."""
+    _count_check(plan, srcs, "srcs")
     _dev_check(plan, packed, prev, *srcs)
     if packed.dtype != torch.float32 or (prev is not None and prev.dtype != torch.float32):
         raise ValueError("packed and prev are fp32")
@@ -246,6 +254,7 @@ def rs_unpack_dequant(plan: Plan, q: torch.Tensor, fmt: str, scales: torch.Tenso
                       dsts: List[Optional[torch.Tensor]]):
     """dst_i <- fl32(code value * block scale) (rounded to bf16 for bf16 tensors) for every
     quantised tensor; entries for other tensors may be None."""
+    _count_check(plan, dsts, "dsts")
     _dev_check(plan, q, scales, *[d for d in dsts if d is not None])
     if q.numel() * q.element_size() < plan.R_mat * plan.S or scales.numel() < plan.n_qblocks:
         raise ValueError("q / scales too short")

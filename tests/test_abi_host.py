@@ -193,3 +193,18 @@ def test_missing_library_fails_loudly(tmp_path):
             "except RuntimeError as e:\n    print('raised:', e)\nelse:\n    print('loaded')\n")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert "raised:" in out.stdout and "no CPU fallback" in out.stdout, out.stdout + out.stderr
+
+
+def test_binding_rejects_a_pointer_list_of_the_wrong_length(rs):
+    """The C calls read one pointer per tensor: a shorter or longer list never reaches them."""
+    import torch
+    from structure_aware_grouped_amd import binding
+    plan = binding.Plan.__new__(binding.Plan)   # host-only stand-in: nothing is loaded on a device
+    plan._h, plan.numels, plan.device, plan.R_mat, plan.S, plan.n_qblocks = None, [16, 32], 0, 1, 48, 0
+    t = torch.zeros(16)
+    for call in (lambda: binding.rs_unpack_gathered(plan, torch.zeros(48), [t]),
+                 lambda: binding.rs_pack_scatter(plan, [t, t, t], torch.zeros(48)),
+                 lambda: binding.rs_unpack_dequant(plan, torch.zeros(48, dtype=torch.uint8), "e4m3",
+                                                   torch.zeros(1), [None])):
+        with pytest.raises(ValueError, match="entries for a plan of 2 tensors"):
+            call()
