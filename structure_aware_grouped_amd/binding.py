@@ -210,6 +210,8 @@ def rs_pack_scatter(plan: Plan, srcs: List[torch.Tensor], packed: torch.Tensor,
                     prev: Optional[torch.Tensor] = None, scale: Optional[float] = None):
     """packed <- [prev +] src * sigma on tensors, +0.0 on padding; sigma = fl32(1/V) unless given."""
     _count_check(plan, srcs, "srcs")
+    if srcs[0].dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("sources are fp32 or bf16")
     _dev_check(plan, packed, prev, *srcs)
     if packed.dtype != torch.float32 or (prev is not None and prev.dtype != torch.float32):
         raise ValueError("packed and prev are fp32")

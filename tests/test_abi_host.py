@@ -208,3 +208,12 @@ def test_binding_rejects_a_pointer_list_of_the_wrong_length(rs):
                                                    torch.zeros(1), [None])):
         with pytest.raises(ValueError, match="entries for a plan of 2 tensors"):
             call()
+
+
+def test_binding_rejects_gradients_of_another_dtype(rs):
+    import torch
+    from structure_aware_grouped_amd import binding
+    plan = binding.Plan.__new__(binding.Plan)
+    plan._h, plan.numels, plan.device, plan.R_mat, plan.S, plan.n_qblocks = None, [16], 0, 1, 16, 0
+    with pytest.raises(ValueError, match="fp32 or bf16"):
+        binding.rs_pack_scatter(plan, [torch.zeros(16, dtype=torch.float16)], torch.zeros(16))
