@@ -36,6 +36,15 @@
  *     new table on `stream` only when they change. A plan is therefore not
  *     safe to use from two threads, or from two streams with different
  *     tensor pointers, at the same time.
+ *   - HIP graphs: the transform calls may be captured (hipStreamBeginCapture
+ *     on `stream`) once a call with the same tensor pointers has run outside
+ *     the capture and is ordered before the replays. The graph then holds
+ *     kernel launches only; they read the plan's pointer table when they run.
+ *     A call whose pointers differ from the plan's last call returns
+ *     RS_EINVAL while its stream is capturing, and launches nothing. Calls
+ *     with other pointers between replays change the tables the replays
+ *     read: keep them fixed while such a graph is in use, or use a second
+ *     plan for other tensors.
  *   - Floating-point inputs must be finite; NaN or Inf inside a quantisation
  *     block gives unspecified codes (padding is never read, so it may hold
  *     anything).

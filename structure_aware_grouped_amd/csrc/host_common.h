@@ -44,9 +44,19 @@ inline int launched(const char* who) {
 }
 
 // Upload a per-tensor pointer table on `stream` if it differs from the last one.
+// Kernels read the table in device memory when they run, so a graph captured
+// from these calls uses the table as it is at replay. A new table is therefore
+// refused while `stream` is being captured: the caller makes one call with the
+// same pointers before the capture, and the capture then holds kernels only.
 inline int sync_table(rs_plan* p, PtrTable* tab, const void* const* ptrs, hipStream_t stream, const char* who) {
   const size_t bytes = sizeof(void*) * static_cast<size_t>(p->n);
   if (tab->valid && std::memcmp(tab->seen.data(), ptrs, bytes) == 0) return RS_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess)
+    return fail(RS_EHIP, std::string(who) + ": hipStreamIsCapturing failed");
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(RS_EINVAL, std::string(who) + ": tensor pointers differ from the plan's last call while the "
+                               "stream is being captured; make one call with these pointers before the capture");
   if (tab->pending && hipEventSynchronize(tab->done) != hipSuccess)
     return fail(RS_EHIP, std::string(who) + ": waiting for the previous table upload failed");
   std::memcpy(tab->stage, ptrs, bytes);
