@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--no-check", action="store_true", help="skip the sampled output checks")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="launches per kernel of the cold-cache pass after the timed region (0: skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph after the warm-up and replay it in the timed region "
+                         "(the per-kernel and cold passes stay eager)")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (system-scope fence at every record)")
     ap.add_argument("--copy-mib", type=int, default=1024,
@@ -371,12 +374,27 @@ def main():
     # (torch's current stream, which the binding passes), bracket the dominant kernel
     # only: every event record adds idle GPU time at a kernel boundary, so the other
     # kernels are timed in the pass that follows.
+    # With --graph the whole step is one captured HIP graph (the warm-up has made the
+    # calls with these pointers, so the capture holds kernel launches only) and the
+    # events bracket each replay.
     stream = torch.cuda.current_stream(dev).cuda_stream
     timer = HipTimer(torch, fenced=args.fenced_events)
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _, fn in steps:
+                fn()
+        graph.replay()
     dom_ev = [(timer.event(), timer.event()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if graph is not None:
+            timer.record(dom_ev[k][0], stream)
+            graph.replay()
+            timer.record(dom_ev[k][1], stream)
+            continue
         for name, fn in steps:
             if name == dominant:
                 timer.record(dom_ev[k][0], stream)
@@ -387,6 +405,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dom_ms = [timer.ms(a, b) for a, b in dom_ev]
+    del graph
 
     # ---- per-kernel pass, right after the timed region and under the same warm
     # conditions: HIP events around every launch
@@ -405,7 +424,12 @@ def main():
                             "min_ms": round(float(np.min(ms)), 5),
                             "GBps": round(nbytes[name] / (avg * 1e-3) / 1e9, 1),
                             "bytes": int(nbytes[name])}
-    per_kernel[dominant]["timed_region_avg_ms"] = round(float(np.mean(dom_ms)), 5)
+    graph_info = None
+    if args.graph:   # events around each replay: the whole step
+        graph_info = {"replay_avg_ms": round(float(np.mean(dom_ms)), 5),
+                      "replay_min_ms": round(float(np.min(dom_ms)), 5)}
+    else:
+        per_kernel[dominant]["timed_region_avg_ms"] = round(float(np.mean(dom_ms)), 5)
     step_bytes = sum(nbytes[name] for name, _ in steps)
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / (wall / args.steps) / 1e9
@@ -482,7 +506,9 @@ def main():
                  f"padding, codes and values outside the tensors are zero)")
     if not args.no_check and args.mode == "adam8":
         check = "skipped (the Adam step is checked by tests/test_gpu_adam.py)"
-    dom_avg_s = float(np.mean(dom_ms)) * 1e-3   # the dominant kernel inside the timed region
+    # the dominant kernel inside the timed region (inside a graph replay it has no events
+    # of its own: then its eager per-kernel average)
+    dom_avg_s = (per_kernel[dominant]["avg_ms"] if args.graph else float(np.mean(dom_ms))) * 1e-3
     achieved = nbytes[dominant] / dom_avg_s / 1e9
     traffic = read_traffic((args.workload, args.mode, bool(args.tile_major)), dominant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -531,8 +557,10 @@ def main():
                    "storage": {0: "fp32 params, grads, prev and packed", 2: "bf16 params, fp32 grads/prev/packed",
                                4: "fp32 m/v, int8/uint8 codes + fp32 scales"}.get(
                        args.workload, "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales"),
-                   "e4m3_encoder": "sw" if os.environ.get("RS_E4M3_ENCODER") == "sw" else "hw"},
+                   "e4m3_encoder": "sw" if os.environ.get("RS_E4M3_ENCODER") == "sw" else "hw",
+                   "launch": "one HIP graph replay per step" if args.graph else "eager"},
         "kernels": per_kernel,
+        "graph": graph_info,
         "cold_cache": cold,
         "copy_ceiling": copy,
         "check": check,
