@@ -217,3 +217,46 @@ def test_binding_rejects_gradients_of_another_dtype(rs):
     plan._h, plan.numels, plan.device, plan.R_mat, plan.S, plan.n_qblocks = None, [16], 0, 1, 16, 0
     with pytest.raises(ValueError, match="fp32 or bf16"):
         binding.rs_pack_scatter(plan, [torch.zeros(16, dtype=torch.float16)], torch.zeros(16))
+
+
+def _llama70b_model(layers):
+    specs = []
+    for l in range(layers):
+        for name, r, c in (("wq", 8192, 8192), ("wk", 1024, 8192), ("wv", 1024, 8192), ("wo", 8192, 8192),
+                           ("gate", 28672, 8192), ("up", 28672, 8192), ("down", 8192, 28672)):
+            specs.append(TensorSpec(f"{l}.{name}", r, c, "TILE", 128, 128))
+        specs += [TensorSpec(f"{l}.n1", 8192, 1, "ROWS", 1), TensorSpec(f"{l}.n2", 8192, 1, "ROWS", 1)]
+    return specs
+
+
+def _moe_experts(layers, experts):
+    """Per-expert tensors of DeepSeek-V3-sized MoE layers (7168 hidden, 2048 expert width)."""
+    specs = []
+    for l in range(layers):
+        for e in range(experts):
+            specs += [TensorSpec(f"{l}.{e}.gate", 2048, 7168, "TILE", 128, 128),
+                      TensorSpec(f"{l}.{e}.up", 2048, 7168, "TILE", 128, 128),
+                      TensorSpec(f"{l}.{e}.down", 7168, 2048, "TILE", 128, 128)]
+    return specs
+
+
+@pytest.mark.slow
+def test_host_planner_matches_oracle_on_a_thousand_expert_tensors(rs):
+    specs, V = _moe_experts(4, 256), 1024          # 3072 tensors, 45B parameters
+    S, starts, _, name = rs.rs_plan_build(specs, V)
+    ref = OP.plan(specs, V)
+    assert (S, starts, name) == (ref.S, [int(s) for s in ref.starts], ref.order_name)
+
+
+@pytest.mark.parametrize("case", ["llama70b_80_layers", "moe_58_layers_256_experts"])
+def test_host_planner_on_whole_models(rs, case):
+    """Whole-model groups plan within the pages' 0.3 s, validly, within twice the lower bound."""
+    specs, V = (_llama70b_model(80), 1024) if case.startswith("llama") else (_moe_experts(58, 256), 4096)
+    t0 = time.perf_counter()
+    S, starts, _, _ = rs.rs_plan_build(specs, V)
+    dt = time.perf_counter() - t0
+    assert dt < 0.3, dt
+    assert OP.check_plan(specs, V, S, starts, 16) == []
+    n = sum(sp.numel for sp in specs)
+    lb = -(-max(-(-n // V), max(min(OP.granularity(sp), sp.numel) for sp in specs)) // 16) * 16
+    assert lb <= S <= 2 * lb
