@@ -194,11 +194,18 @@ class HipTimer:
         self.events = []
 
 
-def cpu_baseline(w, plan, names=None) -> dict:
+def log(msg: str):
+    """A progress line on stderr (the JSON result line goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, plan, names=None, max_seconds: float = 15.0) -> dict:
     """The CPU oracle (single-threaded NumPy) on a bounded sample of the workload:
     the tensors named in `names` (default: every tensor, i.e. one whole step),
-    one at a time, with the bench's byte accounting. Inputs are generated before
-    the clock starts."""
+    one at a time and in order, until `max_seconds` of oracle time have passed
+    (the Llama-3-8B and Llama-3-70B layers finish whole; the MoE layer stops
+    after its first experts), with the bench's byte accounting. Inputs are
+    generated before the clock starts."""
     from oracle import transform as OT
     from tests.gpu_util import Inputs
     import workloads as W
@@ -208,8 +215,11 @@ def cpu_baseline(w, plan, names=None) -> dict:
     inp = Inputs(w, plan.S, plan.starts, plan.R_mat, device="cpu")
     pb = 2 if w.param_dtype == "bf16" else 4
     sigma = OT.inv_v(w.V)
-    moved, dt = 0, 0.0
+    moved, dt, done = 0, 0.0, []
     for i in idx:
+        if dt >= max_seconds:
+            break
+        done.append(i)
         spec, s = w.specs[i], plan.starts[i]
         wb, g, p = inp.weight_bits(i), inp.grad(i), inp.prev_range(s, s + spec.numel)
         t0 = time.perf_counter()
@@ -227,7 +237,12 @@ def cpu_baseline(w, plan, names=None) -> dict:
                 OT.quantize_block(x[pos], w.quant)
             moved += n * pb + n + 4 * OT.count_quant_blocks([spec])
         dt += time.perf_counter() - t0
-    what = "every tensor of the layer (one whole step)" if len(idx) == len(w.specs) else ", ".join(names)
+    if len(done) == len(w.specs):
+        what = "every tensor of the layer (one whole step)"
+    elif len(done) <= 4:
+        what = ", ".join(w.specs[i].name for i in done)
+    else:
+        what = f"the first {len(done)} of the layer's {len(w.specs)} tensors"
     return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{what}: unpack + pack{' + e4m3 tile quant' if w.quant else ''}, "
                       f"{moved / 1e9:.3f} GB in {dt:.1f} s"}
@@ -263,6 +278,7 @@ def main():
     plan = rs.rs_plan_load(specs, w.V, S, starts, R, 0)   # validate, lower, upload the work lists (once)
     torch.cuda.synchronize()
     load_ms = (time.perf_counter() - t0) * 1e3
+    log(f"plan: S={S}, R_mat={R}, lowered in {load_ms:.0f} ms")
     inp = Inputs(w, S, starts, R, device=dev)
     nbytes = algorithmic_bytes(w, plan)
     avg_load = -(-sum(plan.numels) // w.V)
@@ -345,6 +361,7 @@ def main():
             steps.append(("quant", lambda: rs.rs_block_quant(plan, G, q, w.quant, scales)))
         dominant = "pack"
     torch.cuda.synchronize()
+    log("inputs resident in HBM")
 
     copy = None
     if args.copy_mib:
@@ -404,6 +421,7 @@ def main():
                 fn()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    log(f"timed region: {args.steps} steps in {wall * 1e3:.1f} ms")
     dom_ms = [timer.ms(a, b) for a, b in dom_ev]
     del graph
 
@@ -515,9 +533,11 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant])}
 
+    log(f"check: {check}")
     cpu = None
     if args.cpu_sample and not w.adam_states and args.mode == "step":
         cpu = cpu_baseline(w, plan)
+        log(f"CPU oracle: {cpu['sample']}")
 
     names = {0: "tiny group (64x48 1-row blocks, 100x32 16x16 tiles, 7x130 elements; fp32), V=4: unpack + "
                 "pack(1/V, accumulate)",
