@@ -88,6 +88,7 @@ struct Tables {
   int64_t n_qblocks = 0;
   int64_t padding = 0;
   int32_t max_tile_vec16 = 0;
+  bool split_code_lines = false;
 };
 
 void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
@@ -174,6 +175,9 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   for (int64_t ti = 0; ti < n; ++ti) {
     const Tensor& x = t[ti];
     if (x.kind == RS_TILE) {
+      // a code row of one tile then starts or ends inside a 128-byte line that
+      // the tile next to it also writes
+      if (x.cols > x.p1 && ((x.start | x.cols | x.p1) & 127) != 0) tb->split_code_lines = true;
       for (int64_t r0 = 0; r0 < x.rows; r0 += x.p0) {
         for (int64_t c0 = 0; c0 < x.cols; c0 += x.p1) {
           QJob j{};
@@ -437,6 +441,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->n_gtile = tb.n_gtile;
     p->n_gflat = tb.n_gflat;
     p->max_tile_vec16 = tb.max_tile_vec16;
+    p->split_code_lines = tb.split_code_lines;
     // gfx950's FP8 conversion (OCP E4M3, round to nearest even) by default;
     // RS_E4M3_ENCODER=sw selects the integer encoder, which gives the same codes.
     const char* enc = std::getenv("RS_E4M3_ENCODER");

@@ -135,13 +135,13 @@ __device__ void zero_f32(float* o, int64_t base, int64_t len, int tid) {
 // so the whole call is one launch.
 // kQuantThreads threads per tile; the register path holds a whole tile of up
 // to 16384 elements (2048 16-byte vectors of bf16, 4096 of fp32).
-template <bool BF16, int FMT, bool HW>
+template <bool BF16, int FMT, bool HW, unsigned XG>
 __device__ __forceinline__ void quant_tile_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
                                                                    const void* __restrict__ src,
                                                                    uint8_t* __restrict__ q,
                                                                    float* __restrict__ scales) {
   __shared__ uint32_t red[kQuantThreads / kWave];
-  const unsigned b = piece_index<kTileXcdGroup>(jb, n_jobs);
+  const unsigned b = piece_index<XG>(jb, n_jobs);
   const QJob j = jobs[b];
   if (static_cast<int64_t>(b) >= n_main) {
     zero_bytes<kQuantThreads>(q, j.base, j.stride, threadIdx.x);
@@ -151,13 +151,13 @@ __device__ __forceinline__ void quant_tile_kernel_job(unsigned jb, unsigned n_jo
       src, q, scales, j.base, j.stride, j.rows, j.cols, j.scale, threadIdx.x, red);
 }
 
-template <bool BF16, int FMT, bool HW>
+template <bool BF16, int FMT, bool HW, unsigned XG>
 __global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* __restrict__ jobs, int64_t n_main,
                                                                    const void* __restrict__ src,
                                                                    uint8_t* __restrict__ q,
                                                                    float* __restrict__ scales, unsigned n_jobs) {
   for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
-    quant_tile_kernel_job<BF16, FMT, HW>(jb, n_jobs, jobs, n_main, src, q, scales);
+    quant_tile_kernel_job<BF16, FMT, HW, XG>(jb, n_jobs, jobs, n_main, src, q, scales);
     __syncthreads();   // the next job reuses this workgroup's LDS
   }
 }
@@ -318,8 +318,12 @@ void launch_quant_kinds(const rs_plan* p, const void* src, uint8_t* q, float* sc
   const int64_t nz = p->n_qzero;
   if (p->n_qtile) {
     const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
-    hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW>), grid_of(p, n), dim3(kQuantThreads), 0, s, tiles,
-                       p->n_qtile, src, q, scales, static_cast<unsigned>(n));
+    if (p->split_code_lines)
+      hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW, kTileXcdGroupSplit>), grid_of(p, n), dim3(kQuantThreads), 0,
+                         s, tiles, p->n_qtile, src, q, scales, static_cast<unsigned>(n));
+    else
+      hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW, kTileXcdGroup>), grid_of(p, n), dim3(kQuantThreads), 0, s,
+                         tiles, p->n_qtile, src, q, scales, static_cast<unsigned>(n));
   }
   if (p->n_qflat)
     hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), grid_of(p, p->n_qflat + nz), dim3(kFlatThreads), 0, s, flats,

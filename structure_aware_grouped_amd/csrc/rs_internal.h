@@ -72,8 +72,7 @@ constexpr unsigned kUnpackXcdGroup = RS_UNPACK_XCD_GROUP;
 constexpr unsigned kPackXcdGroup = RS_PACK_XCD_GROUP;
 constexpr unsigned kGatherXcdGroup = RS_GATHER_XCD_GROUP;
 // the same for the per-block kernels (quant, dequant, Adam): consecutive tiles
-// per XCD (4: tile quant 5.98 -> 6.32 TB/s on the 8B layer; the MoE layer's
-// 2880-wide tensors would gain more from 32, 5.50 -> 5.74), consecutive
+// per XCD (4: tile quant 5.98 -> 6.32 TB/s on the 8B layer), consecutive
 // flat-block groups per XCD (1: grouping slowed the Adam-state kernels)
 #ifndef RS_TILE_XCD_GROUP
 #define RS_TILE_XCD_GROUP 4
@@ -81,7 +80,19 @@ constexpr unsigned kGatherXcdGroup = RS_GATHER_XCD_GROUP;
 #ifndef RS_FLAT_XCD_GROUP
 #define RS_FLAT_XCD_GROUP 1
 #endif
+// Tile quant of a plan whose code rows share 128-byte lines between
+// neighbouring tiles (a TILE tensor whose start, width or tile width is not a
+// multiple of 128 codes, such as the MoE layer's 2880-wide tensors). Such
+// tensors quantise slower: 128x128 tiles of bf16 ran at 5.6 TB/s on
+// 2880-wide tensors, 6.1 on 2944-wide and 6.3 on 4096-wide. Longer runs of
+// consecutive tiles per XCD recover part of it, on measurement rather than a
+// model (the write counter did not fall): on the MoE layer 5.50 TB/s at 4,
+// 5.65 at 32, 5.75 at 64 and 128, 5.70 at 256.
+#ifndef RS_TILE_XCD_GROUP_SPLIT
+#define RS_TILE_XCD_GROUP_SPLIT 64
+#endif
 constexpr unsigned kTileXcdGroup = RS_TILE_XCD_GROUP;
+constexpr unsigned kTileXcdGroupSplit = RS_TILE_XCD_GROUP_SPLIT;
 constexpr unsigned kFlatXcdGroup = RS_FLAT_XCD_GROUP;
 // Threads per tile in the tile quant kernel.
 #ifndef RS_QUANT_THREADS
@@ -276,6 +287,7 @@ struct rs_plan {
   int64_t n_qtile = 0, n_qflat = 0, n_qzero = 0;
   int64_t n_qblocks = 0;
   int32_t max_tile_vec16 = 0;  // largest tile, in 16-byte vectors of 4-byte input
+  bool split_code_lines = false;  // neighbouring tiles share 128-byte lines of codes
 
   rs::TmJob* tmjobs = nullptr;         // unpack / pack of TILEMAJOR tensors
   int64_t n_tm = 0;
