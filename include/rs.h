@@ -33,9 +33,12 @@
  *     the status is returned and rs_last_error() says why. No C++ exception
  *     crosses this boundary.
  *   - A plan caches the per-tensor pointer tables it last saw and uploads a
- *     new table on `stream` only when they change. A plan is therefore not
- *     safe to use from two threads, or from two streams with different
- *     tensor pointers, at the same time.
+ *     new table on `stream` only when they change; kernels read the table
+ *     when they run. The upload is ordered with the work on `stream` only.
+ *     A plan is therefore not safe to use from two threads at once; and when
+ *     its calls go to more than one stream, a call with new tensor pointers
+ *     must be ordered after every earlier call on the other streams, and the
+ *     later calls on other streams after it (an event or a synchronisation).
  *   - HIP graphs: the transform calls may be captured (hipStreamBeginCapture
  *     on `stream`) once a call with the same tensor pointers has run outside
  *     the capture and is ordered before the replays. The graph then holds
