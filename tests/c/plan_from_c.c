@@ -29,11 +29,11 @@ int main(void) {
   const int st = rs_plan_build(specs, n, V, 16, RS_ORDER_BEST, &S, starts, order, &kind);
   if (st != RS_OK) {
     printf("error %d %s\n", st, rs_last_error());
-    return 0;
+  } else {
+    printf("%lld\n", (long long)S);
+    for (long long i = 0; i < n; ++i) printf("%lld%c", (long long)starts[i], i + 1 < n ? ' ' : '\n');
+    printf("%d\n", kind);
   }
-  printf("%lld\n", (long long)S);
-  for (long long i = 0; i < n; ++i) printf("%lld%c", (long long)starts[i], i + 1 < n ? ' ' : '\n');
-  printf("%d\n", kind);
   free(specs);
   free(starts);
   free(order);
