@@ -5,6 +5,9 @@ include/rs.h); ``binding`` exposes its calls under the same names.
 """
 from .binding import (  # noqa: F401
     Plan,
+    PlanSpec,
+    plan_from_json,
+    plan_to_json,
     rs_adam8_step,
     RsError,
     load,

@@ -9,8 +9,9 @@ If the library is missing, load() raises: there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import json
 import os
-from typing import List, Optional, Sequence
+from typing import List, NamedTuple, Optional, Sequence
 
 import torch
 
@@ -133,6 +134,57 @@ def rs_plan_build(specs, V: int, align: int = 16, policy: str = "best"):
     return S.value, list(starts), list(order), ORDER_KINDS[kind.value]
 
 
+# ---------------------------------------------------------------- plans as data
+
+PLAN_FORMAT = "rs-plan/1"
+
+
+class PlanSpec(NamedTuple):
+    """One tensor of a plan read back from JSON (the fields rs_plan_load reads)."""
+    name: str
+    rows: int
+    cols: int
+    kind: str
+    p0: int = 0
+    p1: int = 0
+
+    @property
+    def numel(self) -> int:
+        return self.rows * self.cols
+
+
+def plan_to_json(specs, V: int, S: int, starts: Sequence[int], R_mat: Optional[int] = None) -> str:
+    """A plan as JSON. A plan is pure data: the tensors (shape and atomic block),
+    V, S, the starts and the materialised ranks. rs_plan_load validates it again
+    and rebuilds the same device work lists from it, so a saved plan resumes a
+    group without planning again."""
+    kinds = {v: k for k, v in KINDS.items()}
+    out = []
+    for i, sp in enumerate(specs):
+        kind = sp.kind if isinstance(sp.kind, str) else kinds[int(sp.kind)]
+        out.append({"name": str(getattr(sp, "name", f"t{i}")), "rows": int(sp.rows), "cols": int(sp.cols),
+                    "kind": kind, "p0": int(getattr(sp, "p0", 0)), "p1": int(getattr(sp, "p1", 0))})
+    return json.dumps({"format": PLAN_FORMAT, "V": int(V), "S": int(S), "R_mat": int(V if R_mat is None else R_mat),
+                       "starts": [int(x) for x in starts], "tensors": out})
+
+
+def plan_from_json(text: str):
+    """(specs, V, S, starts, R_mat) from plan_to_json's output; checks the format
+    and the field types only (validation is rs_plan_load's)."""
+    d = json.loads(text)
+    if d.get("format") != PLAN_FORMAT:
+        raise ValueError(f"not an {PLAN_FORMAT} plan: format {d.get('format')!r}")
+    specs = []
+    for t in d["tensors"]:
+        if t["kind"] not in KINDS:
+            raise ValueError(f"unknown block kind {t['kind']!r}")
+        specs.append(PlanSpec(str(t["name"]), int(t["rows"]), int(t["cols"]), t["kind"], int(t["p0"]), int(t["p1"])))
+    starts = [int(x) for x in d["starts"]]
+    if len(starts) != len(specs):
+        raise ValueError(f"{len(starts)} starts for {len(specs)} tensors")
+    return specs, int(d["V"]), int(d["S"]), starts, int(d["R_mat"])
+
+
 class Plan:
     """A loaded plan (device work lists); freed with close() or when collected."""
 
@@ -144,6 +196,9 @@ class Plan:
         _check(load().rs_plan_info(handle, ctypes.byref(r), ctypes.byref(q), ctypes.byref(pad)))
         self.R_used, self.n_qblocks, self.padding = r.value, q.value, pad.value
         self.numels = [int(s.rows) * int(s.cols) for s in specs]
+
+    def to_json(self) -> str:
+        return plan_to_json(self.specs, self.V, self.S, self.starts, self.R_mat)
 
     @property
     def handle(self):

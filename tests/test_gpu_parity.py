@@ -444,3 +444,32 @@ def test_bad_arguments_launch_nothing(gpu_lib):
     torch.cuda.synchronize()
     assert bool((dst[0] == 7.0).all()) and bool((q == 3).all())
     plan.close()
+
+
+def test_plan_reloaded_from_json(gpu_lib):
+    """A plan saved as JSON and loaded again drives the kernels exactly like the original."""
+    import structure_aware_grouped_amd as rs
+    rng = _rng(2024)
+    V = 6
+    a = _plan(rs, RAGGED, V)
+    specs, V2, S, starts, R = rs.plan_from_json(a.to_json())
+    b = rs.rs_plan_load(specs, V2, S, starts, R, 0)
+    assert (b.S, b.starts, b.R_mat, b.n_qblocks, b.padding) == (a.S, a.starts, a.R_mat, a.n_qblocks, a.padding)
+    G, _, _ = _flat_input(rng, a, torch.bfloat16)
+    grads = [torch.from_numpy(_values(rng, sp.rows * sp.cols, scale=1e-3)).to(DEV).view(sp.rows, sp.cols)
+             for sp in RAGGED]
+    prev = torch.from_numpy(_values(rng, a.R_mat * a.S, scale=1e-3)).to(DEV)
+    res = []
+    for plan in (a, b):
+        outs = [garbage(sp.rows * sp.cols, torch.bfloat16, DEV).view(sp.rows, sp.cols) for sp in RAGGED]
+        rs.rs_unpack_gathered(plan, G, outs)
+        packed = garbage(plan.R_mat * plan.S, torch.float32, DEV)
+        rs.rs_pack_scatter(plan, grads, packed, prev=prev)
+        q = garbage(plan.R_mat * plan.S, torch.uint8, DEV)
+        scales = garbage(plan.n_qblocks, torch.float32, DEV)
+        rs.rs_block_quant(plan, G, q, "e4m3", scales)
+        torch.cuda.synchronize()
+        res.append([tensor_bits(t) for t in (*outs, packed, q, scales)])
+    assert all(np.array_equal(x, y) for x, y in zip(*res))
+    a.close()
+    b.close()
