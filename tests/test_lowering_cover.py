@@ -1,0 +1,97 @@
+"""The work lists rs_plan_load uploads, checked on the host element by element
+(tests/cpp/lowering_cover.cpp, which includes plan.cpp): unpack writes every
+tensor element once from its own flat position; pack writes every flat
+position once, from its own tensor element or as padding; quant writes every
+code once (blocks whole, zero ranges outside them) and every scale once; the
+gather side writes every element of every quantised tensor once with its own
+block's scale; tile-major strips map tile-by-tile positions to row-major
+elements. Planted mistakes in the lists are reported."""
+import os
+import random
+import shutil
+import subprocess
+
+import pytest
+
+from oracle import plan as OP
+from workloads import TensorSpec, tile_major_variant, workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "structure_aware_grouped_amd", "csrc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+KINDS = {"ELEM": 0, "ROWS": 1, "TILE": 2, "FLAT": 3, "WHOLE": 4, "TILEMAJOR": 5}
+
+
+@pytest.fixture(scope="module")
+def exe(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if not gxx or not os.path.exists(os.path.join(ROCM, "include", "hip", "hip_runtime_api.h")):
+        pytest.skip("needs g++ and the HIP headers")
+    out = str(tmp_path_factory.mktemp("cover") / "lowering_cover")
+    cmd = [gxx, "-std=c++17", "-O2", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(ROOT, "tests", "cpp", "lowering_cover.cpp"),
+           os.path.join(CSRC, "planner.cpp"), "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}", "-pthread", "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return out
+
+
+def _run(exe, specs, V, R=None, plant=0):
+    ref = OP.plan(specs, V)
+    R = V if R is None else R
+    lines = [f"{len(specs)} {V} {ref.S} {R}"] + [f"{s.rows} {s.cols} {KINDS[s.kind]} {s.p0} {s.p1} {int(st)}"
+                                                 for s, st in zip(specs, ref.starts)]
+    args = [exe] + ([str(plant)] if plant else [])
+    r = subprocess.run(args, input="\n".join(lines) + "\n", capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr
+    return r.stdout.strip()
+
+
+@pytest.mark.parametrize("idx,tm", [(0, False), (1, False), (1, True), (2, False), (4, False)])
+def test_workload_lists(exe, idx, tm):
+    w = workload(idx)
+    if tm:
+        w = tile_major_variant(w)
+    R = None if w.materialize_all_ranks else OP.plan(w.specs, w.V).R_used
+    assert _run(exe, list(w.specs), w.V, R) == "ok"
+
+
+def _random_group(rng):
+    specs = []
+    for i in range(rng.randint(1, 7)):
+        kind = rng.choice(["ROWS", "TILE", "TILE", "FLAT", "WHOLE", "ELEM", "TILEMAJOR"])
+        if kind == "TILEMAJOR":
+            br, bc = rng.choice([(16, 16), (2, 8192), (4, 64), (16, 3), (32, 32)])
+            specs.append(TensorSpec(f"t{i}", br * rng.randint(1, 3), bc * rng.randint(1, 3), kind, br, bc))
+            continue
+        r, c = rng.randint(1, 600), rng.choice([1, 3, 16, 130, 256, 1000])
+        p0 = rng.choice([1, 3, 16, 128]) if kind in ("ROWS", "TILE") else (rng.choice([1, 7, 64, 2048, 5000])
+                                                                         if kind == "FLAT" else 0)
+        p1 = rng.choice([1, 5, 16, 64, 128]) if kind == "TILE" else 0
+        specs.append(TensorSpec(f"t{i}", r, c, kind, p0, p1))
+    return specs
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_group_lists(exe, seed):
+    rng = random.Random(9000 + seed)
+    specs = _random_group(rng)
+    V = rng.choice([1, 2, 3, 5, 8, 16, 64])
+    R = OP.plan(specs, V).R_used if seed % 3 == 0 else None
+    assert _run(exe, specs, V, R) == "ok"
+
+
+def test_gather_runs_and_strips_of_a_mid_size_group(exe):
+    specs = [TensorSpec("a", 1024, 2048, "TILE", 128, 128), TensorSpec("b", 300, 1000, "TILE", 64, 64),
+             TensorSpec("c", 300001, 1, "FLAT", 2048), TensorSpec("d", 256, 512, "TILEMAJOR", 32, 32),
+             TensorSpec("e", 64, 4096, "ROWS", 1), TensorSpec("f", 5000, 1, "ELEM")]
+    assert _run(exe, specs, 7) == "ok"
+
+
+@pytest.mark.parametrize("plant", [1, 2, 3, 4])
+def test_planted_mistakes_are_reported(exe, plant):
+    specs = [TensorSpec("a", 256, 512, "TILE", 128, 128), TensorSpec("c", 5000, 1, "FLAT", 2048),
+             TensorSpec("d", 64, 64, "TILEMAJOR", 32, 32), TensorSpec("e", 100, 30, "ELEM")]
+    out = _run(exe, specs, 4, plant=plant)
+    assert out.startswith("FAIL"), out
