@@ -40,7 +40,9 @@ METRIC = "DBuffer pack/unpack+blockquant GB/s, % HBM peak (Llama-3-8B layer, V=6
 PROFILE_TRAFFIC = {(1, "step", False): "llama3_8b_v64", (1, "step", True): "llama3_8b_v64_tile_major",
                    (1, "fp8_gather", False): "llama3_8b_v64_fp8_gather", (4, "adam8", False): "adam8_llama3_8b_v64",
                    (2, "step", False): "llama3_70b_v1024", (3, "step", False): "moe128_v256",
-                   (4, "step", False): "adam_states_llama3_8b_v64"}
+                   (4, "step", False): "adam_states_llama3_8b_v64",
+                   (3, "fp8_gather", False): "moe128_v256_fp8_gather",
+                   (1, "fp8_gather", True): "llama3_8b_v64_tile_major_fp8_gather"}
 KERNEL_SOURCES = [os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", f)
                   for f in ("device_common.h", "host_common.h", "transform.hip", "quant.hip", "gather.hip",
                             "adam.hip", "rs_internal.h", "plan.cpp")]
