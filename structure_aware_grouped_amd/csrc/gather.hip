@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_tm_kernel(const TmJob* 
                                                                   const float* __restrict__ scales,
                                                                   void* const* __restrict__ dst, int split, unsigned n_pieces) {
   for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
-    gather_tm_kernel_piece<FMT, HW, BF16OUT>(p, jobs, q, scales, dst, split);
+    gather_tm_kernel_piece<FMT, HW, BF16OUT>(piece_index<kGatherXcdGroup>(p, n_pieces), jobs, q, scales, dst, split);
 }
 
 }  // namespace

@@ -58,7 +58,9 @@ constexpr int64_t kPackSplit = (kPackChunk / 4 + kPackPiece - 1) / kPackPiece;
 // Pack, with three streams, gains from runs of 256 pieces (512 KiB of output)
 // per XCD: 6.52 -> 6.67 TB/s on the Llama-3-8B layer, 5.97 -> 6.59 TB/s on the
 // 55 GB MoE layer. Unpack is fastest with plain round-robin; the row-run
-// gather of the MoE layer gains 7% from runs of 128.
+// gather of the MoE layer gains 7% from runs of 128, and the tile-major gather
+// of the 8B layer 6% (5.72 -> 6.09 TB/s; each strip's two pieces then read its
+// job and scales from one L2).
 #ifndef RS_UNPACK_XCD_GROUP
 #define RS_UNPACK_XCD_GROUP 1
 #endif
