@@ -309,7 +309,7 @@ void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipS
   const QJob* tiles = p->gjobs;
   const QJob* flats = tiles + p->n_gtile;
   if (p->n_gchunks) {
-    const int64_t split = gather_split(BF16OUT ? 8 : 4);
+    const int64_t split = BF16OUT ? p->gather_split8 : p->gather_split4;
     const int64_t n = p->n_gchunks * split;
     hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT>), grid_of(p, n), dim3(kGatherThreads), 0, s, p->gchunks, q,
                        scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));

@@ -89,7 +89,52 @@ struct Tables {
   int64_t padding = 0;
   int32_t max_tile_vec16 = 0;
   bool split_code_lines = false;
+  int64_t gather_split8 = 0, gather_split4 = 0;
 };
+
+// Gather runs of one tensor: `unit` codes per row (TILE) or per flat block
+// (FLAT), grouped into bands of `band` units (`n_full` full bands and one of
+// `last` units if last > 0) that no run crosses.
+struct RunGroups {
+  int64_t unit, band, n_full, last;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Units per run for a target of P pieces of pc codes.
+int64_t run_units(const RunGroups& g, int64_t P, int64_t pc) {
+  return std::max<int64_t>(1, std::min<int64_t>(g.band, P * pc / g.unit));
+}
+
+// Runs and the largest run (in pieces of pc codes) of a tensor for `per` units per run.
+void run_stats(const RunGroups& g, int64_t per, int64_t pc, int64_t* runs, int64_t* max_pieces) {
+  auto band_runs = [&](int64_t units) {
+    if (units <= 0) return;
+    *runs += ceil_div(units, per);
+    *max_pieces = std::max(*max_pieces, ceil_div(std::min(per, units) * g.unit, pc));
+  };
+  if (g.n_full > 0) {
+    *runs += ceil_div(g.band, per) * (g.n_full - 1);   // band_runs adds the last full band
+    band_runs(g.band);
+  }
+  band_runs(g.last);
+}
+
+// Target pieces per run for the whole plan: the one that launches the fewest
+// workgroups (runs x the largest run), the longer target on ties.
+int64_t pick_run_pieces(const std::vector<RunGroups>& gs, int64_t pc) {
+  int64_t best_P = kGatherMinPieces, best = -1;
+  for (int64_t P = kGatherMinPieces; P <= kGatherMaxPieces; ++P) {
+    int64_t runs = 0, maxp = 0;
+    for (const RunGroups& g : gs) run_stats(g, run_units(g, P, pc), pc, &runs, &maxp);
+    const int64_t cost = runs * maxp;
+    if (best < 0 || cost <= best) {
+      best = cost;
+      best_P = P;
+    }
+  }
+  return best_P;
+}
 
 void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   const int64_t top = R_mat * S;
@@ -274,13 +319,33 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   for (const QJob& j : tb->qjobs)
     if (j.kind == QJOB_TILE && !tile_vec[j.tensor] && t[j.tensor].kind != RS_TILEMAJOR)
       tb->gjobs.push_back(j);   // TILEMAJOR tensors use the tile-major strips
+  // one run length for the plan (8-code pieces: kGatherPiece vectors of 8 codes)
+  const int64_t pc8 = kGatherPiece * 8;
+  std::vector<RunGroups> groups(n, RunGroups{0, 0, 0, 0});
+  std::vector<RunGroups> used;
+  for (int64_t ti = 0; ti < n; ++ti) {
+    const Tensor& x = t[ti];
+    if (x.kind == RS_TILE && tile_vec[ti]) groups[ti] = {x.cols, x.p0, x.rows / x.p0, x.rows % x.p0};
+    else if (x.kind == RS_FLAT && x.p0 % 16 == 0 && x.n / x.p0 > 0) groups[ti] = {x.p0, x.n / x.p0, 1, 0};
+    if (groups[ti].unit) used.push_back(groups[ti]);
+  }
+  const int64_t P = pick_run_pieces(used, pc8);
+  {
+    int64_t runs = 0, m8 = 0, m4 = 0;
+    for (const RunGroups& g : used) {
+      run_stats(g, run_units(g, P, pc8), pc8, &runs, &m8);
+      run_stats(g, run_units(g, P, pc8), pc8 / 2, &runs, &m4);
+    }
+    tb->gather_split8 = m8;
+    tb->gather_split4 = m4;
+  }
   q = 0;
   for (int64_t ti = 0; ti < n; ++ti) {
     const Tensor& x = t[ti];
     if (x.kind == RS_TILE) {
       const int64_t ntc = (x.cols + x.p1 - 1) / x.p1;
       if (tile_vec[ti]) {
-        const int64_t per = std::max<int64_t>(1, kGatherChunk / x.cols);
+        const int64_t per = run_units(groups[ti], P, pc8);
         for (int64_t r0 = 0; r0 < x.rows; r0 += x.p0) {
           const int64_t band_end = std::min(x.rows, r0 + x.p0);
           for (int64_t r = r0; r < band_end; r += per) {
@@ -303,8 +368,8 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     } else if (x.kind == RS_FLAT) {
       const int64_t nfull = x.n / x.p0;            // whole blocks
       int64_t done = 0;
-      if (x.p0 % 16 == 0) {
-        const int64_t per = std::max<int64_t>(1, kGatherChunk / x.p0);
+      if (groups[ti].unit) {
+        const int64_t per = run_units(groups[ti], P, pc8);
         for (; done < nfull; done += per) {
           GatherChunk c{};
           c.qbase = x.start + done * x.p0;
@@ -408,7 +473,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     // for any plan but one made of tiny tiles.
     const int64_t items = std::max({static_cast<int64_t>(tb.unpack.size()) * unpack_split(4),
                                     static_cast<int64_t>(tb.pack.size()) * kPackSplit,
-                                    static_cast<int64_t>(tb.gchunks.size()) * gather_split(4),
+                                    static_cast<int64_t>(tb.gchunks.size()) * tb.gather_split4,
                                     static_cast<int64_t>(tb.tm.size()) * tm_pieces(tb.tm_max_strip, 4, kTmThreads),
                                     static_cast<int64_t>(tb.qjobs.size()), static_cast<int64_t>(tb.gjobs.size())});
     if (items > 0xFFFFFFFFll)
@@ -442,6 +507,8 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->n_gflat = tb.n_gflat;
     p->max_tile_vec16 = tb.max_tile_vec16;
     p->split_code_lines = tb.split_code_lines;
+    p->gather_split8 = tb.gather_split8;
+    p->gather_split4 = tb.gather_split4;
     // gfx950's FP8 conversion (OCP E4M3, round to nearest even) by default;
     // RS_E4M3_ENCODER=sw selects the integer encoder, which gives the same codes.
     const char* enc = std::getenv("RS_E4M3_ENCODER");
