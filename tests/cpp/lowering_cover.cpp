@@ -44,9 +44,14 @@ int64_t scale_of(const Tensor& x, int64_t first, int64_t e) {
   return first + (R / x.p0) * ntc + C / x.p1;
 }
 
+int64_t g_split8 = 0, g_split4 = 0, g_runs = 0;
+
 bool check(const std::vector<Tensor>& t, int64_t S, int64_t R, int plant) {
   Tables tb;
   lower(t, S, R, &tb);
+  g_split8 = tb.gather_split8;
+  g_split4 = tb.gather_split4;
+  g_runs = static_cast<int64_t>(tb.gchunks.size());
   if (plant == 1 && !tb.pack.empty()) tb.pack.pop_back();
   if (plant == 2 && !tb.qjobs.empty()) tb.qjobs.insert(tb.qjobs.begin(), tb.qjobs.front());
   if (plant == 3 && !tb.gchunks.empty()) tb.gchunks.back().scale0 += 1;
@@ -172,10 +177,14 @@ bool check(const std::vector<Tensor>& t, int64_t S, int64_t R, int plant) {
   for (int64_t p = 0; p < top; ++p) CHECK(qc[p] == 1, "quant: code %lld written %d times", (long long)p, qc[p]);
   for (int64_t s = 0; s < first[n]; ++s) CHECK(sc[s] == 1, "quant: scale %lld written %d times", (long long)s, sc[s]);
 
-  // gather side: every element of every quantised tensor once, with its own scale
+  // gather side: every element of every quantised tensor once, with its own scale;
+  // no run longer than its launch's split covers
   reset();
   for (const GatherChunk& c : tb.gchunks) {
     const Tensor& x = t[c.tensor];
+    CHECK(ceil_div(int64_t(c.rows) * c.cols, kGatherPiece * 8) <= tb.gather_split8 &&
+              ceil_div(int64_t(c.rows) * c.cols, kGatherPiece * 4) <= tb.gather_split4,
+          "gather run of %lld codes longer than the split", (long long)c.rows * c.cols);
     CHECK(c.qbase == x.start + c.toff && c.cols % 8 == 0, "gather run of tensor %d", c.tensor);
     for (int64_t r = 0; r < c.rows; ++r)
       for (int64_t k = 0; k < c.cols; ++k) {
@@ -236,5 +245,7 @@ int main(int argc, char** argv) {
     return 0;
   }
   std::printf("ok\n");
+  std::printf("gather runs %lld split8 %lld split4 %lld\n", (long long)g_runs, (long long)g_split8,
+              (long long)g_split4);
   return 0;
 }

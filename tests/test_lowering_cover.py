@@ -45,7 +45,18 @@ def _run(exe, specs, V, R=None, plant=0):
     args = [exe] + ([str(plant)] if plant else [])
     r = subprocess.run(args, input="\n".join(lines) + "\n", capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr
-    return r.stdout.strip()
+    return r.stdout.strip().split("\n")[0]
+
+
+def _gather_shape(exe, specs, V):
+    ref = OP.plan(specs, V)
+    lines = [f"{len(specs)} {V} {ref.S} {V}"] + [f"{s.rows} {s.cols} {KINDS[s.kind]} {s.p0} {s.p1} {int(st)}"
+                                                 for s, st in zip(specs, ref.starts)]
+    r = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, timeout=600)
+    out = r.stdout.split("\n")
+    assert out[0] == "ok", r.stdout
+    w = out[1].split()
+    return int(w[2]), int(w[4]), int(w[6])
 
 
 @pytest.mark.parametrize("idx,tm", [(0, False), (1, False), (1, True), (2, False), (4, False)])
@@ -95,3 +106,14 @@ def test_planted_mistakes_are_reported(exe, plant):
              TensorSpec("d", 64, 64, "TILEMAJOR", 32, 32), TensorSpec("e", 100, 30, "ELEM")]
     out = _run(exe, specs, 4, plant=plant)
     assert out.startswith("FAIL"), out
+
+
+def test_gather_runs_fill_their_workgroups(exe):
+    # MoE-shaped experts (2880-wide rows, 128-row bands): 16-row runs of exactly 45 pieces of 1024 codes
+    specs = []
+    for e in range(4):
+        specs += [TensorSpec(f"e{e}.gate_up", 5760, 2880, "TILE", 128, 128),
+                  TensorSpec(f"e{e}.down", 2880, 2880, "TILE", 128, 128)]
+    runs, split8, split4 = _gather_shape(exe, specs, 8)
+    assert (split8, split4) == (45, 90)
+    assert runs == 4 * (5760 // 16 + (22 * 128 // 16 + 64 // 16))
