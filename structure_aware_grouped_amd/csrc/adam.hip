@@ -18,9 +18,10 @@ struct AdamK {
 };
 
 // m1, v1 and the new parameter of one element (every operation rounded).
-// The square root is __builtin_sqrtf, which this build (correctly rounded
-// divide and sqrt) lowers to a correctly rounded sequence; __fsqrt_rn is not
-// correctly rounded on this toolchain (about 15% of inputs differ by an ulp).
+// The square root is __builtin_sqrtf, which the library's compile flags
+// (-fhip-fp32-correctly-rounded-divide-sqrt) lower to a correctly rounded
+// sequence; __fsqrt_rn is not correctly rounded with this compiler (about 15%
+// of inputs differ by an ulp).
 __device__ __forceinline__ void adam_elem(float p, float g, float m0, float v0, const AdamK& k,
                                           float& p1, float& m1, float& v1) {
   m1 = __fadd_rn(__fmul_rn(k.b1, m0), __fmul_rn(k.c1, g));

@@ -73,8 +73,9 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
 // the lanes of a wave read and write one contiguous range each. Workgroup b
 // takes piece b % split of run b / split: kGatherVec vectors per thread, and
 // again split pieces further on while the run lasts. A run of several rows
-// holds fewer than 2^16 vectors (the lowering keeps it under 16384 elements),
-// so its row and tile-column indices come from div_u16.
+// holds at most kGatherMaxPieces * kGatherPiece * 8 = 65536 elements, fewer
+// than 2^16 vectors, so its row and tile-column indices come from div_u16; a
+// one-row run needs no division.
 template <int FMT, bool HW, bool BF16OUT>
 __device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const GatherChunk* __restrict__ chunks,
                                                                     const uint8_t* __restrict__ q,

@@ -1,4 +1,4 @@
-"""Static checks of the top-level scripts that only run on a GPU machine (bench.py,
+"""Static checks of the top-level scripts that need a GPU to run (bench.py,
 __graft_entry__.py): every name a function reads must be defined somewhere -
 a local, a parameter, a module-level definition or import, or a builtin. A
 name lost in an edit would otherwise surface only on the GPU."""
