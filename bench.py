@@ -247,7 +247,8 @@ def cpu_baseline(w, plan, names=None, max_seconds: float = 15.0) -> dict:
         what = f"the first {len(done)} of the layer's {len(w.specs)} tensors"
     return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{what}: unpack + pack{' + e4m3 tile quant' if w.quant else ''}, "
-                      f"{moved / 1e9:.3f} GB in {dt:.1f} s"}
+                      + (f"{moved / 1e9:.3f} GB in {dt:.1f} s" if moved >= 1e8 else
+                         f"{moved / 1e6:.3f} MB in {dt * 1e3:.2f} ms")}
 
 
 def main():
