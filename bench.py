@@ -61,6 +61,8 @@ def parse():
                          "one AdamW step on the int8/uint8 block-quantised m and v")
     ap.add_argument("--tile-major", action="store_true",
                     help="store the TILE tensors tile by tile (TILEMAJOR): unpack and pack reorder through LDS")
+    ap.add_argument("--packed-bf16", action="store_true",
+                    help="pack into a bf16 buffer (a bf16 ReduceScatter): each fp32 result rounded once")
     ap.add_argument("--cpu-sample", type=int, default=1, help="0 disables the CPU-oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled output checks")
     ap.add_argument("--cold-steps", type=int, default=5,
@@ -76,8 +78,9 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, plan) -> dict:
-    """Bytes each kernel must move once per call (read + write)."""
+def algorithmic_bytes(w, plan, packed_bytes: int = 4) -> dict:
+    """Bytes each kernel must move once per call (read + write); packed_bytes is the
+    element size of the packed buffer (4 for fp32, 2 for bf16)."""
     n_all = sum(plan.numels)
     R, S = plan.R_mat, plan.S
     pb = 2 if w.param_dtype == "bf16" else 4
@@ -97,7 +100,7 @@ def algorithmic_bytes(w, plan) -> dict:
             out[f"dequant_{which}"] = dequant
         return out
     out["unpack"] = 2 * n_all * pb
-    out["pack"] = n_all * (4 + (4 if w.accumulate else 0) + 4) + 4 * plan.padding
+    out["pack"] = n_all * (4 + (4 if w.accumulate else 0) + packed_bytes) + packed_bytes * plan.padding
     if w.quant:
         nq = sum(n for sp, n in zip(w.specs, plan.numels) if sp.kind in ("TILE", "TILEMAJOR", "FLAT"))
         out["quant"] = nq * pb + R * S + 4 * plan.n_qblocks
@@ -283,7 +286,10 @@ def main():
     load_ms = (time.perf_counter() - t0) * 1e3
     log(f"plan: S={S}, R_mat={R}, lowered in {load_ms:.0f} ms")
     inp = Inputs(w, S, starts, R, device=dev)
-    nbytes = algorithmic_bytes(w, plan)
+    if args.packed_bf16 and (w.adam_states or args.mode != "step"):
+        print("--packed-bf16 applies to the step of workloads 0-3", file=sys.stderr)
+        sys.exit(2)
+    nbytes = algorithmic_bytes(w, plan, 2 if args.packed_bf16 else 4)
     avg_load = -(-sum(plan.numels) // w.V)
 
     # ---- inputs resident in HBM
@@ -353,7 +359,7 @@ def main():
         params = inp.empty_params()
         grads = inp.grads()
         prev = inp.prev()
-        packed = garbage(R * S, torch.float32, dev)
+        packed = garbage(R * S, torch.bfloat16 if args.packed_bf16 else torch.float32, dev)
         steps = [
             ("unpack", lambda: rs.rs_unpack_gathered(plan, G, params)),
             ("pack", lambda: rs.rs_pack_scatter(plan, grads, packed, prev=prev)),
@@ -498,7 +504,7 @@ def main():
         i = 1
         assert np.array_equal(tensor_bits(params[i]).ravel(), inp.weight_bits(i)), "unpack"
         pads = padding_ranges(specs, starts, S, R)
-        pk = packed.view(torch.int32)
+        pk = packed.view(torch.int16 if args.packed_bf16 else torch.int32)
         assert all(bool((pk[b:e] == 0).all()) for b, e in pads), "pack padding"
         if w.quant:
             assert all(bool((q[b:e] == 0).all()) for b, e in pads), "codes outside blocks"
@@ -531,7 +537,8 @@ def main():
     # of its own: then its eager per-kernel average)
     dom_avg_s = (per_kernel[dominant]["avg_ms"] if args.graph else float(np.mean(dom_ms))) * 1e-3
     achieved = nbytes[dominant] / dom_avg_s / 1e9
-    traffic = read_traffic((args.workload, args.mode, bool(args.tile_major)), dominant)
+    # counter summaries exist for the fp32 packed buffer only
+    traffic = None if args.packed_bf16 else read_traffic((args.workload, args.mode, bool(args.tile_major)), dominant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant])}
@@ -556,9 +563,10 @@ def main():
     if args.mode == "adam8":
         names[4] = ("8-bit Adam states on the Llama-3-8B layer shapes, 2048-element blocks, V=64: one fused "
                     "AdamW step (dequant m, v; update fp32 params; requant m int8, v uint8)")
-    metric = METRIC if (args.workload == 1 and args.mode == "step" and not args.tile_major) else \
+    metric = METRIC if (args.workload == 1 and args.mode == "step" and not args.tile_major
+                        and not args.packed_bf16) else \
         f"DBuffer layout transform GB/s (workload {args.workload}, {args.mode}" + \
-        (", tile-major)" if args.tile_major else ")")
+        (", tile-major" if args.tile_major else "") + (", bf16 packed" if args.packed_bf16 else "") + ")"
     line = {
         "metric": metric,
         "value": round(value, 1),
@@ -579,7 +587,8 @@ def main():
                    "bytes_per_step": int(step_bytes), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "storage": {0: "fp32 params, grads, prev and packed", 2: "bf16 params, fp32 grads/prev/packed",
                                4: "fp32 m/v, int8/uint8 codes + fp32 scales"}.get(
-                       args.workload, "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales"),
+                       args.workload, "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales")
+                   + ("; the packed buffer is bf16" if args.packed_bf16 else ""),
                    "e4m3_encoder": "sw" if os.environ.get("RS_E4M3_ENCODER") == "sw" else "hw",
                    "launch": "one HIP graph replay per step" if args.graph else "eager"},
         "kernels": per_kernel,

@@ -201,15 +201,19 @@ enum { RS_SCALE_INV_V = 0, RS_SCALE_GIVEN = 1 };
  * (for a TILEMAJOR tensor, element (r, c) goes to its place in its tile)
  * (scale first, then add: two IEEE round-to-nearest-even operations, never a
  * fused multiply-add), and packed[p] = +0.0 at every padding position p in
- * [0, R_mat*S). Padding of `prev` is never read.
+ * [0, R_mat*S). Padding of `prev` is never read. With packed_dt = RS_BF16
+ * (a bf16 ReduceScatter, as in mixed-precision training) each fp32 result
+ * is rounded once to the nearest bf16, ties to even.
  * src: HOST array of n device pointers to contiguous gradients (src_dt
  * RS_F32 or RS_BF16, 16-byte aligned). prev: device fp32 R_mat*S or NULL (no
- * accumulation); it may equal `packed` (in-place accumulation). packed:
- * device fp32 R_mat*S, 16-byte aligned.
+ * accumulation); it may equal `packed` (in-place accumulation) only when
+ * packed_dt is RS_F32 (otherwise RS_EINVAL), and must not overlap it in any
+ * other way. packed: device R_mat*S elements of packed_dt (RS_F32 or
+ * RS_BF16), 16-byte aligned.
  * Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */
 int rs_pack_scatter(rs_plan* plan, const void* const* src, int32_t src_dt,
-                    const float* prev, float* packed, int32_t scale_mode, float scale,
-                    void* stream);
+                    const float* prev, void* packed, int32_t packed_dt, int32_t scale_mode,
+                    float scale, void* stream);
 
 /* Block-wise quantisation of every locally whole block (feynmanwiki
  * walkthrough: a quantisation block should live on one device because its

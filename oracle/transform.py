@@ -96,6 +96,17 @@ def pack(grads: Sequence[np.ndarray], prev, specs, starts, S: int, R_mat: int,
     return out
 
 
+def pack_to_bf16(grads: Sequence[np.ndarray], prev, specs, starts, S: int, R_mat: int,
+                 sigma, accumulate: bool) -> np.ndarray:
+    """The packed buffer for a bf16 ReduceScatter (mixed-precision training): every
+    fp32 value of `pack` rounded once to the nearest bf16, ties to even; uint16 bits,
+    padding +0.0. Reading: the pages fuse the copy with the pre-communication ops
+    (walkthrough, DBuffer paragraphs) and train in mixed precision (end-to-end
+    paragraphs) without naming the reduce dtype; a bf16 buffer takes the fp32
+    result of the fused ops and rounds it once, so no intermediate is bf16."""
+    return bf16_round(pack(grads, prev, specs, starts, S, R_mat, sigma, accumulate))
+
+
 # ---------------------------------------------------------------- quant blocks
 
 def quant_blocks(specs, starts) -> Iterator[Tuple[int, int, np.ndarray]]:

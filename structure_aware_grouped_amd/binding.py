@@ -69,7 +69,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rs_plan_free.argtypes = [P]
     lib.rs_plan_free.restype = None
     lib.rs_unpack_gathered.argtypes = [P, P, I32, ctypes.POINTER(P), P]
-    lib.rs_pack_scatter.argtypes = [P, ctypes.POINTER(P), I32, P, P, I32, F, P]
+    lib.rs_pack_scatter.argtypes = [P, ctypes.POINTER(P), I32, P, P, I32, I32, F, P]
     lib.rs_block_quant.argtypes = [P, P, I32, P, I32, P, P]
     lib.rs_block_dequant.argtypes = [P, P, I32, P, P, P]
     lib.rs_unpack_dequant.argtypes = [P, P, I32, P, ctypes.POINTER(P), I32, P]
@@ -263,13 +263,16 @@ def rs_unpack_gathered(plan: Plan, gathered: torch.Tensor, dsts: List[torch.Tens
 
 def rs_pack_scatter(plan: Plan, srcs: List[torch.Tensor], packed: torch.Tensor,
                     prev: Optional[torch.Tensor] = None, scale: Optional[float] = None):
-    """packed <- [prev +] src * sigma on tensors, +0.0 on padding; sigma = fl32(1/V) unless given."""
+    """packed <- [prev +] src * sigma on tensors, +0.0 on padding; sigma = fl32(1/V) unless given.
+    packed is fp32, or bf16 (each fp32 result rounded once to nearest even); prev is fp32."""
     _count_check(plan, srcs, "srcs")
     if srcs[0].dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("sources are fp32 or bf16")
     _dev_check(plan, packed, prev, *srcs)
-    if packed.dtype != torch.float32 or (prev is not None and prev.dtype != torch.float32):
-        raise ValueError("packed and prev are fp32")
+    if packed.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("packed is fp32 or bf16")
+    if prev is not None and prev.dtype != torch.float32:
+        raise ValueError("prev is fp32")
     if packed.numel() < plan.R_mat * plan.S or (prev is not None and prev.numel() < plan.R_mat * plan.S):
         raise ValueError("packed / prev shorter than R_mat * S")
     dt = srcs[0].dtype
@@ -279,6 +282,7 @@ def rs_pack_scatter(plan: Plan, srcs: List[torch.Tensor], packed: torch.Tensor,
     mode, val = (0, 0.0) if scale is None else (1, float(scale))
     _check(load().rs_pack_scatter(plan.handle, _ptrs(srcs), RS_F32 if dt == torch.float32 else RS_BF16,
                                   prev.data_ptr() if prev is not None else None, packed.data_ptr(),
+                                  RS_F32 if packed.dtype == torch.float32 else RS_BF16,
                                   mode, ctypes.c_float(val), _stream(plan.device)))
 
 

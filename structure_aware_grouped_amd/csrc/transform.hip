@@ -73,25 +73,45 @@ __device__ __forceinline__ float load1(const void* p, int64_t e) {
     return static_cast<const float*>(p)[e];
 }
 
+// Four (or one) packed values at element `pos` of the packed buffer: fp32, or,
+// for a bf16 buffer (OB), each fp32 result rounded once to the nearest bf16
+// (ties to even).
+template <bool OB>
+__device__ __forceinline__ void store_packed4(void* out, int64_t pos, const f32x4& y) {
+  if constexpr (OB)
+    stg(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + pos),
+        u32x2{bf16_rne(y.x) | (bf16_rne(y.y) << 16), bf16_rne(y.z) | (bf16_rne(y.w) << 16)});
+  else
+    stg(reinterpret_cast<f32x4*>(static_cast<float*>(out) + pos), y);
+}
+
+template <bool OB>
+__device__ __forceinline__ void store_packed1(void* out, int64_t pos, float y) {
+  if constexpr (OB)
+    static_cast<uint16_t*>(out)[pos] = static_cast<uint16_t>(bf16_rne(y));
+  else
+    static_cast<float*>(out)[pos] = y;
+}
+
 // packed = acc ? prev + src*sigma : src*sigma on tensor data, +0.0 on padding.
 // Workgroup b writes piece b % kPackSplit (kPackPiece output vectors) of
 // chunk b / kPackSplit. `prev` may alias `out`: every element is read before
-// it is written, by the same thread.
-template <bool BF16, bool ACC>
+// it is written, by the same thread (fp32 output only).
+template <bool BF16, bool ACC, bool OB>
 __device__ __forceinline__ void pack_kernel_piece(unsigned b, const PackChunk* __restrict__ chunks,
                                                              const void* const* __restrict__ src,
-                                                             const float* prev, float* out, float sigma) {
+                                                             const float* prev, void* out, float sigma) {
   const unsigned cu = b / static_cast<unsigned>(kPackSplit);
   const int ci = static_cast<int>(cu);
   const int piece = static_cast<int>(b - cu * static_cast<unsigned>(kPackSplit));
   const PackChunk c = chunks[ci];
-  f32x4* o4 = reinterpret_cast<f32x4*>(out + c.out);
   const int nv = c.n_total >> 2;
   const int v0 = piece * static_cast<int>(kPackPiece) + static_cast<int>(threadIdx.x);
   if (c.tensor < 0) {
 #pragma unroll
     for (int u = 0; u < kPackVec; ++u)
-      if (v0 + u * kPackThreads < nv) stg(o4 + v0 + u * kPackThreads, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      if (v0 + u * kPackThreads < nv)
+        store_packed4<OB>(out, c.out + 4 * static_cast<int64_t>(v0 + u * kPackThreads), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
     return;
   }
   const void* g = src[c.tensor];
@@ -137,16 +157,16 @@ __device__ __forceinline__ void pack_kernel_piece(unsigned b, const PackChunk* _
       }
       y = f32x4{t[0], t[1], t[2], t[3]};
     }
-    stg(o4 + i, y);
+    store_packed4<OB>(out, c.out + 4 * static_cast<int64_t>(i), y);
   }
 }
 
-template <bool BF16, bool ACC>
+template <bool BF16, bool ACC, bool OB>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
                                                              const void* const* __restrict__ src,
-                                                             const float* prev, float* out, float sigma, unsigned n_pieces) {
+                                                             const float* prev, void* out, float sigma, unsigned n_pieces) {
   for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
-    pack_kernel_piece<BF16, ACC>(piece_index<kPackXcdGroup>(p, n_pieces), chunks, src, prev, out, sigma);
+    pack_kernel_piece<BF16, ACC, OB>(piece_index<kPackXcdGroup>(p, n_pieces), chunks, src, prev, out, sigma);
 }
 
 // ------------------------------------------------------------------ tile-major layout
@@ -214,10 +234,10 @@ __global__ __launch_bounds__(kTmLdsThreads) void unpack_tm_kernel(const TmJob* _
 // tile's run of h*bc elements is written contiguously as
 // [prev +] fl32(g * sigma). `prev` may alias `out` (each element is read and
 // written by the same thread).
-template <bool BF16, bool ACC>
+template <bool BF16, bool ACC, bool OB>
 __device__ __forceinline__ void pack_tm_kernel_job(unsigned jb, unsigned n_jobs, const TmJob* __restrict__ jobs,
                                                            const void* const* __restrict__ src,
-                                                           const float* prev, float* out, float sigma) {
+                                                           const float* prev, void* out, float sigma) {
   extern __shared__ __attribute__((aligned(16))) float tm_stage_f32[];   // the plan's largest strip
   float* stage = tm_stage_f32;
   const TmJob j = jobs[jb];
@@ -241,7 +261,7 @@ __device__ __forceinline__ void pack_tm_kernel_job(unsigned jb, unsigned n_jobs,
         const f32x4 pv = ldg(reinterpret_cast<const f32x4*>(prev + pos));
         y = f32x4{__fadd_rn(pv.x, y.x), __fadd_rn(pv.y, y.y), __fadd_rn(pv.z, y.z), __fadd_rn(pv.w, y.w)};
       }
-      stg(reinterpret_cast<f32x4*>(out + pos), y);
+      store_packed4<OB>(out, pos, y);
     }
     return;
   }
@@ -255,16 +275,16 @@ __device__ __forceinline__ void pack_tm_kernel_job(unsigned jb, unsigned n_jobs,
     const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
     float y = __fmul_rn(stage[r * width + t * bc + c], sigma);
     if constexpr (ACC) y = __fadd_rn(prev[pos], y);
-    out[pos] = y;
+    store_packed1<OB>(out, pos, y);
   }
 }
 
-template <bool BF16, bool ACC>
+template <bool BF16, bool ACC, bool OB>
 __global__ __launch_bounds__(kTmLdsThreads) void pack_tm_kernel(const TmJob* __restrict__ jobs,
                                                            const void* const* __restrict__ src,
-                                                           const float* prev, float* out, float sigma, unsigned n_jobs) {
+                                                           const float* prev, void* out, float sigma, unsigned n_jobs) {
   for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
-    pack_tm_kernel_job<BF16, ACC>(jb, n_jobs, jobs, src, prev, out, sigma);
+    pack_tm_kernel_job<BF16, ACC, OB>(jb, n_jobs, jobs, src, prev, out, sigma);
     __syncthreads();   // the next job reuses this workgroup's LDS
   }
 }
@@ -322,10 +342,10 @@ __global__ __launch_bounds__(kTmThreads) void unpack_tm_direct_kernel(const TmJo
     unpack_tm_direct_kernel_piece<EB>(p, jobs, gathered, dst, split);
 }
 
-template <bool BF16, bool ACC>
+template <bool BF16, bool ACC, bool OB>
 __device__ __forceinline__ void pack_tm_direct_kernel_piece(unsigned b, const TmJob* __restrict__ jobs,
                                                                     const void* const* __restrict__ src,
-                                                                    const float* prev, float* out, float sigma,
+                                                                    const float* prev, void* out, float sigma,
                                                                     int split) {
   const unsigned ju = b / static_cast<unsigned>(split);
   const int ji = static_cast<int>(ju);
@@ -349,7 +369,7 @@ __device__ __forceinline__ void pack_tm_direct_kernel_piece(unsigned b, const Tm
         const f32x4 pv = ldg(reinterpret_cast<const f32x4*>(prev + pos));
         y = f32x4{__fadd_rn(pv.x, y.x), __fadd_rn(pv.y, y.y), __fadd_rn(pv.z, y.z), __fadd_rn(pv.w, y.w)};
       }
-      stg(reinterpret_cast<f32x4*>(out + pos), y);
+      store_packed4<OB>(out, pos, y);
     }
     return;
   }
@@ -362,17 +382,17 @@ __device__ __forceinline__ void pack_tm_direct_kernel_piece(unsigned b, const Tm
     const int64_t pos = j.base + static_cast<int64_t>(t) * j.tile_elems + e;
     float y = __fmul_rn(load1<BF16>(g, j.toff + static_cast<int64_t>(r) * j.cols + t * bc + c), sigma);
     if constexpr (ACC) y = __fadd_rn(prev[pos], y);
-    out[pos] = y;
+    store_packed1<OB>(out, pos, y);
   }
 }
 
-template <bool BF16, bool ACC>
+template <bool BF16, bool ACC, bool OB>
 __global__ __launch_bounds__(kTmThreads) void pack_tm_direct_kernel(const TmJob* __restrict__ jobs,
                                                                     const void* const* __restrict__ src,
-                                                                    const float* prev, float* out, float sigma,
+                                                                    const float* prev, void* out, float sigma,
                                                                     int split, unsigned n_pieces) {
   for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
-    pack_tm_direct_kernel_piece<BF16, ACC>(p, jobs, src, prev, out, sigma, split);
+    pack_tm_direct_kernel_piece<BF16, ACC, OB>(p, jobs, src, prev, out, sigma, split);
 }
 
 }  // namespace
@@ -424,14 +444,47 @@ extern "C" int rs_unpack_gathered(rs_plan* p, const void* gathered, int32_t dt, 
   return launched(who);
 }
 
+namespace {
+
+template <bool BF16, bool ACC, bool OB>
+void launch_pack(const rs_plan* p, void** tab, const float* prev, void* packed, float sigma, hipStream_t s) {
+  if (p->n_pack) {
+    const int64_t n_pieces = p->n_pack * kPackSplit;
+    hipLaunchKernelGGL((pack_kernel<BF16, ACC, OB>), grid_of(p, n_pieces), dim3(kPackThreads), 0, s, p->pack, tab,
+                       prev, packed, sigma, static_cast<unsigned>(n_pieces));
+  }
+  if (p->n_tm && !p->tm_pack_lds) {
+    const int64_t split = tm_pieces(p->tm_max_strip, 4, kTmThreads);
+    const int64_t n = p->n_tm * split;
+    hipLaunchKernelGGL((pack_tm_direct_kernel<BF16, ACC, OB>), grid_of(p, n), dim3(kTmThreads), 0, s, p->tmjobs, tab,
+                       prev, packed, sigma, static_cast<int>(split), static_cast<unsigned>(n));
+  } else if (p->n_tm) {
+    const unsigned lds = static_cast<unsigned>(p->tm_max_strip * 4);
+    hipLaunchKernelGGL((pack_tm_kernel<BF16, ACC, OB>), grid_of(p, p->n_tm), dim3(kTmLdsThreads), lds, s, p->tmjobs,
+                       tab, prev, packed, sigma, static_cast<unsigned>(p->n_tm));
+  }
+}
+
+template <bool BF16, bool OB>
+void launch_pack_acc(const rs_plan* p, void** tab, const float* prev, void* packed, float sigma, hipStream_t s) {
+  if (prev) launch_pack<BF16, true, OB>(p, tab, prev, packed, sigma, s);
+  else launch_pack<BF16, false, OB>(p, tab, prev, packed, sigma, s);
+}
+
+}  // namespace
+
 extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_dt, const float* prev,
-                               float* packed, int32_t scale_mode, float scale, void* stream) {
+                               void* packed, int32_t packed_dt, int32_t scale_mode, float scale, void* stream) {
   const char* who = "rs_pack_scatter";
   clear_error();
   int st = check_call(p, who);
   if (st != RS_OK) return st;
   if (src_dt != RS_F32 && src_dt != RS_BF16) return fail(RS_EDTYPE, std::string(who) + ": src must be fp32 or bf16");
+  if (packed_dt != RS_F32 && packed_dt != RS_BF16)
+    return fail(RS_EDTYPE, std::string(who) + ": packed must be fp32 or bf16");
   if (!src || !packed) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+  if (packed_dt == RS_BF16 && prev && static_cast<const void*>(prev) == packed)
+    return fail(RS_EINVAL, std::string(who) + ": in-place accumulation needs an fp32 packed buffer");
   if (!aligned16(packed) || (prev && !aligned16(prev)))
     return fail(RS_EALIGN, std::string(who) + ": packed / prev not 16-byte aligned");
   for (int64_t i = 0; i < p->n; ++i) {
@@ -450,43 +503,10 @@ extern "C" int rs_pack_scatter(rs_plan* p, const void* const* src, int32_t src_d
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = sync_table(p, &p->src, src, s, who);
   if (st != RS_OK) return st;
-  const int64_t n_pieces = p->n_pack * kPackSplit;
-  const unsigned np = static_cast<unsigned>(n_pieces);
-  const dim3 grid = grid_of(p, n_pieces), sblock(kPackThreads);
   void** tab = p->src.dev;
-  if (p->n_pack) {
-    if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_kernel<false, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
-      else hipLaunchKernelGGL((pack_kernel<false, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
-    } else {
-      if (prev) hipLaunchKernelGGL((pack_kernel<true, true>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
-      else hipLaunchKernelGGL((pack_kernel<true, false>), grid, sblock, 0, s, p->pack, tab, prev, packed, sigma, np);
-    }
-  }
-  if (p->n_tm && !p->tm_pack_lds) {
-    const int64_t split = tm_pieces(p->tm_max_strip, 4, kTmThreads);
-    const int64_t n = p->n_tm * split;
-    const dim3 g = grid_of(p, n), b(kTmThreads);
-    const int sp = static_cast<int>(split);
-    const unsigned ntp = static_cast<unsigned>(n);
-    if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<false, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
-      else hipLaunchKernelGGL((pack_tm_direct_kernel<false, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
-    } else {
-      if (prev) hipLaunchKernelGGL((pack_tm_direct_kernel<true, true>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
-      else hipLaunchKernelGGL((pack_tm_direct_kernel<true, false>), g, b, 0, s, p->tmjobs, tab, prev, packed, sigma, sp, ntp);
-    }
-  } else if (p->n_tm) {
-    const dim3 g = grid_of(p, p->n_tm);
-    const unsigned nj = static_cast<unsigned>(p->n_tm);
-    const unsigned lds = static_cast<unsigned>(p->tm_max_strip * 4);
-    if (src_dt == RS_F32) {
-      if (prev) hipLaunchKernelGGL((pack_tm_kernel<false, true>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
-      else hipLaunchKernelGGL((pack_tm_kernel<false, false>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
-    } else {
-      if (prev) hipLaunchKernelGGL((pack_tm_kernel<true, true>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
-      else hipLaunchKernelGGL((pack_tm_kernel<true, false>), g, dim3(kTmLdsThreads), lds, s, p->tmjobs, tab, prev, packed, sigma, nj);
-    }
-  }
+  if (src_dt == RS_F32 && packed_dt == RS_F32) launch_pack_acc<false, false>(p, tab, prev, packed, sigma, s);
+  else if (src_dt == RS_F32) launch_pack_acc<false, true>(p, tab, prev, packed, sigma, s);
+  else if (packed_dt == RS_F32) launch_pack_acc<true, false>(p, tab, prev, packed, sigma, s);
+  else launch_pack_acc<true, true>(p, tab, prev, packed, sigma, s);
   return launched(who);
 }

@@ -131,7 +131,7 @@ int main(int argc, char** argv) {
 
   /* the null stream: every call is ordered on it */
   RS_OK_(rs_unpack_gathered(plan, d_gathered, RS_F32, dst, NULL));
-  RS_OK_(rs_pack_scatter(plan, src, RS_F32, d_prev, d_packed, RS_SCALE_INV_V, 0.0f, NULL));
+  RS_OK_(rs_pack_scatter(plan, src, RS_F32, d_prev, d_packed, RS_F32, RS_SCALE_INV_V, 0.0f, NULL));
   RS_OK_(rs_block_quant(plan, d_gathered, RS_F32, d_codes, RS_E4M3, d_scales, NULL));
   HIP_OK(hipDeviceSynchronize());
 

@@ -93,6 +93,14 @@ def _full_check(rs, specs, V, pdtype, seed, fmts=("e4m3", "i8", "u8"), R_mat=Non
     rs.rs_pack_scatter(plan, grads, inplace, prev=inplace, scale=0.75)
     want2 = OT.pack(grads_h, prev_h, specs, plan.starts, S, R, np.float32(0.75), True)
     assert np.array_equal(tensor_bits(inplace), want2.view(np.uint32))
+    # a bf16 packed buffer (bf16 ReduceScatter): each fp32 result rounded once to nearest even
+    for acc in (True, False):
+        bwhole, pb = guarded(total, torch.bfloat16, DEV)
+        pb.view(torch.uint8).fill_(0xA5)
+        rs.rs_pack_scatter(plan, grads, pb, prev=prev if acc else None)
+        want_b = OT.pack_to_bf16(grads_h, prev_h if acc else None, specs, plan.starts, S, R, sigma, acc)
+        assert np.array_equal(tensor_bits(pb), want_b), acc
+        assert guard_intact(bwhole, total)
 
     # quant and dequant of the flat parameter buffer
     for fmt in fmts:
@@ -438,11 +446,18 @@ def test_bad_arguments_launch_nothing(gpu_lib):
     st = lib.rs_block_quant(plan.handle, G.data_ptr(), b.RS_F32, q.data_ptr(), b.RS_F32,
                             sc.data_ptr(), b._stream(0))
     assert st == b.RS_EDTYPE
-    st = lib.rs_pack_scatter(plan.handle, b._ptrs([dst[0]]), b.RS_E4M3, None, G.data_ptr(), 0,
+    st = lib.rs_pack_scatter(plan.handle, b._ptrs([dst[0]]), b.RS_E4M3, None, G.data_ptr(), b.RS_F32, 0,
                              0.0, b._stream(0))
     assert st == b.RS_EDTYPE
+    st = lib.rs_pack_scatter(plan.handle, b._ptrs([dst[0]]), b.RS_F32, None, G.data_ptr(), b.RS_E4M3, 0,
+                             0.0, b._stream(0))
+    assert st == b.RS_EDTYPE
+    # a bf16 packed buffer cannot also be the fp32 accumulator
+    st = lib.rs_pack_scatter(plan.handle, b._ptrs([dst[0]]), b.RS_F32, G.data_ptr(), G.data_ptr(), b.RS_BF16, 0,
+                             0.0, b._stream(0))
+    assert st == b.RS_EINVAL
     torch.cuda.synchronize()
-    assert bool((dst[0] == 7.0).all()) and bool((q == 3).all())
+    assert bool((dst[0] == 7.0).all()) and bool((q == 3).all()) and bool((G == 0).all())
     plan.close()
 
 

@@ -102,6 +102,19 @@ def test_param_and_grad_workloads(gpu_lib, idx, tile_major):
     pads = OP.padding_ranges(specs, plan.starts, S, R)
     _zero_everywhere(packed, pads)
     print(f"  unpack and pack match on tensors {sample}; padding zero", flush=True)
+    if idx == 1 and not tile_major:
+        # the same pack into a bf16 buffer (bf16 ReduceScatter): each fp32 result rounded once
+        del packed
+        packed_b = garbage(R * S, torch.bfloat16, DEV)
+        rs.rs_pack_scatter(plan, grads, packed_b, prev=prev)
+        torch.cuda.synchronize()
+        for i in sample:
+            s, n = plan.starts[i], plan.numels[i]
+            want = OT.bf16_round(OT.pack_values(inp.grad(i).ravel(), inp.prev_range(s, s + n), sigma, True))
+            assert np.array_equal(tensor_bits(packed_b[s: s + n]), want), f"bf16 pack {i}"
+        _zero_everywhere(packed_b.view(torch.int16), pads)
+        del packed_b
+        print("  bf16 pack matches on the same tensors; padding zero", flush=True)
 
     if w.quant:
         first = [0]

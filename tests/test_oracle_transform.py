@@ -260,3 +260,26 @@ def test_unpack_dequant_round_trips_values_on_the_code_grid(fmt):
             want = src[s: s + n].reshape(specs[i].rows, specs[i].cols)
             got = full[i] if out == "f32" else (full[i].astype(np.uint32) << 16).view(np.float32)
             assert np.array_equal(got, want)
+
+
+def test_pack_to_bf16_rounds_each_fp32_result_once():
+    """A bf16 packed buffer is the fp32 pack rounded to nearest even once: equal to torch's
+    fp32 -> bf16 cast of the fp32 result, ties to the even mantissa, padding +0.0."""
+    import torch
+    w, p = _tiny_plan()
+    S, R = p.S, w.V
+    grads = [W.tensor_values(w, i, W.Role.GRAD) for i in range(3)]
+    prev = np.concatenate([W.prev_slice(w, k, S) for k in range(R)])
+    for acc in (True, False):
+        f32 = T.pack(grads, prev if acc else None, w.specs, p.starts, S, R, T.inv_v(w.V), acc)
+        got = T.pack_to_bf16(grads, prev if acc else None, w.specs, p.starts, S, R, T.inv_v(w.V), acc)
+        want = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert got.dtype == np.uint16 and np.array_equal(got, want)
+        for b, e in P.padding_ranges(w.specs, p.starts, S, R):
+            assert np.all(got[b:e] == 0)
+    # exact midpoints between neighbouring bf16 values go to the even one (sigma = 1, no accumulation)
+    spec = [TensorSpec("t", 1, 16, "ELEM")]
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0xBF818000, 0x3F80C000, 0x3F804000] + [0] * 10,
+                    dtype=np.uint32).view(np.float32)
+    out = T.pack_to_bf16([ties], None, spec, [0], 16, 1, np.float32(1.0), False)
+    assert list(out[:6]) == [0x3F80, 0x3F82, 0xBF80, 0xBF82, 0x3F81, 0x3F80]
