@@ -188,20 +188,34 @@ def block_dequant(q: np.ndarray, scales, specs, starts, S: int, R_mat: int, fmt:
 # ---------------------------------------------------------------- gather side
 
 def bf16_round(x) -> np.ndarray:
-    """Nearest bf16 value of each finite fp32, ties to the even bf16 mantissa; uint16 bits.
+    """Nearest bf16 of each fp32, ties to the even bf16 mantissa; uint16 bits.
 
-    The two candidates are x's bits truncated to the top 16 and the next bf16
-    step up (in magnitude); the nearer one wins, a tie goes to the one whose
-    lowest kept bit is 0."""
+    Finite x: the two candidates are x's bits truncated to the top 16 and the
+    next bf16 step up in magnitude; the nearer one wins, a tie goes to the one
+    whose lowest kept bit is 0. A candidate past the largest finite bf16 is
+    infinity and is weighed as 2^128, the value the next step would have
+    (IEEE 754 overflow under round to nearest: from the midpoint between the
+    largest finite bf16 and 2^128 on, the result is infinity). Infinities are
+    kept. NaN stays NaN (reading, the pages name no NaN rule): its sign and
+    top seven payload bits are kept and the quiet bit 0x0040 is set, so no
+    NaN payload can carry into the exponent and turn into a number."""
     x = np.asarray(x, dtype=np.float32)
     u = x.view(np.uint32)
     lo = u & np.uint32(0xFFFF0000)
     hi = lo + np.uint32(0x10000)
-    a = np.abs(x.astype(np.float64))
-    d_lo = a - np.abs(lo.view(np.float32).astype(np.float64))
-    d_hi = np.abs(hi.view(np.float32).astype(np.float64)) - a
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo >> np.uint32(16)) & np.uint32(1)).astype(bool))
-    return (np.where(pick_hi, hi, lo) >> np.uint32(16)).astype(np.uint16)
+    hi_exp_all_ones = (hi & np.uint32(0x7F800000)) == np.uint32(0x7F800000)
+    with np.errstate(invalid="ignore"):   # NaN inputs, and NaN bit patterns among the candidates
+        a = np.abs(x.astype(np.float64))
+        lo_mag = np.abs(lo.view(np.float32).astype(np.float64))
+        hi_mag = np.where(hi_exp_all_ones, 2.0 ** 128, np.abs(hi.view(np.float32).astype(np.float64)))
+    finite = np.isfinite(a)
+    a_f = np.where(finite, a, 0.0)
+    d_lo = np.where(finite, a_f - np.where(finite, lo_mag, 0.0), 0.0)
+    d_hi = np.where(finite, hi_mag - a_f, 1.0)
+    pick_hi = finite & ((d_hi < d_lo) | ((d_hi == d_lo) & ((lo >> np.uint32(16)) & np.uint32(1)).astype(bool)))
+    out = (np.where(pick_hi, hi, lo) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(a)
+    return np.where(nan, ((u >> np.uint32(16)) | np.uint32(0x0040)).astype(np.uint16), out)
 
 
 def unpack_dequant(q: np.ndarray, scales, specs, starts, fmt: str, out: str):

@@ -227,6 +227,36 @@ def test_bf16_round_matches_torch_and_hand_cases():
     assert T.bf16_round(np.float32([1 + 3 * 2 ** -8]))[0] == 0x3F82
 
 
+def test_bf16_round_overflow_and_infinities_match_torch():
+    """IEEE overflow: the largest finite bf16 is 0x7F7F = (2 - 2^-7) * 2^127; from the midpoint
+    between it and 2^128, (2 - 2^-8) * 2^127 = fp32 bits 0x7F7F8000, the result is infinity.
+    Below the midpoint it stays 0x7F7F. torch's cast and the closed form agree."""
+    import torch
+    bits = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x7F800000,
+                     0xFF7F7FFF, 0xFF7F8000, 0xFF7FFFFF, 0xFF800000, 0x7F7E8000, 0x7F7F0000], dtype=np.uint32)
+    x = bits.view(np.float32)
+    got = T.bf16_round(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    assert list(got) == [0x7F7F, 0x7F80, 0x7F80, 0x7F80, 0x7F80, 0xFF7F, 0xFF80, 0xFF80, 0xFF80, 0x7F7E, 0x7F7F]
+
+
+def test_bf16_round_keeps_nan():
+    """A NaN stays NaN (torch's cast does too) with its sign and the top payload bits; the
+    quiet bit is set. A payload that rounding would carry into the exponent (0x7FFFFFFF,
+    0xFFFFFFFF) must not come out as a number."""
+    import torch
+    bits = np.array([0x7FFFFFFF, 0xFFFFFFFF, 0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001,
+                     0x7FBFFFFF, 0x7FC0FFFF, 0x7FFF8000], dtype=np.uint32)
+    x = bits.view(np.float32)
+    got = T.bf16_round(x)
+    as_f32 = (got.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    assert np.all(np.isnan(as_f32))
+    assert np.isnan(torch.from_numpy(x).to(torch.bfloat16).float().numpy()).all()
+    assert np.array_equal(got >> np.uint16(15), (bits >> np.uint32(31)).astype(np.uint16))   # sign kept
+    assert list(got) == [0x7FFF, 0xFFFF, 0x7FC0, 0xFFC0, 0x7FC0, 0xFFC0, 0x7FFF, 0x7FC0, 0x7FFF]
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "i8", "u8"])
 def test_unpack_dequant_round_trips_values_on_the_code_grid(fmt):
     """Blocks whose values are code values times a power-of-two scale with amax exactly Q*2^k
