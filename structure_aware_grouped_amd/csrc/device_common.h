@@ -243,10 +243,14 @@ __device__ __forceinline__ unsigned piece_index(unsigned b, unsigned n) {
   }
 }
 
-// Nearest bf16 of a finite fp32, ties to even: add 0x7fff plus the kept lsb,
-// keep the top half.
+// Nearest bf16 of an fp32, ties to even: add 0x7fff plus the kept lsb, keep
+// the top half (a finite value past the overflow midpoint carries into
+// infinity; infinities stay). A NaN keeps its sign and top payload bits with
+// the quiet bit set: the rounding add would carry some NaN payloads into the
+// exponent and sign (0x7fffffff would become -0.0).
 __device__ __forceinline__ uint32_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 

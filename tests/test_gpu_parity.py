@@ -296,6 +296,43 @@ def test_trailing_padding_ranks(gpu_lib):
     _full_check(rs, specs, 16, torch.bfloat16, 3)
 
 
+def test_bf16_pack_keeps_nan_and_overflows_to_infinity(gpu_lib):
+    """A bf16 packed buffer from gradients holding NaN payloads that the rounding add would
+    carry into the exponent (0x7FFFFFFF, 0xFFFFFFFF) and other NaNs: every NaN stays NaN
+    (checked position by position against the oracle). Values past bf16's overflow midpoint
+    come out as infinities, bit for bit, as do all finite values."""
+    import structure_aware_grouped_amd as rs
+    specs = [TensorSpec("a", 40, 48, "ROWS", 1), TensorSpec("b", 300, 1, "ELEM")]
+    plan = _plan(rs, specs, 4)
+    R, S = plan.R_mat, plan.S
+    rng = _rng(77)
+    specials = np.array([0x7FFFFFFF, 0xFFFFFFFF, 0x7FC00000, 0xFFC00001, 0x7FBFFFFF, 0x7F7FFFFF, 0xFF7FFFFF,
+                         0x7F7F8000, 0x7F7F7FFF, 0x7F800000, 0xFF800000], dtype=np.uint32).view(np.float32)
+    grads_h = []
+    for sp in specs:
+        g = _values(rng, sp.rows * sp.cols, scale=1e-3)
+        pos = rng.choice(g.size, size=4 * specials.size, replace=False)
+        g[pos] = np.tile(specials, 4)
+        grads_h.append(g.reshape(sp.rows, sp.cols))
+    grads = [torch.from_numpy(g).to(DEV) for g in grads_h]
+    prev_h = _values(rng, R * S, scale=1e-3)
+    prev = torch.from_numpy(prev_h).to(DEV)
+    for acc in (False, True):
+        whole, pb = guarded(R * S, torch.bfloat16, DEV)
+        pb.view(torch.uint8).fill_(0xA5)
+        rs.rs_pack_scatter(plan, grads, pb, prev=prev if acc else None, scale=1.0)
+        torch.cuda.synchronize()
+        want = OT.pack_to_bf16(grads_h, prev_h if acc else None, specs, plan.starts, S, R, np.float32(1.0), acc)
+        got = tensor_bits(pb)
+        as_f32 = lambda b: (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        nan_w, nan_g = np.isnan(as_f32(want)), np.isnan(as_f32(got))
+        assert nan_w.sum() >= 4 * 5 * len(specs) and np.array_equal(nan_w, nan_g), acc
+        assert np.array_equal(got[~nan_w], want[~nan_w]), acc
+        assert np.isinf(as_f32(got)).sum() >= 4 * 5 * len(specs), acc
+        assert guard_intact(whole, R * S)
+    plan.close()
+
+
 def test_single_element_group(gpu_lib):
     import structure_aware_grouped_amd as rs
     _full_check(rs, [TensorSpec("x", 1, 1, "FLAT", 1)], 1, torch.float32, 5)
