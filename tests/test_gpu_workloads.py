@@ -11,7 +11,7 @@ import torch
 
 from oracle import plan as OP, transform as OT
 from tests.gpu_util import Inputs, garbage, tensor_bits
-from workloads import f32_from_bf16_bits, tile_major_variant, workload
+from workloads import tile_major_variant, workload
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -43,11 +43,6 @@ def _zero_everywhere(t: torch.Tensor, ranges):
         assert bool((flat[b:e] == 0).all().item()), (b, e)
 
 
-def _tensor_param_f32(inp, i):
-    bits = inp.weight_bits(i)
-    return f32_from_bf16_bits(bits) if bits.dtype == np.uint16 else bits.view(np.float32)
-
-
 def _arrange(specs):
     """Row-major bits -> the order of the tensor's interval (the oracle's layout)."""
     def arrange(i, bits):
@@ -57,6 +52,75 @@ def _arrange(specs):
         out[OP.layout_offsets(specs[i])] = bits
         return out
     return arrange
+
+
+def _quant_bands(w, plan):
+    """{tensor: [(r0, r1), ...]} of the tile bands whose codes, scales and rebuilt bf16
+    rows are compared with the oracle at full size.
+    Llama-3-8B layer (row-major or tile-major): every band of every quantised tensor,
+    down (4096 x 14336, the widest) included.
+    MoE layer: the router, the first and the last expert whole, and in every tensor that
+    a rank boundary crosses, the band on each side of that boundary."""
+    specs = list(w.specs)
+    quantised = [i for i, sp in enumerate(specs) if sp.kind in ("TILE", "TILEMAJOR")]
+
+    def all_bands(i):
+        sp = specs[i]
+        return [(r0, min(r0 + sp.p0, sp.rows)) for r0 in range(0, sp.rows, sp.p0)]
+
+    if w.index == 1:
+        return {i: all_bands(i) for i in quantised}
+    names = {sp.name: i for i, sp in enumerate(specs)}
+    whole = [names["router"], names["e0.gate_up"], names["e0.down"], names["e127.gate_up"], names["e127.down"]]
+    wanted = {i: all_bands(i) for i in whole}
+    S = plan.S
+    for k in range(1, plan.R_mat):
+        pos = k * S
+        for i in quantised:
+            s, sp = plan.starts[i], specs[i]
+            if s < pos < s + sp.numel:
+                e = pos - s
+                assert e % (sp.p0 * sp.cols) == 0, "a rank boundary inside a tile band"
+                row = e // sp.cols
+                if i not in whole:
+                    bands = wanted.setdefault(i, [])
+                    for b in ((row - sp.p0, row), (row, min(row + sp.p0, sp.rows))):
+                        if b not in bands:
+                            bands.append(b)
+    for i in wanted:
+        wanted[i].sort()
+    return wanted
+
+
+def _check_quant_full_size(w, idx, tile_major, plan, q, scales, gathered):
+    """Codes, scales and the fused gather side of the chosen bands (every tile of each band)
+    against the oracle, computed band by band in worker processes."""
+    from tests import oracle_pool
+    specs = list(w.specs)
+    first = [0]
+    for sp in specs:
+        first.append(first[-1] + OT.count_quant_blocks([sp]))
+    sc_bits = tensor_bits(scales)
+    wanted = _quant_bands(w, plan)
+    n_tiles = sum(OT.count_quant_blocks([oracle_pool._band_spec(specs[i], r0, r1)])
+                  for i, b in wanted.items() for r0, r1 in b)
+    print(f"  quant: comparing {n_tiles} tiles of {len(wanted)} tensors with the oracle "
+          f"({'all' if idx == 1 else 'stratified'})", flush=True)
+    jobs = oracle_pool.band_jobs(idx, tile_major, w.quant, wanted)
+    done = 0
+    for i, results in oracle_pool.run(jobs):
+        sp, s = specs[i], plan.starts[i]
+        tpr = -(-sp.cols // sp.p1)
+        g_rows = gathered[i].view(sp.rows, sp.cols)
+        for r0, r1, want_q, want_sc, want_g in results:
+            got_q = tensor_bits(q[s + r0 * sp.cols: s + r1 * sp.cols])
+            assert np.array_equal(got_q, want_q), f"quant {sp.name} rows {r0}-{r1}"
+            b0 = first[i] + (r0 // sp.p0) * tpr
+            assert np.array_equal(sc_bits[b0: b0 + want_sc.size], want_sc), f"scales {sp.name} rows {r0}-{r1}"
+            assert np.array_equal(tensor_bits(g_rows[r0:r1]), want_g), f"unpack-dequant {sp.name} rows {r0}-{r1}"
+            done += OT.count_quant_blocks([oracle_pool._band_spec(sp, r0, r1)])
+    assert done == n_tiles
+    print(f"  quant, scales and unpack-dequant match on all {n_tiles} tiles", flush=True)
 
 
 @pytest.mark.parametrize("idx,tile_major", [(1, False), (2, False), (3, False), (1, True)])
@@ -117,25 +181,7 @@ def test_param_and_grad_workloads(gpu_lib, idx, tile_major):
         print("  bf16 pack matches on the same tensors; padding zero", flush=True)
 
     if w.quant:
-        first = [0]
-        for sp in specs:
-            first.append(first[-1] + OT.count_quant_blocks([sp]))
-        sc_bits = tensor_bits(scales)
-        for i in sample[: min(len(sample), 6)]:
-            s, n = plan.starts[i], plan.numels[i]
-            lay = OP.layout_offsets(specs[i])
-            x = np.empty(n, np.float32)
-            x[lay] = _tensor_param_f32(inp, i)           # the tensor's interval order
-            elem = np.empty(n, np.int64)
-            elem[lay] = np.arange(n)                     # interval position -> row-major element
-            got_q = tensor_bits(q[s: s + n])
-            got_g = tensor_bits(gathered[i]).ravel() if gathered[i] is not None else None
-            for _, b, pos in OT.quant_blocks([specs[i]], [0]):
-                c, sc = OT.quantize_block(x[pos], w.quant)
-                assert np.array_equal(got_q[pos], c), f"quant {i} block {b}"
-                assert sc_bits[first[i] + b] == np.float32(sc).view(np.uint32), f"scale {i} block {b}"
-                want_g = OT.bf16_round(OT.dequant_values(c, sc, w.quant))
-                assert np.array_equal(got_g[elem[pos]], want_g), f"unpack-dequant {i} block {b}"
+        _check_quant_full_size(w, idx, tile_major, plan, q, scales, gathered)
         _zero_everywhere(q, OP.padding_ranges([sp for sp in specs if sp.kind in ("TILE", "TILEMAJOR", "FLAT")],
                                               [st for sp, st in zip(specs, plan.starts)
                                                if sp.kind in ("TILE", "TILEMAJOR", "FLAT")], S, R))
