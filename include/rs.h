@@ -216,8 +216,9 @@ int rs_pack_scatter(rs_plan* plan, const void* const* src, int32_t src_dt,
                     float scale, void* stream);
 
 /* Block-wise quantisation of every locally whole block (feynmanwiki
- * walkthrough: a quantisation block should live on one device because its
- * values share scale metadata; the 8-bit Adam paragraph). For each block B
+ * walkthrough, block-quantisation paragraph: all codes of a block depend on
+ * one per-block scale, so a rank boundary must never split a block; and the
+ * 8-bit Adam paragraph). For each block B
  * (a br x bc tile of a TILE tensor, partial at the edges, or a b-element
  * block of a FLAT tensor):
  *   amax = max |x| over B;  Q = 448 (RS_E4M3), 127 (RS_I8), 255 (RS_U8);

@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 The pages run 8-bit Adam on RaggedShard ([walk], 8-bit Adam paragraph:
 optimizer statistics quantised in blocks that stay whole on their device, so
-each device quantises its own state without exchanging scale metadata) but
+no device needs another device's block scales to requantise its part) but
 give no update formula. Reading: the decoupled-weight-decay Adam update
 (AdamW), applied to every element of every quantisation block of the plan,
 with the state kept as block-quantised codes:

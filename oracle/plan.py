@@ -32,8 +32,8 @@ notes):
     per order.
   * Choice among orders: smallest S, then the smallest end max(s_i + n_i),
     then the order listed first.
-  * Feasibility for a fixed order and S ([walk], "for a candidate per-device
-    size"): the pages' DP f(i, j) counts the shards needed to place the
+  * Feasibility for a fixed order and S ([walk], the candidate-size
+    paragraph): the pages' DP f(i, j) counts the shards needed to place the
     tensors before T_i and the first j blocks of T_i. Because T_i is
     contiguous, its placement is decided by s_i alone, and the constraint on
     s_i does not depend on the other tensors; so placing each tensor at its

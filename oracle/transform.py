@@ -24,8 +24,8 @@ Readings (listed in the design notes):
   * Layouts: a tensor occupies [s_i, s_i + n_i); element (r, c) sits at
     s_i + r*cols + c, except for TILEMAJOR tensors, stored tile by tile
     (tile-row-major, each tile row-major inside). Unpack and pack apply that
-    reordering ([walk], RaggedShard paragraphs: 2-D blocks distributed
-    asymmetrically across devices).
+    reordering ([walk], RaggedShard paragraphs: 2-D blocks may be spread
+    unevenly over the devices).
   * Per block: amax = max |x| (exact). If amax > 0 the stored scale is
     fl32(amax / Q) and values are multiplied by r = min(fl32(Q / amax),
     FLT_MAX) before encoding (one correctly rounded division per block; the

@@ -238,6 +238,13 @@ def _count_check(plan: Plan, items, what: str):
         raise ValueError(f"{what}: {len(items)} entries for a plan of {len(plan.numels)} tensors")
 
 
+def _scales_check(plan: Plan, scales: torch.Tensor):
+    """The kernels read n_qblocks fp32 scales: a tensor of another dtype with that many
+    entries would be read past its end."""
+    if scales.dtype != torch.float32 or scales.numel() < plan.n_qblocks:
+        raise ValueError("scales: fp32 with n_qblocks entries")
+
+
 def _dev_check(plan: Plan, *tensors):
     for t in tensors:
         if t is None:
@@ -288,13 +295,12 @@ def rs_pack_scatter(plan: Plan, srcs: List[torch.Tensor], packed: torch.Tensor,
 
 def rs_block_quant(plan: Plan, src: torch.Tensor, q: torch.Tensor, fmt: str, scales: torch.Tensor):
     """Per-block absmax codes (fmt "e4m3" | "i8" | "u8") of the flat buffer, plus fp32 scales."""
+    _scales_check(plan, scales)
     _dev_check(plan, src, q, scales)
     if src.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("src is fp32 or bf16")
     if src.numel() < plan.R_mat * plan.S or q.numel() * q.element_size() < plan.R_mat * plan.S:
         raise ValueError("src / q shorter than R_mat * S")
-    if scales.dtype != torch.float32 or scales.numel() < plan.n_qblocks:
-        raise ValueError("scales: fp32 with n_qblocks entries")
     _check(load().rs_block_quant(plan.handle, src.data_ptr(),
                                  RS_F32 if src.dtype == torch.float32 else RS_BF16, q.data_ptr(),
                                  CODE_FORMATS[fmt], scales.data_ptr(), _stream(plan.device)))
@@ -302,6 +308,7 @@ def rs_block_quant(plan: Plan, src: torch.Tensor, q: torch.Tensor, fmt: str, sca
 
 def rs_block_dequant(plan: Plan, q: torch.Tensor, fmt: str, scales: torch.Tensor, out: torch.Tensor):
     """out <- code value * block scale inside blocks, +0.0 elsewhere."""
+    _scales_check(plan, scales)
     _dev_check(plan, q, scales, out)
     if out.dtype != torch.float32 or out.numel() < plan.R_mat * plan.S:
         raise ValueError("out: fp32 with R_mat * S entries")
@@ -315,6 +322,7 @@ def rs_unpack_dequant(plan: Plan, q: torch.Tensor, fmt: str, scales: torch.Tenso
                       dsts: List[Optional[torch.Tensor]]):
     """dst_i <- fl32(code value * block scale) (rounded to bf16 for bf16 tensors) for every
     quantised tensor; entries for other tensors may be None."""
+    _scales_check(plan, scales)
     _count_check(plan, dsts, "dsts")
     _dev_check(plan, q, scales, *[d for d in dsts if d is not None])
     if q.numel() * q.element_size() < plan.R_mat * plan.S or scales.numel() < plan.n_qblocks:

@@ -219,6 +219,24 @@ def test_binding_rejects_gradients_of_another_dtype(rs):
         binding.rs_pack_scatter(plan, [torch.zeros(16, dtype=torch.float16)], torch.zeros(16))
 
 
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16", "int32", "float64"])
+def test_binding_rejects_scales_of_another_dtype(rs, dtype):
+    """Every call that reads or writes scales takes n_qblocks fp32 values: a scales tensor of
+    another dtype with n_qblocks entries would be read or written past its end."""
+    import torch
+    from structure_aware_grouped_amd import binding
+    plan = binding.Plan.__new__(binding.Plan)
+    plan._h, plan.numels, plan.device, plan.R_mat, plan.S, plan.n_qblocks = None, [64], 0, 1, 64, 4
+    plan.specs = [TensorSpec("t", 8, 8, "TILE", 4, 4)]
+    sc = torch.zeros(4, dtype=getattr(torch, dtype))
+    q = torch.zeros(64, dtype=torch.uint8)
+    for call in (lambda: binding.rs_block_quant(plan, torch.zeros(64), q, "e4m3", sc),
+                 lambda: binding.rs_block_dequant(plan, q, "e4m3", sc, torch.zeros(64)),
+                 lambda: binding.rs_unpack_dequant(plan, q, "e4m3", sc, [torch.zeros(8, 8)])):
+        with pytest.raises(ValueError, match="scales: fp32"):
+            call()
+
+
 def _llama70b_model(layers):
     specs = []
     for l in range(layers):

@@ -48,3 +48,14 @@ def test_the_check_catches_a_missing_name(tmp_path):
     p.write_text("import os\n\ndef f():\n    return Missing(os.sep)\n")
     rel = os.path.relpath(p, ROOT)
     assert _undefined(rel) == ["f:Missing"]
+
+
+def test_bench_and_product_do_not_import_the_test_tree():
+    """bench.py, the package and the input generators take nothing from tests/."""
+    import re
+    paths = ["bench.py", "__graft_entry__.py"]
+    for d in ("structure_aware_grouped_amd", "workloads"):
+        paths += [os.path.join(d, f) for f in os.listdir(os.path.join(ROOT, d)) if f.endswith(".py")]
+    for p in paths:
+        src = open(os.path.join(ROOT, p)).read()
+        assert not re.search(r"^\s*(from|import)\s+tests\b", src, re.M), p

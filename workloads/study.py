@@ -2,7 +2,7 @@
 
 One FSDP group per decoder layer, from the public architectures the pages
 evaluate padding on (walkthrough, the ablation paragraph on planner padding:
-DeepSeek-V3-671B and GPT-OSS-120B at 1x / 16x / 128x row granularity):
+GPT-OSS-120B and DeepSeek-V3-671B, at 1x / 16x / 128x row granularity):
 
 * GPT-OSS-120B: hidden 2880, 64 query heads and 8 key-value heads of width
   64, attention projections with biases, learned attention sinks, 128 experts
