@@ -21,60 +21,6 @@ thread_local std::string g_error;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Checks a plan against the constraints; fills the tensor table.
-int validate(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S, const int64_t* starts,
-             int64_t R_mat, std::vector<Tensor>* out, int64_t* R_used) {
-  if (!specs || !starts) return fail(RS_EINVAL, "rs_plan_load: null specs or starts");
-  if (n < 1 || n > (int64_t(1) << 31)) return fail(RS_EINVAL, "rs_plan_load: bad tensor count");
-  if (V < 1) return fail(RS_EINVAL, "rs_plan_load: V must be >= 1");
-  if (S <= 0) return fail(RS_EINVAL, "rs_plan_load: S must be > 0");
-  if (S % 16 != 0) return fail(RS_EALIGN, "rs_plan_load: S must be a multiple of 16");
-  const int64_t kLimit = int64_t(1) << 62;
-  if (V > kLimit / S) return fail(RS_ERANGE, "rs_plan_load: V * S overflows");
-  const int64_t total = V * S;
-
-  out->resize(n);
-  std::vector<std::pair<int64_t, int64_t>> iv(n);
-  int64_t max_end = 0;
-  for (int64_t i = 0; i < n; ++i) {
-    std::string why;
-    if (!spec_ok(specs[i], &why))
-      return fail(RS_EINVAL, "rs_plan_load: tensor " + std::to_string(i) + ": " + why);
-    Tensor& t = (*out)[i];
-    t.rows = specs[i].rows;
-    t.cols = specs[i].cols;
-    t.n = t.rows * t.cols;
-    t.g = granularity(specs[i]);
-    t.kind = specs[i].kind;
-    t.p0 = specs[i].p0;
-    t.p1 = specs[i].p1;
-    t.start = starts[i];
-    const std::string tag = "rs_plan_load: tensor " + std::to_string(i);
-    if (t.start % 16 != 0) return fail(RS_EALIGN, tag + ": start not a multiple of 16");
-    if (t.start < 0 || t.start > total - t.n)
-      return fail(RS_EPLAN, tag + ": interval outside [0, V*S)");
-    // rank boundaries strictly inside the tensor: the first one at b, then every S
-    const int64_t b = (t.start / S + 1) * S;
-    if (b < t.start + t.n) {
-      if ((b - t.start) % t.g != 0) return fail(RS_EPLAN, tag + ": a rank boundary cuts an atomic block");
-      if (b + S < t.start + t.n && S % t.g != 0)
-        return fail(RS_EPLAN, tag + ": a rank boundary cuts an atomic block");
-    }
-    iv[i] = {t.start, t.start + t.n};
-    max_end = std::max(max_end, t.start + t.n);
-  }
-  std::sort(iv.begin(), iv.end());
-  for (int64_t i = 1; i < n; ++i)
-    if (iv[i].first < iv[i - 1].second) return fail(RS_EPLAN, "rs_plan_load: tensors overlap");
-  *R_used = (max_end + S - 1) / S;
-  if (R_mat < *R_used || R_mat > V)
-    return fail(RS_ERANGE, "rs_plan_load: R_mat must lie in [R_used, V] (R_used = " +
-                               std::to_string(*R_used) + ")");
-  if (R_mat > kMaxElems / S)
-    return fail(RS_ERANGE, "rs_plan_load: R_mat * S exceeds 2^39 elements, more than one device holds");
-  return RS_OK;
-}
-
 struct Tables {
   std::vector<TmJob> tm;
   std::vector<CopyChunk> unpack;
@@ -216,99 +162,16 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   tb->padding = top - covered;
 
   // quant / dequant: tiles and flat blocks in scale order, then zero ranges
-  int64_t q = 0;
-  for (int64_t ti = 0; ti < n; ++ti) {
-    const Tensor& x = t[ti];
-    if (x.kind == RS_TILE) {
-      // a code row of one tile then starts or ends inside a 128-byte line that
-      // the tile next to it also writes
-      if (x.cols > x.p1 && ((x.start | x.cols | x.p1) & 127) != 0) tb->split_code_lines = true;
-      for (int64_t r0 = 0; r0 < x.rows; r0 += x.p0) {
-        for (int64_t c0 = 0; c0 < x.cols; c0 += x.p1) {
-          QJob j{};
-          j.base = x.start + r0 * x.cols + c0;
-          j.stride = x.cols;
-          j.scale = q++;
-          j.rows = static_cast<int32_t>(std::min(x.p0, x.rows - r0));
-          j.cols = static_cast<int32_t>(std::min(x.p1, x.cols - c0));
-          j.kind = QJOB_TILE;
-          j.last = 0;
-          j.tensor = static_cast<int32_t>(ti);
-          j.toff = j.base - x.start;
-          j.tstride = x.cols;
-          tb->qjobs.push_back(j);
-          const int64_t v16 = int64_t(j.rows) * ((int64_t(j.cols) * 4 + 15) / 16);
-          tb->max_tile_vec16 = static_cast<int32_t>(std::max<int64_t>(tb->max_tile_vec16, std::min<int64_t>(v16, 1 << 30)));
-        }
-      }
-    } else if (x.kind == RS_TILEMAJOR) {
-      const int64_t br = x.p0, bc = x.p1, ntc = x.cols / bc;
-      for (int64_t tr = 0; tr < x.rows / br; ++tr) {
-        for (int64_t tc = 0; tc < ntc; ++tc) {
-          QJob j{};
-          j.base = x.start + (tr * ntc + tc) * br * bc;   // the tile is contiguous
-          j.stride = bc;
-          j.scale = q++;
-          j.rows = static_cast<int32_t>(br);
-          j.cols = static_cast<int32_t>(bc);
-          j.kind = QJOB_TILE;
-          j.last = 0;
-          j.tensor = static_cast<int32_t>(ti);
-          j.toff = tr * br * x.cols + tc * bc;
-          j.tstride = x.cols;
-          tb->qjobs.push_back(j);
-        }
-      }
-    } else if (x.kind == RS_FLAT) {
-      const int64_t nblk = (x.n + x.p0 - 1) / x.p0;
-      for (int64_t b0 = 0; b0 < nblk; b0 += kFlatPerGroup) {
-        const int64_t cnt = std::min<int64_t>(kFlatPerGroup, nblk - b0);
-        QJob j{};
-        j.base = x.start + b0 * x.p0;
-        j.stride = x.p0;
-        j.scale = q;
-        j.rows = static_cast<int32_t>(cnt);
-        j.cols = static_cast<int32_t>(x.p0);
-        j.kind = QJOB_FLAT;
-        j.last = static_cast<int32_t>(std::min(x.p0, x.n - (b0 + cnt - 1) * x.p0));
-        j.tensor = static_cast<int32_t>(ti);
-        j.toff = j.base - x.start;
-        j.tstride = x.p0;
-        tb->qjobs.push_back(j);
-        q += cnt;
-      }
-    }
-  }
-  tb->n_qblocks = q;
-  assert(q == first_scale[n]);
-  std::vector<std::pair<int64_t, int64_t>> qiv;
-  for (const Tensor& x : t)
-    if (x.kind == RS_TILE || x.kind == RS_FLAT || x.kind == RS_TILEMAJOR) qiv.push_back({x.start, x.start + x.n});
-  std::sort(qiv.begin(), qiv.end());
-  auto zero = [&](int64_t from, int64_t to) {
-    for (int64_t p = from; p < to; p += kZeroChunk) {
-      QJob j{};
-      j.base = p;
-      j.stride = std::min(kZeroChunk, to - p);
-      j.kind = QJOB_ZERO;
-      j.tensor = -1;
-      tb->qjobs.push_back(j);
-    }
-  };
-  pos = 0;
-  for (auto& r : qiv) {
-    zero(pos, r.first);
-    pos = r.second;
-  }
-  zero(pos, top);
-  // one kernel per job kind: keep each kind contiguous
-  std::stable_sort(tb->qjobs.begin(), tb->qjobs.end(),
-                   [](const QJob& a, const QJob& b) { return a.kind < b.kind; });
-  for (const QJob& j : tb->qjobs) {
-    if (j.kind == QJOB_TILE) ++tb->n_qtile;
-    else if (j.kind == QJOB_FLAT) ++tb->n_qflat;
-    else ++tb->n_qzero;
-  }
+  QuantList ql;
+  lower_quant(t, top, &ql);
+  tb->qjobs = std::move(ql.jobs);
+  tb->n_qtile = ql.n_tile;
+  tb->n_qflat = ql.n_flat;
+  tb->n_qzero = ql.n_zero;
+  tb->n_qblocks = ql.n_blocks;
+  tb->max_tile_vec16 = ql.max_tile_vec16;
+  tb->split_code_lines = ql.split_code_lines;
+  assert(tb->n_qblocks == first_scale[n]);
 
   // gather side: contiguous row runs where every 16-element vector has one
   // scale; per-block jobs (as for quant) for everything else
@@ -330,6 +193,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     if (groups[ti].unit) used.push_back(groups[ti]);
   }
   const int64_t P = pick_run_pieces(used, pc8);
+  int64_t q = 0;
   {
     int64_t runs = 0, m8 = 0, m4 = 0;
     for (const RunGroups& g : used) {
@@ -339,7 +203,6 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
     tb->gather_split8 = m8;
     tb->gather_split4 = m4;
   }
-  q = 0;
   for (int64_t ti = 0; ti < n; ++ti) {
     const Tensor& x = t[ti];
     if (x.kind == RS_TILE) {
@@ -425,6 +288,165 @@ int fail(int status, const std::string& msg) {
 
 void clear_error() { g_error.clear(); }
 
+// Checks a plan against the constraints; fills the tensor table. Messages
+// start with `who`, the entry point that was called.
+int validate_plan(const char* who, const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,
+                  const int64_t* starts, int64_t R_mat, std::vector<Tensor>* out, int64_t* R_used) {
+  const std::string w = who;
+  if (!specs || !starts) return fail(RS_EINVAL, w + ": null specs or starts");
+  if (n < 1 || n > (int64_t(1) << 31)) return fail(RS_EINVAL, w + ": bad tensor count");
+  if (V < 1) return fail(RS_EINVAL, w + ": V must be >= 1");
+  if (S <= 0) return fail(RS_EINVAL, w + ": S must be > 0");
+  if (S % 16 != 0) return fail(RS_EALIGN, w + ": S must be a multiple of 16");
+  const int64_t kLimit = int64_t(1) << 62;
+  if (V > kLimit / S) return fail(RS_ERANGE, w + ": V * S overflows");
+  const int64_t total = V * S;
+
+  out->resize(n);
+  std::vector<std::pair<int64_t, int64_t>> iv(n);
+  int64_t max_end = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    std::string why;
+    if (!spec_ok(specs[i], &why))
+      return fail(RS_EINVAL, w + ": tensor " + std::to_string(i) + ": " + why);
+    Tensor& t = (*out)[i];
+    t.rows = specs[i].rows;
+    t.cols = specs[i].cols;
+    t.n = t.rows * t.cols;
+    t.g = granularity(specs[i]);
+    t.kind = specs[i].kind;
+    t.p0 = specs[i].p0;
+    t.p1 = specs[i].p1;
+    t.start = starts[i];
+    const std::string tag = w + ": tensor " + std::to_string(i);
+    if (t.start % 16 != 0) return fail(RS_EALIGN, tag + ": start not a multiple of 16");
+    if (t.start < 0 || t.start > total - t.n)
+      return fail(RS_EPLAN, tag + ": interval outside [0, V*S)");
+    // rank boundaries strictly inside the tensor: the first one at b, then every S
+    const int64_t b = (t.start / S + 1) * S;
+    if (b < t.start + t.n) {
+      if ((b - t.start) % t.g != 0) return fail(RS_EPLAN, tag + ": a rank boundary cuts an atomic block");
+      if (b + S < t.start + t.n && S % t.g != 0)
+        return fail(RS_EPLAN, tag + ": a rank boundary cuts an atomic block");
+    }
+    iv[i] = {t.start, t.start + t.n};
+    max_end = std::max(max_end, t.start + t.n);
+  }
+  std::sort(iv.begin(), iv.end());
+  for (int64_t i = 1; i < n; ++i)
+    if (iv[i].first < iv[i - 1].second) return fail(RS_EPLAN, w + ": tensors overlap");
+  *R_used = (max_end + S - 1) / S;
+  if (R_mat < *R_used || R_mat > V)
+    return fail(RS_ERANGE, w + ": R_mat must lie in [R_used, V] (R_used = " +
+                               std::to_string(*R_used) + ")");
+  if (R_mat > kMaxElems / S)
+    return fail(RS_ERANGE, w + ": R_mat * S exceeds 2^39 elements, more than one device holds");
+  return RS_OK;
+}
+
+// Quant / dequant work list of a validated plan over [0, top): one job per
+// tile (TILE: a br x bc tile of the row-major tensor, partial at the edges;
+// TILEMAJOR: one contiguous tile) and per group of up to kFlatPerGroup flat
+// blocks, in scale order (tensors in spec order, tiles row-major), then
+// zero-range jobs for every position outside all blocks; the list is sorted
+// by job kind (stable), so each kind is one contiguous run for its kernel.
+void lower_quant(const std::vector<Tensor>& t, int64_t top, QuantList* ql) {
+  const int64_t n = static_cast<int64_t>(t.size());
+  int64_t q = 0;
+  for (int64_t ti = 0; ti < n; ++ti) {
+    const Tensor& x = t[ti];
+    if (x.kind == RS_TILE) {
+      // a code row of one tile then starts or ends inside a 128-byte line that
+      // the tile next to it also writes
+      if (x.cols > x.p1 && ((x.start | x.cols | x.p1) & 127) != 0) ql->split_code_lines = true;
+      for (int64_t r0 = 0; r0 < x.rows; r0 += x.p0) {
+        for (int64_t c0 = 0; c0 < x.cols; c0 += x.p1) {
+          QJob j{};
+          j.base = x.start + r0 * x.cols + c0;
+          j.stride = x.cols;
+          j.scale = q++;
+          j.rows = static_cast<int32_t>(std::min(x.p0, x.rows - r0));
+          j.cols = static_cast<int32_t>(std::min(x.p1, x.cols - c0));
+          j.kind = QJOB_TILE;
+          j.last = 0;
+          j.tensor = static_cast<int32_t>(ti);
+          j.toff = j.base - x.start;
+          j.tstride = x.cols;
+          ql->jobs.push_back(j);
+          const int64_t v16 = int64_t(j.rows) * ((int64_t(j.cols) * 4 + 15) / 16);
+          ql->max_tile_vec16 = static_cast<int32_t>(std::max<int64_t>(ql->max_tile_vec16, std::min<int64_t>(v16, 1 << 30)));
+        }
+      }
+    } else if (x.kind == RS_TILEMAJOR) {
+      const int64_t br = x.p0, bc = x.p1, ntc = x.cols / bc;
+      for (int64_t tr = 0; tr < x.rows / br; ++tr) {
+        for (int64_t tc = 0; tc < ntc; ++tc) {
+          QJob j{};
+          j.base = x.start + (tr * ntc + tc) * br * bc;   // the tile is contiguous
+          j.stride = bc;
+          j.scale = q++;
+          j.rows = static_cast<int32_t>(br);
+          j.cols = static_cast<int32_t>(bc);
+          j.kind = QJOB_TILE;
+          j.last = 0;
+          j.tensor = static_cast<int32_t>(ti);
+          j.toff = tr * br * x.cols + tc * bc;
+          j.tstride = x.cols;
+          ql->jobs.push_back(j);
+        }
+      }
+    } else if (x.kind == RS_FLAT) {
+      const int64_t nblk = (x.n + x.p0 - 1) / x.p0;
+      for (int64_t b0 = 0; b0 < nblk; b0 += kFlatPerGroup) {
+        const int64_t cnt = std::min<int64_t>(kFlatPerGroup, nblk - b0);
+        QJob j{};
+        j.base = x.start + b0 * x.p0;
+        j.stride = x.p0;
+        j.scale = q;
+        j.rows = static_cast<int32_t>(cnt);
+        j.cols = static_cast<int32_t>(x.p0);
+        j.kind = QJOB_FLAT;
+        j.last = static_cast<int32_t>(std::min(x.p0, x.n - (b0 + cnt - 1) * x.p0));
+        j.tensor = static_cast<int32_t>(ti);
+        j.toff = j.base - x.start;
+        j.tstride = x.p0;
+        ql->jobs.push_back(j);
+        q += cnt;
+      }
+    }
+  }
+  ql->n_blocks = q;
+  std::vector<std::pair<int64_t, int64_t>> qiv;
+  for (const Tensor& x : t)
+    if (x.kind == RS_TILE || x.kind == RS_FLAT || x.kind == RS_TILEMAJOR) qiv.push_back({x.start, x.start + x.n});
+  std::sort(qiv.begin(), qiv.end());
+  auto zero = [&](int64_t from, int64_t to) {
+    for (int64_t p = from; p < to; p += kZeroChunk) {
+      QJob j{};
+      j.base = p;
+      j.stride = std::min(kZeroChunk, to - p);
+      j.kind = QJOB_ZERO;
+      j.tensor = -1;
+      ql->jobs.push_back(j);
+    }
+  };
+  int64_t pos = 0;
+  for (auto& r : qiv) {
+    zero(pos, r.first);
+    pos = r.second;
+  }
+  zero(pos, top);
+  // one kernel per job kind: keep each kind contiguous
+  std::stable_sort(ql->jobs.begin(), ql->jobs.end(),
+                   [](const QJob& a, const QJob& b) { return a.kind < b.kind; });
+  for (const QJob& j : ql->jobs) {
+    if (j.kind == QJOB_TILE) ++ql->n_tile;
+    else if (j.kind == QJOB_FLAT) ++ql->n_flat;
+    else ++ql->n_zero;
+  }
+}
+
+
 }  // namespace rs
 
 using namespace rs;
@@ -463,7 +485,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     if (device < 0) return fail(RS_EINVAL, "rs_plan_load: bad device");
     std::vector<Tensor> t;
     int64_t R_used = 0;
-    int st = validate(specs, n, V, S, starts, R_mat, &t, &R_used);
+    int st = validate_plan("rs_plan_load", specs, n, V, S, starts, R_mat, &t, &R_used);
     if (st != RS_OK) return st;
 
     Tables tb;

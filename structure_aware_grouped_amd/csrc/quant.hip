@@ -308,41 +308,54 @@ using namespace rs;
 
 namespace {
 
+// What one quant call launches: the job list (tiles, then flat groups, then
+// zero ranges) in device memory, and the launch limits.
+struct QuantLaunch {
+  const QJob* jobs;
+  int64_t n_tile, n_flat, n_zero;
+  bool split_code_lines;
+  int64_t max_grid;
+};
+
+dim3 grid_for(const QuantLaunch& L, int64_t n_items) {
+  return dim3(static_cast<unsigned>(std::min<int64_t>(n_items, L.max_grid)));
+}
+
 // The zero-range jobs follow the flat groups, which follow the tiles: they ride
 // at the end of the last launch that has blocks, or get their own launch.
 template <bool BF16, int FMT, bool HW>
-void launch_quant_kinds(const rs_plan* p, const void* src, uint8_t* q, float* scales, hipStream_t s) {
+void launch_quant_kinds(const QuantLaunch& L, const void* src, uint8_t* q, float* scales, hipStream_t s) {
   const dim3 block(kThreads);
-  const QJob* tiles = p->qjobs;
-  const QJob* flats = tiles + p->n_qtile;
-  const int64_t nz = p->n_qzero;
-  if (p->n_qtile) {
-    const int64_t n = p->n_qtile + (p->n_qflat ? 0 : nz);
-    if (p->split_code_lines)
-      hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW, kTileXcdGroupSplit>), grid_of(p, n), dim3(kQuantThreads), 0,
-                         s, tiles, p->n_qtile, src, q, scales, static_cast<unsigned>(n));
+  const QJob* tiles = L.jobs;
+  const QJob* flats = tiles + L.n_tile;
+  const int64_t nz = L.n_zero;
+  if (L.n_tile) {
+    const int64_t n = L.n_tile + (L.n_flat ? 0 : nz);
+    if (L.split_code_lines)
+      hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW, kTileXcdGroupSplit>), grid_for(L, n), dim3(kQuantThreads), 0,
+                         s, tiles, L.n_tile, src, q, scales, static_cast<unsigned>(n));
     else
-      hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW, kTileXcdGroup>), grid_of(p, n), dim3(kQuantThreads), 0, s,
-                         tiles, p->n_qtile, src, q, scales, static_cast<unsigned>(n));
+      hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW, kTileXcdGroup>), grid_for(L, n), dim3(kQuantThreads), 0, s,
+                         tiles, L.n_tile, src, q, scales, static_cast<unsigned>(n));
   }
-  if (p->n_qflat)
-    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), grid_of(p, p->n_qflat + nz), dim3(kFlatThreads), 0, s, flats,
-                       p->n_qflat, src, q, scales, static_cast<unsigned>(p->n_qflat + nz));
-  if (!p->n_qtile && !p->n_qflat && nz)
-    hipLaunchKernelGGL(zero_codes_kernel, grid_of(p, nz), block, 0, s, flats, q, static_cast<unsigned>(nz));
+  if (L.n_flat)
+    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), grid_for(L, L.n_flat + nz), dim3(kFlatThreads), 0, s, flats,
+                       L.n_flat, src, q, scales, static_cast<unsigned>(L.n_flat + nz));
+  if (!L.n_tile && !L.n_flat && nz)
+    hipLaunchKernelGGL(zero_codes_kernel, grid_for(L, nz), block, 0, s, flats, q, static_cast<unsigned>(nz));
 }
 
 template <bool BF16>
-void launch_quant(const rs_plan* p, const void* src, int fmt, bool hw, uint8_t* q, float* scales,
+void launch_quant(const QuantLaunch& L, const void* src, int fmt, bool hw, uint8_t* q, float* scales,
                   hipStream_t s) {
   if (fmt == FMT_E4M3 && hw)
-    launch_quant_kinds<BF16, FMT_E4M3, true>(p, src, q, scales, s);
+    launch_quant_kinds<BF16, FMT_E4M3, true>(L, src, q, scales, s);
   else if (fmt == FMT_E4M3)
-    launch_quant_kinds<BF16, FMT_E4M3, false>(p, src, q, scales, s);
+    launch_quant_kinds<BF16, FMT_E4M3, false>(L, src, q, scales, s);
   else if (fmt == FMT_I8)
-    launch_quant_kinds<BF16, FMT_I8, false>(p, src, q, scales, s);
+    launch_quant_kinds<BF16, FMT_I8, false>(L, src, q, scales, s);
   else
-    launch_quant_kinds<BF16, FMT_U8, false>(p, src, q, scales, s);
+    launch_quant_kinds<BF16, FMT_U8, false>(L, src, q, scales, s);
 }
 
 template <int FMT, bool HW>
@@ -379,10 +392,11 @@ extern "C" int rs_block_quant(rs_plan* p, const void* src, int32_t src_dt, void*
   if (!aligned16(src) || !aligned16(q)) return fail(RS_EALIGN, std::string(who) + ": src / q not 16-byte aligned");
   if (p->n_qjobs == 0) return RS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const QuantLaunch L{p->qjobs, p->n_qtile, p->n_qflat, p->n_qzero, p->split_code_lines, p->max_grid};
   if (src_dt == RS_BF16)
-    launch_quant<true>(p, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
+    launch_quant<true>(L, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
   else
-    launch_quant<false>(p, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
+    launch_quant<false>(L, src, fmt, p->e4m3_hw, static_cast<uint8_t*>(q), scales, s);
   return launched(who);
 }
 

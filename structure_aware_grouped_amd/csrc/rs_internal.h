@@ -273,6 +273,21 @@ struct PtrTable {
 int64_t granularity(const rs_tensor_spec& s);
 bool spec_ok(const rs_tensor_spec& s, std::string* why);
 
+// Checks a plan (the arguments of rs_plan_load) against the layout
+// constraints and fills the tensor table; returns an rs_status, with a
+// message that starts with `who` (the entry point called).
+int validate_plan(const char* who, const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,
+                  const int64_t* starts, int64_t R_mat, std::vector<Tensor>* out, int64_t* R_used);
+
+// The block quant / dequant work list of a validated plan.
+struct QuantList {
+  std::vector<QJob> jobs;   // tiles, then flat groups, then zero ranges
+  int64_t n_tile = 0, n_flat = 0, n_zero = 0, n_blocks = 0;
+  int32_t max_tile_vec16 = 0;     // largest tile, in 16-byte vectors of 4-byte input
+  bool split_code_lines = false;  // neighbouring tiles share 128-byte lines of codes
+};
+void lower_quant(const std::vector<Tensor>& t, int64_t top, QuantList* ql);
+
 // Thread-local error reporting: record a message, return the status.
 int fail(int status, const std::string& msg);
 void clear_error();

@@ -7,7 +7,7 @@
 // prints "ok" or the first violation. With an argument 1-4 it first plants
 // one mistake in the lists (a pack chunk dropped, a quant job doubled, a
 // gather scale shifted, an unpack source shifted), which must be reported. This file includes plan.cpp so that it
-// can call the file-local validate() and lower(); link it with planner.cpp.
+// can call validate_plan() and the file-local lower(); link it with planner.cpp.
 #include "plan.cpp"
 
 #include <cstdio>
@@ -236,7 +236,7 @@ int main(int argc, char** argv) {
   }
   std::vector<Tensor> t;
   int64_t R_used = 0;
-  if (validate(specs.data(), n, V, S, starts.data(), R, &t, &R_used) != RS_OK) {
+  if (validate_plan("rs_plan_load", specs.data(), n, V, S, starts.data(), R, &t, &R_used) != RS_OK) {
     std::printf("invalid plan: %s\n", rs_last_error());
     return 0;
   }
