@@ -17,6 +17,8 @@
  *   rs_unpack_gathered  gathered flat buffer -> N full tensors
  *   rs_pack_scatter     N full gradients -> flat buffer, fused scale/add/zero
  *   rs_block_quant      per-block absmax 8-bit quantisation of the flat buffer
+ *   rs_block_quant_noalloc  the same from the plan as data, with its work list
+ *                       in static device memory (no allocation)
  *   rs_block_dequant    the inverse of rs_block_quant
  *   rs_unpack_dequant   gathered codes + scales -> the quantised full tensors
  *   rs_adam8_step       one AdamW step on block-quantised int8 / uint8 state
@@ -27,6 +29,8 @@
  *   - Device pointers come from the caller (e.g. torch tensors' data_ptr())
  *     and stay owned by the caller. The library owns rs_plan and the device
  *     tables it allocates once in rs_plan_load; no transform call allocates.
+ *     rs_block_quant_noalloc allocates nothing at all: its work list goes
+ *     into a static device array.
  *   - `stream` is a hipStream_t passed as void* (torch's current stream on
  *     ROCm). Transform calls are asynchronous and ordered on that stream.
  *   - Every check happens before any launch: on error nothing is enqueued,
@@ -237,6 +241,31 @@ int rs_pack_scatter(rs_plan* plan, const void* const* src, int32_t src_dt,
  * Errors: RS_EINVAL, RS_EALIGN, RS_EDTYPE, RS_EHIP. */
 int rs_block_quant(rs_plan* plan, const void* src, int32_t src_dt, void* q, int32_t q_dt,
                    float* scales, void* stream);
+
+/* Allocation-free variant of rs_block_quant, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * allocation). It takes the plan as data (the arguments of rs_plan_load)
+ * instead of a loaded plan: it validates the plan, builds the quant work list
+ * on the host and copies it into a static device array of 16 MiB that each GPU
+ * holds for the life of the process: at most 262,144 work items, one per
+ * tile, per pair of flat blocks and per 65,536 positions outside all blocks.
+ * It calls no hipMalloc, hipFree or other allocating HIP routine. Codes and
+ * scales equal those of rs_block_quant on the same plan, bit for bit.
+ * The work list is copied on `stream`, after the work already queued there,
+ * and the call waits for `stream` before it launches. Every call on one GPU
+ * shares that GPU's array: calls in order on one stream are safe; calls that
+ * may overlap on one GPU (other streams, other host threads) race, and the
+ * caller must serialise them.
+ * specs, n, V, S, starts, R_mat: as for rs_plan_load; the current device runs
+ * the call. src, src_dt, q, q_dt: as for rs_block_quant. scales: device fp32,
+ * scales_len entries, at least the plan's number of blocks.
+ * Errors: the plan's validation errors as for rs_plan_load, RS_EDTYPE,
+ * RS_EALIGN, RS_EINVAL (null buffer, scales too short), RS_ERANGE (work list
+ * larger than the static array: load the plan and call rs_block_quant),
+ * RS_EHIP. Nothing is launched on an error. */
+int rs_block_quant_noalloc(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,
+                           const int64_t* starts, int64_t R_mat, const void* src, int32_t src_dt,
+                           void* q, int32_t q_dt, float* scales, int64_t scales_len, void* stream);
 
 /* Inverse of rs_block_quant: out[p] = fl32(dec(q[p]) * scale[B]) inside
  * block B, +0.0 everywhere else in [0, R_mat*S). Arguments as in

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     load,
     rs_block_dequant,
     rs_block_quant,
+    rs_block_quant_noalloc,
     rs_pack_scatter,
     rs_plan_build,
     rs_plan_load,

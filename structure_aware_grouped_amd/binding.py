@@ -27,7 +27,7 @@ RS_F32, RS_BF16, RS_E4M3, RS_I8, RS_U8 = 0, 1, 2, 3, 4
 CODE_FORMATS = {"e4m3": RS_E4M3, "i8": RS_I8, "u8": RS_U8}
 EXPORTS = ("rs_plan_build", "rs_plan_load", "rs_plan_info", "rs_plan_free", "rs_unpack_gathered",
            "rs_pack_scatter", "rs_block_quant", "rs_block_dequant", "rs_unpack_dequant", "rs_adam8_step",
-           "rs_last_error")
+           "rs_last_error", "rs_block_quant_noalloc")
 
 
 class RsError(RuntimeError):
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rs_block_dequant.argtypes = [P, P, I32, P, P, P]
     lib.rs_unpack_dequant.argtypes = [P, P, I32, P, ctypes.POINTER(P), I32, P]
     lib.rs_adam8_step.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(AdamHParamsC), P]
+    lib.rs_block_quant_noalloc.argtypes = [ctypes.POINTER(TensorSpecC), I64, I64, I64, PI64, I64, P, I32, P, I32,
+                                           P, I64, P]
     lib.rs_last_error.argtypes = []
     lib.rs_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -358,3 +360,23 @@ def rs_adam8_step(plan: Plan, param: torch.Tensor, grad: torch.Tensor, q_m: torc
     hp = AdamHParamsC(lr, beta1, beta2, eps, weight_decay, 0, int(step))
     _check(load().rs_adam8_step(plan.handle, param.data_ptr(), grad.data_ptr(), q_m.data_ptr(), s_m.data_ptr(),
                                 q_v.data_ptr(), s_v.data_ptr(), ctypes.byref(hp), _stream(plan.device)))
+
+
+def rs_block_quant_noalloc(specs, V: int, S: int, starts: Sequence[int], R_mat: int, src: torch.Tensor,
+                           q: torch.Tensor, fmt: str, scales: torch.Tensor):
+    """rs_block_quant without a loaded plan and without any allocation on the device: the
+    plan is passed as data and its work list goes into the library's static device memory
+    (calls that overlap on one GPU race; calls in order on one stream do not)."""
+    if src.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("src is fp32 or bf16")
+    if scales.dtype != torch.float32:
+        raise ValueError("scales: fp32")
+    for t in (src, q, scales):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("src, q and scales are contiguous device tensors")
+    if src.numel() < R_mat * S or q.numel() * q.element_size() < R_mat * S:
+        raise ValueError("src / q shorter than R_mat * S")
+    _check(load().rs_block_quant_noalloc(specs_array(specs), len(specs), int(V), int(S), _i64(starts), int(R_mat),
+                                         src.data_ptr(), RS_F32 if src.dtype == torch.float32 else RS_BF16,
+                                         q.data_ptr(), CODE_FORMATS[fmt], scales.data_ptr(), scales.numel(),
+                                         _stream(src.device)))

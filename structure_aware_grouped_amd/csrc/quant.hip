@@ -10,6 +10,19 @@
 // reduction plus, for tiles, an LDS combine over the waves.
 #include "host_common.h"
 
+#include <cstdlib>
+#include <mutex>
+#include <vector>
+
+// Work-list memory of rs_block_quant_noalloc, for callers that cannot
+// allocate: a static device array, so the library never allocates for that
+// call. Each GPU the library runs on holds its own copy at its own address
+// until the process ends. In host code the array's name is only a host-side
+// stand-in: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kNoallocScratchBytes = int64_t(16) << 20;   // 262,144 work items of 64 bytes
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 namespace rs {
 namespace {
 
@@ -422,4 +435,92 @@ extern "C" int rs_block_dequant(rs_plan* p, const void* q, int32_t q_dt, const f
   else
     launch_dequant<FMT_U8, false>(p, qb, scales, out, s);
   return launched(who);
+}
+
+// ------------------------------------------------------------------ allocation-free quant
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on device `dev`, which is current; taken once per device.
+int scratch_on(int dev, void** out, const char* who) {
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(RS_EINVAL, std::string(who) + ": device index " + std::to_string(dev) + " out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RS_EHIP, std::string(who) + ": hipGetSymbolAddress of the work-list memory failed: " +
+                               hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RS_OK;
+}
+
+}  // namespace
+
+extern "C" int rs_block_quant_noalloc(const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,
+                                      const int64_t* starts, int64_t R_mat, const void* src, int32_t src_dt,
+                                      void* q, int32_t q_dt, float* scales, int64_t scales_len, void* stream) {
+  const char* who = "rs_block_quant_noalloc";
+  try {
+    clear_error();
+    if (src_dt != RS_F32 && src_dt != RS_BF16) return fail(RS_EDTYPE, std::string(who) + ": src must be fp32 or bf16");
+    const int fmt = fmt_of(q_dt);
+    if (fmt < 0) return fail(RS_EDTYPE, std::string(who) + ": code format must be E4M3, I8 or U8");
+    if (!src || !q) return fail(RS_EINVAL, std::string(who) + ": null buffer");
+    if (!aligned16(src) || !aligned16(q)) return fail(RS_EALIGN, std::string(who) + ": src / q not 16-byte aligned");
+    if (scales_len < 0) return fail(RS_EINVAL, std::string(who) + ": negative scales_len");
+    std::vector<Tensor> t;
+    int64_t R_used = 0;
+    int st = validate_plan(who, specs, n, V, S, starts, R_mat, &t, &R_used);
+    if (st != RS_OK) return st;
+    QuantList ql;
+    lower_quant(t, R_mat * S, &ql);
+    if (ql.n_blocks > scales_len || (ql.n_blocks > 0 && !scales))
+      return fail(RS_EINVAL, std::string(who) + ": the plan has " + std::to_string(ql.n_blocks) +
+                                 " quantisation blocks; scales holds " + std::to_string(scales ? scales_len : 0));
+    const int64_t bytes = static_cast<int64_t>(sizeof(QJob)) * static_cast<int64_t>(ql.jobs.size());
+    if (bytes > kNoallocScratchBytes)
+      return fail(RS_ERANGE, std::string(who) + ": the plan needs " + std::to_string(ql.jobs.size()) +
+                                 " quant work items (" + std::to_string(bytes) + " bytes); the static work-list "
+                                 "memory holds " + std::to_string(kNoallocScratchBytes / int64_t(sizeof(QJob))) +
+                                 " (" + std::to_string(kNoallocScratchBytes) + " bytes): use rs_plan_load and "
+                                 "rs_block_quant");
+    if (ql.jobs.empty()) return RS_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(RS_EHIP, std::string(who) + ": hipGetDevice failed");
+    void* ptr = nullptr;
+    st = scratch_on(dev, &ptr, who);
+    if (st != RS_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // The list goes in on the call's stream, after the work already queued there
+    // (a previous call on this stream may still be reading it). The copy reads this
+    // call's pageable host memory, so the call waits for it before returning.
+    if (hipMemcpyAsync(ptr, ql.jobs.data(), static_cast<size_t>(bytes), hipMemcpyHostToDevice, s) != hipSuccess)
+      return fail(RS_EHIP, std::string(who) + ": upload of the work list failed");
+    if (hipStreamSynchronize(s) != hipSuccess)
+      return fail(RS_EHIP, std::string(who) + ": waiting for the work-list upload failed");
+    const char* enc = std::getenv("RS_E4M3_ENCODER");
+    const bool hw = !(enc && std::strcmp(enc, "sw") == 0);
+    int64_t max_grid = kMaxGrid;
+    if (const char* mg = std::getenv("RS_MAX_GRID")) {
+      const long long v = std::strtoll(mg, nullptr, 10);
+      max_grid = std::max<int64_t>(8, std::min<int64_t>(kMaxGrid, v) / 8 * 8);
+    }
+    const QuantLaunch L{static_cast<const QJob*>(ptr), ql.n_tile, ql.n_flat, ql.n_zero, ql.split_code_lines,
+                        max_grid};
+    if (src_dt == RS_BF16)
+      launch_quant<true>(L, src, fmt, hw, static_cast<uint8_t*>(q), scales, s);
+    else
+      launch_quant<false>(L, src, fmt, hw, static_cast<uint8_t*>(q), scales, s);
+    return launched(who);
+  } catch (const std::exception& ex) {
+    return fail(RS_ENOMEM, std::string(who) + ": " + ex.what());
+  }
 }
