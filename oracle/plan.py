@@ -250,17 +250,26 @@ class Plan:
         return -(-self.end // self.S)
 
 
+POLICIES = ("best",) + ORDER_NAMES
+
+
 def plan(specs, V: int, a: int = ALIGN, policy: str = "best") -> Plan:
-    """Plan S and the starts ([walk], planner paragraphs; [summary], Method (2))."""
+    """Plan S and the starts ([walk], planner paragraphs; [summary], Method (2)).
+
+    policy "best" tries the three orders and keeps the best plan; "default",
+    "by_block_size" or "by_shape" plans with that one order (the planner
+    padding study compares them)."""
     if V < 1 or not specs:
         raise ValueError("need V >= 1 and at least one tensor")
+    if policy not in POLICIES:
+        raise ValueError(f"unknown order policy {policy!r}")
     lb = lower_bound(specs, V, a)
     ns = [numel(s) for s in specs]
     best = None
-    cand_orders = orders(specs)
-    if policy == "default":
-        cand_orders = cand_orders[:1]
-    for oi, order in enumerate(cand_orders):
+    cand_orders = list(enumerate(orders(specs)))
+    if policy != "best":
+        cand_orders = [cand_orders[ORDER_NAMES.index(policy)]]
+    for oi, order in cand_orders:
         S, starts = min_feasible_S(specs, order, V, a, lb)
         end = max(int(s) + n for s, n in zip(starts, ns))
         key = (S, end, oi)

@@ -166,6 +166,41 @@ def test_plan_within_twice_the_optimum_over_all_orders(seed):
     assert p.S >= P.lower_bound(specs, V, a) >= 1
 
 
+def test_the_three_orders_by_hand():
+    """Default: the caller's order. By block size: g descending, ties in caller order. By shape:
+    element count descending, then rows descending, ties in caller order."""
+    specs = [TensorSpec("a", 8, 4, "ROWS", 1),      # g 4,  n 32, rows 8
+             TensorSpec("b", 4, 8, "ROWS", 2),      # g 16, n 32, rows 4
+             TensorSpec("c", 2, 2, "WHOLE"),        # g 4,  n 4
+             TensorSpec("d", 1, 64, "FLAT", 16),    # g 16, n 64, rows 1
+             TensorSpec("e", 32, 1, "ELEM")]        # g 1,  n 32, rows 32
+    default, by_block, by_shape = P.orders(specs)
+    assert default == [0, 1, 2, 3, 4]
+    assert by_block == [1, 3, 0, 2, 4]
+    assert by_shape == [3, 4, 0, 1, 2]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_single_order_policies_against_brute_force(seed):
+    """Each single-order policy gives the smallest S its order admits (brute force over S and
+    starts), and "best" is the least of the three (ties: the smaller end, then the order
+    listed first)."""
+    specs, V, a = random_instance(3000 + seed)
+    per = {}
+    for k, name in enumerate(P.ORDER_NAMES):
+        p = P.plan(specs, V, a, name)
+        order = P.orders(specs)[k]
+        assert p.order_name == name and p.order == order
+        assert p.S == brute_min_S(specs, order, V, a)
+        assert list(p.starts) == brute_place(specs, order, p.S, a, V)
+        per[name] = p
+    best = P.plan(specs, V, a, "best")
+    want = min(P.ORDER_NAMES, key=lambda nm: (per[nm].S, per[nm].end, P.ORDER_NAMES.index(nm)))
+    assert (best.S, best.order_name, list(best.starts)) == (per[want].S, want, list(per[want].starts))
+    with pytest.raises(ValueError):
+        P.plan(specs, V, a, "by_name")
+
+
 def test_check_plan_catches_planted_errors():
     specs = [TensorSpec("a", 4, 4, "ROWS", 1), TensorSpec("b", 2, 8, "TILE", 2, 4)]
     V, S, a = 4, 16, 4
