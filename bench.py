@@ -12,10 +12,14 @@ workload (--workload 4) steps through pack, int8/uint8 quant and dequant of m
 and v.
 
 Throughput counts algorithmic bytes (each byte a kernel must read or write
-once) per second of wall time over the K timed steps. Per-kernel durations
-come from HIP events recorded on the stream the kernels run on. The CPU
-baseline times the CPU oracle on a bounded sample of the same workload.
-Prints one JSON line.
+once). In the timed region every kernel launch follows a 1 GiB write that
+leaves none of its inputs in L2 or the 256 MB MALL, and HIP events on the
+stream the kernels run on bracket each launch; the headline divides one
+step's bytes by the sum of its kernels' median durations over the K steps.
+A warm pass (K steps back to back, wall clock) is reported apart, as is a
+16-byte streaming copy of 1 GiB, the practical ceiling. The CPU baseline
+times the CPU oracle on a bounded sample of the same workload, on one core
+and on all host cores. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -35,6 +39,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
+FLUSH_BYTES = 1 << 30   # written before every timed launch: 4x the 256 MB MALL
 METRIC = "DBuffer pack/unpack+blockquant GB/s, % HBM peak (Llama-3-8B layer, V=64)"
 # committed counter summaries: (workload, mode, tile-major) -> profiles/traffic_<name>.md
 PROFILE_TRAFFIC = {(1, "step", False): "llama3_8b_v64", (1, "step", True): "llama3_8b_v64_tile_major",
@@ -51,7 +56,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", f)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps; each kernel's figure is the median over them")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4],
                     help="0 is the tiny three-tensor group: launch-bound, a parity case more than a bandwidth one")
@@ -65,15 +71,16 @@ def parse():
                     help="pack into a bf16 buffer (a bf16 ReduceScatter): each fp32 result rounded once")
     ap.add_argument("--cpu-sample", type=int, default=1, help="0 disables the CPU-oracle baseline")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled output checks")
-    ap.add_argument("--cold-steps", type=int, default=5,
-                    help="launches per kernel of the cold-cache pass after the timed region (0: skip)")
     ap.add_argument("--graph", action="store_true",
-                    help="capture one step in a HIP graph after the warm-up and replay it in the timed region "
-                         "(the per-kernel and cold passes stay eager)")
+                    help="capture one step in a HIP graph after the warm-up and replay it in the warm pass "
+                         "(the flushed timed region stays eager)")
+    ap.add_argument("--flush", default="write", choices=["write", "read"],
+                    help="how the 1 GiB buffer before each timed launch empties L2 and the MALL: written "
+                         "(fill) or read (a sum over it, which leaves no dirty lines behind)")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (system-scope fence at every record)")
     ap.add_argument("--copy-mib", type=int, default=1024,
-                    help="size of the device-to-device copy timed as the practical ceiling "
+                    help="size of the streaming copy (rs_bench_copy) timed as the practical ceiling "
                          "(and used to calibrate HBM byte counters); 0 disables it")
     return ap.parse_args()
 
@@ -199,48 +206,123 @@ class HipTimer:
         self.events = []
 
 
+def bench_lib():
+    """librs_bench.so (the streaming-copy ceiling), opened after torch's HIP runtime."""
+    path = os.path.join(ROOT, "structure_aware_grouped_amd", "librs_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with structure_aware_grouped_amd.build")
+    lib = ctypes.CDLL(path)
+    lib.rs_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.rs_bench_copy.restype = ctypes.c_int
+    return lib
+
+
 def log(msg: str):
     """A progress line on stderr (the JSON result line goes to stdout)."""
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, plan, names=None, max_seconds: float = 15.0) -> dict:
-    """The CPU oracle (single-threaded NumPy) on a bounded sample of the workload:
-    the tensors named in `names` (default: every tensor, i.e. one whole step),
-    one at a time and in order, until `max_seconds` of oracle time have passed
-    (the Llama-3-8B and Llama-3-70B layers finish whole; the MoE layer stops
-    after its first experts), with the bench's byte accounting. Inputs are
-    generated before the clock starts."""
+def _oracle_step_on(w, spec, sigma, fmt, wb, g, p, pb):
+    """The oracle's unpack, pack and (for tiled tensors) block quant of one tensor or
+    tile band; returns the algorithmic bytes that work moves."""
+    from oracle import transform as OT
+    import workloads as W
+    n = spec.numel
+    OT.unpack(wb, [spec], [0])                       # the tensor is its slice of the buffer
+    OT.pack_values(g.ravel(), p, sigma, True)        # scale, accumulate
+    moved = 2 * n * pb + n * 12
+    if spec.kind in ("TILE", "TILEMAJOR", "FLAT") and fmt:
+        x = W.f32_from_bf16_bits(wb) if wb.dtype == np.uint16 else wb.view(np.float32)
+        for _, b, pos in OT.quant_blocks([spec], [0]):
+            OT.quantize_block(x[pos], fmt)
+        moved += n * pb + n + 4 * OT.count_quant_blocks([spec])
+    return moved
+
+
+def _cpu_units(w, starts, S, idx, rows_per_unit: int = 1024):
+    """(tensor, r0, r1) pieces of the sampled tensors for the all-core leg: tile bands of
+    about rows_per_unit rows (whole bands), whole tensors otherwise."""
+    units = []
+    for i in idx:
+        sp = w.specs[i]
+        step = sp.rows
+        if sp.kind in ("TILE", "TILEMAJOR") and sp.rows > rows_per_unit:
+            step = max(sp.p0, rows_per_unit // sp.p0 * sp.p0)
+        for r0 in range(0, sp.rows, step):
+            units.append((i, r0, min(sp.rows, r0 + step)))
+    return units
+
+
+def _cpu_worker(widx, tile_major, S, starts, units, barrier, results):
+    """One process of the all-core leg: regenerate its pieces' inputs, wait for the
+    others, run the oracle on its pieces, report (bytes, start, end) on the monotonic
+    clock that all processes share."""
+    from oracle import transform as OT
+    import workloads as W
+    w = W.workload(widx)
+    if tile_major:
+        w = W.tile_major_variant(w)
+    pb = 2 if w.param_dtype == "bf16" else 4
+    sigma = OT.inv_v(w.V)
+    prev_cache = {}
+
+    def prev_range(b, e):
+        parts = []
+        for k in range(b // S, (e - 1) // S + 1):
+            if k not in prev_cache:
+                prev_cache[k] = W.prev_slice(w, k, S)
+            lo, hi = max(b, k * S) - k * S, min(e, (k + 1) * S) - k * S
+            parts.append(prev_cache[k][lo:hi])
+        return np.concatenate(parts)
+
+    work, cache = [], {}
+    for i, r0, r1 in units:
+        sp = w.specs[i]
+        if i not in cache:
+            cache = {i: (W.weight_bits(w, i).reshape(sp.rows, sp.cols),
+                         W.tensor_values(w, i, W.Role.GRAD))}
+        wb, g = cache[i]
+        band = W.TensorSpec(sp.name, r1 - r0, sp.cols, sp.kind, sp.p0, sp.p1)
+        s = starts[i] + r0 * sp.cols
+        work.append((band, np.ascontiguousarray(wb[r0:r1]).ravel(), np.ascontiguousarray(g[r0:r1]),
+                     prev_range(s, s + band.numel)))
+    cache = prev_cache = None
+    barrier.wait()
+    t0 = time.perf_counter()
+    moved = sum(_oracle_step_on(w, band, sigma, w.quant, wb, g, p, pb) for band, wb, g, p in work)
+    results.put((moved, t0, time.perf_counter()))
+
+
+def _secs(t: float) -> str:
+    return f"{t:.2f} s" if t >= 1 else f"{t * 1e3:.2f} ms"
+
+
+def cpu_baseline(w, plan, tile_major: bool = False, max_seconds: float = 15.0) -> dict:
+    """The CPU oracle (NumPy) on a bounded sample of the workload, single-threaded and
+    then on all host cores.
+
+    Single core: the tensors one at a time and in order until `max_seconds` of oracle
+    time have passed (the Llama-3-8B and Llama-3-70B layers finish whole; the MoE layer
+    stops after its first experts). All cores: the same tensors cut into tile bands,
+    spread over one process per core (at most 16), each regenerating its inputs before a
+    common start. Both use the bench's byte accounting; inputs are generated before the
+    clock starts."""
+    import multiprocessing
     from oracle import transform as OT
     from workloads.device import Inputs
-    import workloads as W
 
-    names = [sp.name for sp in w.specs] if names is None else list(names)
-    idx = [i for i, sp in enumerate(w.specs) if sp.name in names]
     inp = Inputs(w, plan.S, plan.starts, plan.R_mat, device="cpu")
     pb = 2 if w.param_dtype == "bf16" else 4
     sigma = OT.inv_v(w.V)
     moved, dt, done = 0, 0.0, []
-    for i in idx:
+    for i in range(len(w.specs)):
         if dt >= max_seconds:
             break
         done.append(i)
         spec, s = w.specs[i], plan.starts[i]
         wb, g, p = inp.weight_bits(i), inp.grad(i), inp.prev_range(s, s + spec.numel)
         t0 = time.perf_counter()
-        n = spec.numel
-        # unpack: the tensor is its slice of the gathered buffer
-        OT.unpack(wb, [spec], [0])
-        moved += 2 * n * pb
-        # pack: scale, accumulate
-        OT.pack_values(g.ravel(), p, sigma, True)
-        moved += n * 12
-        # quant: every tile of the tensor
-        if spec.kind in ("TILE", "TILEMAJOR", "FLAT") and w.quant:
-            x = W.f32_from_bf16_bits(wb) if wb.dtype == np.uint16 else wb.view(np.float32)
-            for _, b, pos in OT.quant_blocks([spec], [0]):
-                OT.quantize_block(x[pos], w.quant)
-            moved += n * pb + n + 4 * OT.count_quant_blocks([spec])
+        moved += _oracle_step_on(w, spec, sigma, w.quant, wb, g, p, pb)
         dt += time.perf_counter() - t0
     if len(done) == len(w.specs):
         what = "every tensor of the layer (one whole step)"
@@ -248,10 +330,36 @@ def cpu_baseline(w, plan, names=None, max_seconds: float = 15.0) -> dict:
         what = ", ".join(w.specs[i].name for i in done)
     else:
         what = f"the first {len(done)} of the layer's {len(w.specs)} tensors"
-    return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{what}: unpack + pack{' + e4m3 tile quant' if w.quant else ''}, "
-                      + (f"{moved / 1e9:.3f} GB in {dt:.1f} s" if moved >= 1e8 else
-                         f"{moved / 1e6:.3f} MB in {dt * 1e3:.2f} ms")}
+    work = f"unpack + pack{' + ' + w.quant + ' tile quant' if w.quant else ''}"
+    size = (f"{moved / 1e9:.3f} GB" if moved >= 1e8 else f"{moved / 1e6:.3f} MB")
+    single = {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+              "seconds": round(dt, 3)}
+
+    affinity = len(os.sched_getaffinity(0))
+    procs = max(1, min(16, affinity))
+    units = _cpu_units(w, plan.starts, plan.S, done)
+    loads = [[] for _ in range(procs)]
+    sizes = [0] * procs
+    for u in sorted(units, key=lambda u: -(u[2] - u[1]) * w.specs[u[0]].cols):   # largest first
+        k = sizes.index(min(sizes))
+        loads[k].append(u)
+        sizes[k] += (u[2] - u[1]) * w.specs[u[0]].cols
+    loads = [sorted(l) for l in loads if l]
+    ctx = multiprocessing.get_context("spawn")       # the workers never touch the GPU
+    barrier, results = ctx.Barrier(len(loads)), ctx.Queue()
+    ps = [ctx.Process(target=_cpu_worker, args=(w.index, tile_major, plan.S, list(plan.starts), l, barrier, results))
+          for l in loads]
+    for p in ps:
+        p.start()
+    got = [results.get(timeout=600) for _ in ps]
+    for p in ps:
+        p.join()
+    par_moved = sum(r[0] for r in got)
+    wall = max(r[2] for r in got) - min(r[1] for r in got)
+    assert par_moved == moved, "the all-core leg covers the same work as the single-core leg"
+    return {"value": round(par_moved / wall / 1e9, 4), "unit": "GB/s", "cores": len(loads), "kind": "oracle",
+            "sample": f"{what}: {work}, {size}; {len(loads)} processes in {_secs(wall)}, 1 core in {_secs(dt)}",
+            "single_core": single, "nproc": os.cpu_count(), "affinity": affinity}
 
 
 def main():
@@ -379,23 +487,55 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident in HBM")
 
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    timer = HipTimer(torch, fenced=args.fenced_events)
+    flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush64 = flush.view(torch.int64)
+
+    def empty_caches(k):
+        """Touch 1 GiB (4x the MALL): nothing a kernel reads is left in L2 or the MALL."""
+        if args.flush == "write":
+            flush.fill_(k & 0xFF)
+        else:
+            flush64.sum()
+
+    def flushed_launches(fn, n):
+        """n launches of fn, each after the 1 GiB flush; HIP events around the launch only.
+        Durations in ms."""
+        ev = [(timer.event(), timer.event()) for _ in range(n)]
+        for k, (a, b) in enumerate(ev):
+            empty_caches(k)
+            timer.record(a, stream)
+            fn()
+            timer.record(b, stream)
+        torch.cuda.synchronize()
+        return [timer.ms(a, b) for a, b in ev]
+
     copy = None
     if args.copy_mib:
-        # a plain device-to-device copy of known size: the practical HBM ceiling, and the
-        # reference whose counter readings calibrate FETCH_SIZE / WRITE_SIZE
+        # the practical HBM ceiling: a 16-byte streaming copy of known size (the library's
+        # benchmark helper), timed like the kernels; its counter readings calibrate
+        # FETCH_SIZE / WRITE_SIZE. torch's own device copy is timed beside it for context.
+        blib = bench_lib()
         nb = args.copy_mib << 20
         src_c = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
         dst_c = torch.empty_like(src_c)
-        ms = []
-        for _ in range(6):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            dst_c.copy_(src_c)
-            b.record()
-            torch.cuda.synchronize()
-            ms.append(a.elapsed_time(b))
-        best = float(np.median(ms[1:]))
-        copy = {"bytes": 2 * nb, "median_ms": round(best, 4), "GBps": round(2 * nb / (best * 1e-3) / 1e9, 1)}
+
+        def own_copy():
+            rc = blib.rs_bench_copy(ctypes.c_void_p(dst_c.data_ptr()), ctypes.c_void_p(src_c.data_ptr()),
+                                    ctypes.c_int64(nb), ctypes.c_void_p(stream))
+            if rc != 0:
+                raise RuntimeError(f"rs_bench_copy returned {rc}")
+        own_copy()
+        torch.cuda.synchronize()
+        assert bool(torch.equal(dst_c[:: 1 << 16], src_c[:: 1 << 16])), "rs_bench_copy"
+        ms = flushed_launches(own_copy, args.steps)
+        med = float(np.median(ms))
+        tms = flushed_launches(lambda: dst_c.copy_(src_c), 5)
+        copy = {"kernel": "rs_bench_copy: 16-byte nontemporal loads and stores, 64-thread workgroups of 1 KiB",
+                "bytes": 2 * nb, "median_ms": round(med, 5), "GBps": round(2 * nb / (med * 1e-3) / 1e9, 1),
+                "torch_copy_GBps": round(2 * nb / (float(np.median(tms)) * 1e-3) / 1e9, 1),
+                "timing": f"median of {args.steps} flushed launches"}
         del src_c, dst_c
 
     for _ in range(args.warmup):
@@ -403,15 +543,10 @@ def main():
             fn()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps. HIP events, on the stream the library launches on
-    # (torch's current stream, which the binding passes), bracket the dominant kernel
-    # only: every event record adds idle GPU time at a kernel boundary, so the other
-    # kernels are timed in the pass that follows.
-    # With --graph the whole step is one captured HIP graph (the warm-up has made the
-    # calls with these pointers, so the capture holds kernel launches only) and the
-    # events bracket each replay.
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    timer = HipTimer(torch, fenced=args.fenced_events)
+    # ---- timed region: K steps, cold. Before every kernel launch a 1 GiB buffer is written
+    # (outside the events), so no kernel finds its inputs in L2 or the MALL; HIP events
+    # on the stream the library launches on (torch's current stream, which the binding
+    # passes) bracket each launch. Per kernel: the median over the K steps.
     graph = None
     if args.graph:
         graph = torch.cuda.CUDAGraph()
@@ -419,6 +554,34 @@ def main():
             for _, fn in steps:
                 fn()
         graph.replay()
+    kev = [[(timer.event(), timer.event()) for _ in steps] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for (name, fn), (a, b) in zip(steps, kev[k]):
+            empty_caches(k)
+            timer.record(a, stream)
+            fn()
+            timer.record(b, stream)
+    torch.cuda.synchronize()
+    wall_cold = time.perf_counter() - t0
+    log(f"timed region: {args.steps} flushed steps in {wall_cold * 1e3:.1f} ms (flushes included)")
+    per_kernel = {}
+    for j, (name, _) in enumerate(steps):
+        ms = [timer.ms(kev[k][j][0], kev[k][j][1]) for k in range(args.steps)]
+        med, avg = float(np.median(ms)), float(np.mean(ms))
+        per_kernel[name] = {"median_ms": round(med, 5), "avg_ms": round(avg, 5), "min_ms": round(float(np.min(ms)), 5),
+                            "GBps": round(nbytes[name] / (med * 1e-3) / 1e9, 1), "bytes": int(nbytes[name])}
+    step_bytes = sum(nbytes[name] for name, _ in steps)
+    ms_per_step = sum(per_kernel[name]["median_ms"] for name, _ in steps)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dom_avg_s = per_kernel[dominant]["avg_ms"] * 1e-3
+
+    # ---- warm pass, labelled apart: K steps back to back, as a training loop calls them
+    # (a kernel may find part of its input in the MALL, left there by the kernel before
+    # it). Events around the dominant kernel only, the wall clock around the K steps; then
+    # K more steps with events around every launch. With --graph each step is one replay
+    # of the captured step.
     dom_ev = [(timer.event(), timer.event()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -437,59 +600,24 @@ def main():
                 fn()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(f"timed region: {args.steps} steps in {wall * 1e3:.1f} ms")
     dom_ms = [timer.ms(a, b) for a, b in dom_ev]
     del graph
-
-    # ---- per-kernel pass, right after the timed region and under the same warm
-    # conditions: HIP events around every launch
-    kev = [[(timer.event(), timer.event()) for _ in steps] for _ in range(args.steps)]
+    wev = [[(timer.event(), timer.event()) for _ in steps] for _ in range(args.steps)]
     for k in range(args.steps):
-        for (name, fn), (a, b) in zip(steps, kev[k]):
+        for (name, fn), (a, b) in zip(steps, wev[k]):
             timer.record(a, stream)
             fn()
             timer.record(b, stream)
     torch.cuda.synchronize()
-    per_kernel = {}
+    warm = {"label": f"warm caches: {args.steps} steps back to back" +
+                     (" (one HIP graph replay each)" if args.graph else ""),
+            "value": round(step_bytes / (wall / args.steps) / 1e9, 1), "ms_per_step": round(wall / args.steps * 1e3, 4),
+            ("graph_replay_avg_ms" if args.graph else f"{dominant}_in_steps_avg_ms"): round(float(np.mean(dom_ms)), 5)}
     for j, (name, _) in enumerate(steps):
-        ms = [timer.ms(kev[k][j][0], kev[k][j][1]) for k in range(args.steps)]
-        avg = float(np.mean(ms))
-        per_kernel[name] = {"avg_ms": round(avg, 5), "median_ms": round(float(np.median(ms)), 5),
-                            "min_ms": round(float(np.min(ms)), 5),
-                            "GBps": round(nbytes[name] / (avg * 1e-3) / 1e9, 1),
-                            "bytes": int(nbytes[name])}
-    graph_info = None
-    if args.graph:   # events around each replay: the whole step
-        graph_info = {"replay_avg_ms": round(float(np.mean(dom_ms)), 5),
-                      "replay_min_ms": round(float(np.min(dom_ms)), 5)}
-    else:
-        per_kernel[dominant]["timed_region_avg_ms"] = round(float(np.mean(dom_ms)), 5)
-    step_bytes = sum(nbytes[name] for name, _ in steps)
-    ms_per_step = wall / args.steps * 1e3
-    value = step_bytes / (wall / args.steps) / 1e9
-
-    # ---- cold-cache pass, after and outside the timed region: before every launch a
-    # 1 GiB scratch buffer is written (outside the events), so neither L2 nor the
-    # 256 MB MALL holds anything the kernel reads
-    cold = None
-    if args.cold_steps:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        cev = [[(timer.event(), timer.event()) for _ in steps] for _ in range(args.cold_steps)]
-        for k in range(args.cold_steps):
-            for (name, fn), (a, b) in zip(steps, cev[k]):
-                flush.fill_(k & 0xFF)
-                timer.record(a, stream)
-                fn()
-                timer.record(b, stream)
-        torch.cuda.synchronize()
-        cold = {"label": f"cold L2 and MALL: a 1 GiB buffer written before each launch, "
-                         f"{args.cold_steps} launches per kernel, median"}
-        for j, (name, _) in enumerate(steps):
-            ms = [timer.ms(cev[k][j][0], cev[k][j][1]) for k in range(args.cold_steps)]
-            med = float(np.median(ms))
-            cold[name] = {"median_ms": round(med, 5), "min_ms": round(float(np.min(ms)), 5),
-                          "GBps": round(nbytes[name] / (med * 1e-3) / 1e9, 1)}
-        del flush
+        ms = [timer.ms(wev[k][j][0], wev[k][j][1]) for k in range(args.steps)]
+        warm[name] = {"median_ms": round(float(np.median(ms)), 5),
+                      "GBps": round(nbytes[name] / (float(np.median(ms)) * 1e-3) / 1e9, 1)}
+    del flush, flush64
 
     # ---- sampled checks of the outputs of the last step
     check = "skipped"
@@ -505,11 +633,13 @@ def main():
             "unpack_dequant"
         check = f"ok ({specs[i].name}: rebuilt weights within E4M3 rounding of the originals)"
     elif not args.no_check and not w.adam_states:
-        # sampled checks that need no oracle (the oracle parity tests live in tests/): the
-        # second tensor unpacks to its generated weights, padding is +0.0, codes outside
-        # blocks are 0, scales are finite and positive
-        i = 1
-        assert np.array_equal(tensor_bits(params[i]).ravel(), inp.weight_bits(i)), "unpack"
+        # checks that need no oracle (the oracle parity tests live in tests/): the tensors
+        # unpack to their generated weights (every tensor; on the MoE layer the first and
+        # last expert and the router), padding is +0.0, codes outside blocks are 0, scales
+        # are finite and positive
+        which = range(len(specs)) if len(specs) < 64 else [0, 1, len(specs) - 3, len(specs) - 2, len(specs) - 1]
+        for i in which:
+            assert np.array_equal(tensor_bits(params[i]).ravel(), inp.weight_bits(i)), f"unpack {specs[i].name}"
         pads = padding_ranges(specs, starts, S, R)
         pk = packed.view(torch.int16 if args.packed_bf16 else torch.int32)
         assert all(bool((pk[b:e] == 0).all()) for b, e in pads), "pack padding"
@@ -517,7 +647,8 @@ def main():
             assert all(bool((q[b:e] == 0).all()) for b, e in pads), "codes outside blocks"
             sf = scales.float()
             assert bool(torch.isfinite(sf).all()) and bool((sf > 0).all()), "scales"
-        check = f"ok ({specs[i].name} unpacks to its weights; padding and codes outside blocks are zero)"
+        check = (f"ok ({'every tensor unpacks' if len(specs) < 64 else f'{len(which)} tensors unpack'} to its "
+                 f"weights; padding and codes outside blocks are zero)")
     elif not args.no_check and args.mode == "step":
         # Adam-state layer, again without the oracle: the second tensor's m and v pack bit
         # for bit (sigma = 1, no accumulate), their dequantised values lie within half a
@@ -540,20 +671,20 @@ def main():
                  f"padding, codes and values outside the tensors are zero)")
     if not args.no_check and args.mode == "adam8":
         check = "skipped (the Adam step is checked by tests/test_gpu_adam.py)"
-    # the dominant kernel inside the timed region (inside a graph replay it has no events
-    # of its own: then its eager per-kernel average)
-    dom_avg_s = (per_kernel[dominant]["avg_ms"] if args.graph else float(np.mean(dom_ms))) * 1e-3
     achieved = nbytes[dominant] / dom_avg_s / 1e9
     # counter summaries exist for the fp32 packed buffer only
     traffic = None if args.packed_bf16 else read_traffic((args.workload, args.mode, bool(args.tile_major)), dominant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant])}
+                "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant]),
+                "timing": f"mean of {args.steps} flushed launches in the timed region",
+                "copy_ceiling_GBps": copy["GBps"] if copy else None,
+                "frac_of_copy_ceiling": round(achieved / copy["GBps"], 4) if copy else None}
 
     log(f"check: {check}")
     cpu = None
     if args.cpu_sample and not w.adam_states and args.mode == "step":
-        cpu = cpu_baseline(w, plan)
+        cpu = cpu_baseline(w, plan, tile_major=bool(args.tile_major))
         log(f"CPU oracle: {cpu['sample']}")
 
     names = {0: "tiny group (64x48 1-row blocks, 100x32 16x16 tiles, 7x130 elements; fp32), V=4: unpack + "
@@ -597,10 +728,12 @@ def main():
                        args.workload, "bf16 params, fp32 grads/prev/packed, e4m3 codes + fp32 scales")
                    + ("; the packed buffer is bf16" if args.packed_bf16 else ""),
                    "e4m3_encoder": "sw" if os.environ.get("RS_E4M3_ENCODER") == "sw" else "hw",
-                   "launch": "one HIP graph replay per step" if args.graph else "eager"},
+                   "launch": "eager" + ("; warm pass: one HIP graph replay per step" if args.graph else "")},
+        "timing": f"value: algorithmic bytes of one step over the sum of its kernels' median durations, "
+                  f"{args.steps} launches each, every launch after a 1 GiB {args.flush} that empties L2 and the "
+                  f"MALL (HIP events on the launch stream; the flush is outside the events)",
         "kernels": per_kernel,
-        "graph": graph_info,
-        "cold_cache": cold,
+        "warm": warm,
         "copy_ceiling": copy,
         "check": check,
         "roofline": roofline,

@@ -1,4 +1,6 @@
-"""Build librs_hip.so for gfx950 with hipcc (in-tree, next to this file).
+"""Build librs_hip.so (the layout library) and librs_bench.so (the
+benchmark's streaming-copy ceiling) for gfx950 with hipcc, in-tree next to
+this file.
 
     python -m structure_aware_grouped_amd.build
 """
@@ -15,6 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librs_hip.so")
 SOURCES = ["planner.cpp", "plan.cpp", "transform.hip", "quant.hip", "gather.hip", "adam.hip"]
+BENCH_LIB = os.path.join(HERE, "librs_bench.so")
+BENCH_SOURCES = ["stream_copy.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -36,10 +40,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into librs_hip.so; returns its path. Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _compile(sources, lib, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
@@ -47,8 +50,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile both libraries; returns the layout library's path. Always recompiles."""
+    _compile(BENCH_SOURCES, BENCH_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -30,6 +30,23 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(rs_\w+)\s*\(", text, re.M)))
 
 
+def test_bench_helper_library_exports_its_declared_call(rs):
+    """librs_bench.so (the benchmark's streaming-copy ceiling) exports what rs_bench.h declares;
+    bad arguments are refused before any launch."""
+    import ctypes
+    text = open(os.path.join(ROOT, "include", "rs_bench.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(rs_\w+)\s*\(", text, re.M)))
+    assert names == ["rs_bench_copy"]
+    path = os.path.join(ROOT, "structure_aware_grouped_amd", "librs_bench.so")
+    assert os.path.exists(path), "librs_bench.so is not built: run __graft_entry__.build()"
+    lib = ctypes.CDLL(path)
+    lib.rs_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    assert lib.rs_bench_copy(a, b, 15, None) == -1                      # not a multiple of 16
+    assert lib.rs_bench_copy(a, ctypes.c_void_p((1 << 20) + 16), 64, None) == -1   # overlapping
+    assert lib.rs_bench_copy(a, b, 0, None) == 0                        # nothing to do
+
+
 def test_library_exports_every_declared_call(rs):
     from structure_aware_grouped_amd import binding
     names = _declared()
