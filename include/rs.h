@@ -125,7 +125,7 @@ typedef struct rs_tensor_spec {
 
 typedef struct rs_plan rs_plan;   /* opaque, owned by the library */
 
-enum { RS_ORDER_BEST = 0, RS_ORDER_DEFAULT = 1 };
+enum { RS_ORDER_BEST = 0, RS_ORDER_DEFAULT = 1, RS_ORDER_BLOCK_SIZE = 2, RS_ORDER_SHAPE = 3 };
 enum { RS_ORDER_KIND_DEFAULT = 0, RS_ORDER_KIND_BLOCK = 1, RS_ORDER_KIND_SHAPE = 2 };
 
 /* Host planner (feynmanwiki walkthrough: the planner paragraphs on the
@@ -138,8 +138,9 @@ enum { RS_ORDER_KIND_DEFAULT = 0, RS_ORDER_KIND_BLOCK = 1, RS_ORDER_KIND_SHAPE =
  * for which placing each tensor at its earliest valid start after the
  * previous tensor's end fits inside V*S. Keep the order with the smallest S,
  * then the smallest end max(s_i + n_i), then the one listed first.
- * policy: RS_ORDER_BEST tries the three orders, RS_ORDER_DEFAULT only the
- * caller's. align >= 1 (16 for plans that rs_plan_load accepts).
+ * policy: RS_ORDER_BEST tries the three orders; RS_ORDER_DEFAULT,
+ * RS_ORDER_BLOCK_SIZE or RS_ORDER_SHAPE plans with that one order (to compare
+ * the orders). align >= 1 (16 for plans that rs_plan_load accepts).
  * Outputs (caller-owned host arrays): *S_out; starts_out[n] in the caller's
  * tensor order; order_out[n] the placement order (a permutation of 0..n-1);
  * *order_kind_out one of RS_ORDER_KIND_*. order_out / order_kind_out may be

@@ -123,14 +123,15 @@ def _copy_code(t: torch.Tensor) -> int:
 # ---------------------------------------------------------------- planner
 
 def rs_plan_build(specs, V: int, align: int = 16, policy: str = "best"):
-    """(S, starts, order, order_name) from the host planner."""
+    """(S, starts, order, order_name) from the host planner. policy: "best" (the three orders),
+    or one order: "default", "by_block_size", "by_shape"."""
     lib = load()
     n = len(specs)
     S = ctypes.c_int64()
     starts = (ctypes.c_int64 * n)()
     order = (ctypes.c_int64 * n)()
     kind = ctypes.c_int32()
-    pol = {"best": 0, "default": 1}[policy]
+    pol = {"best": 0, "default": 1, "by_block_size": 2, "by_shape": 3}[policy]
     _check(lib.rs_plan_build(specs_array(specs), n, int(V), int(align), pol, ctypes.byref(S),
                              starts, order, ctypes.byref(kind)))
     return S.value, list(starts), list(order), ORDER_KINDS[kind.value]

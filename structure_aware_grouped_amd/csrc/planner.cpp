@@ -233,7 +233,8 @@ extern "C" int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, 
     if (n < 1) return fail(RS_EINVAL, "rs_plan_build: need at least one tensor");
     if (V < 1) return fail(RS_EINVAL, "rs_plan_build: V must be >= 1");
     if (align < 1) return fail(RS_EINVAL, "rs_plan_build: align must be >= 1");
-    if (policy != RS_ORDER_BEST && policy != RS_ORDER_DEFAULT)
+    if (policy != RS_ORDER_BEST && policy != RS_ORDER_DEFAULT && policy != RS_ORDER_BLOCK_SIZE &&
+        policy != RS_ORDER_SHAPE)
       return fail(RS_EINVAL, "rs_plan_build: unknown order policy");
 
     std::vector<Item> items(n);
@@ -269,22 +270,27 @@ extern "C" int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, 
     for (int64_t p = 0; p < n; ++p)
       prefix_lcm[p + 1] = lcm_cap(prefix_lcm[p], items[by_n[p]].g, s_max);
 
-    std::vector<std::vector<int>> orders;
+    // the three orders (kind RS_ORDER_KIND_*), or the one the policy names
     std::vector<int> ident(n);
     std::iota(ident.begin(), ident.end(), 0);
-    orders.push_back(ident);
-    if (policy == RS_ORDER_BEST) {
-      std::vector<int> by_block = ident;
-      std::stable_sort(by_block.begin(), by_block.end(),
-                       [&](int x, int y) { return items[x].g > items[y].g; });
-      orders.push_back(by_block);
-      std::vector<int> by_shape = ident;
-      std::stable_sort(by_shape.begin(), by_shape.end(), [&](int x, int y) {
-        if (items[x].n != items[y].n) return items[x].n > items[y].n;
-        return items[x].rows > items[y].rows;
-      });
-      orders.push_back(by_shape);
-    }
+    std::vector<int> by_block = ident;
+    std::stable_sort(by_block.begin(), by_block.end(), [&](int x, int y) { return items[x].g > items[y].g; });
+    std::vector<int> by_shape = ident;
+    std::stable_sort(by_shape.begin(), by_shape.end(), [&](int x, int y) {
+      if (items[x].n != items[y].n) return items[x].n > items[y].n;
+      return items[x].rows > items[y].rows;
+    });
+    std::vector<std::vector<int>> orders;
+    std::vector<int32_t> kinds;
+    auto take = [&](int32_t pol, const std::vector<int>& order, int32_t kind) {
+      if (policy == RS_ORDER_BEST || policy == pol) {
+        orders.push_back(order);
+        kinds.push_back(kind);
+      }
+    };
+    take(RS_ORDER_DEFAULT, ident, RS_ORDER_KIND_DEFAULT);
+    take(RS_ORDER_BLOCK_SIZE, by_block, RS_ORDER_KIND_BLOCK);
+    take(RS_ORDER_SHAPE, by_shape, RS_ORDER_KIND_SHAPE);
 
     const Candidates cand{&items, &by_n, &prefix_lcm, align, s_max};
     int64_t best_S = -1, best_end = -1;
@@ -313,7 +319,7 @@ extern "C" int rs_plan_build(const rs_tensor_spec* specs, int64_t n, int64_t V, 
     std::memcpy(starts_out, best_starts.data(), sizeof(int64_t) * n);
     if (order_out)
       for (int64_t i = 0; i < n; ++i) order_out[i] = orders[best_o][i];
-    if (order_kind_out) *order_kind_out = best_o;
+    if (order_kind_out) *order_kind_out = kinds[best_o];
     return RS_OK;
   } catch (const std::exception& ex) {
     return fail(RS_ENOMEM, std::string("rs_plan_build: ") + ex.what());

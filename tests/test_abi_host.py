@@ -72,7 +72,7 @@ def test_host_planner_matches_oracle_on_workloads(rs, idx):
 @pytest.mark.parametrize("seed", range(150))
 def test_host_planner_matches_oracle_on_random_instances(rs, seed):
     specs, V, a = random_instance(10_000 + seed)
-    for policy in ("best", "default"):
+    for policy in ("best", "default", "by_block_size", "by_shape"):
         S, starts, order, name = rs.rs_plan_build(specs, V, a, policy)
         ref = OP.plan(specs, V, a, policy)
         assert (S, starts, order, name) == (ref.S, [int(s) for s in ref.starts], ref.order,
