@@ -14,6 +14,10 @@ GPT-OSS-120B and DeepSeek-V3-671B, at 1x / 16x / 128x row granularity):
   256 routed experts and one shared expert of width 2048, a 256-way router
   with its score-correction bias.
 
+Beside them, the bench's own groups with the same block convention: the
+Llama-3-8B layer and the 128-expert MoE layer, per-expert and with each
+projection of all experts fused into one tensor.
+
 A 2-D tensor gets ROWS(k) atomic blocks (k = the row granularity); a 1-D
 tensor (norm, bias, sink) gets one-element blocks.
 """
@@ -76,5 +80,37 @@ def deepseek_v3_layer(k: int) -> List[TensorSpec]:
     return specs
 
 
+def llama3_8b_layer(k: int) -> List[TensorSpec]:
+    """The Llama-3-8B decoder layer of the bench (hidden 4096, 8 key-value heads of 128,
+    FFN 14336), with k-row blocks instead of its 128x128 tiles."""
+    h, kv, ffn = 4096, 1024, 14336
+    return [_mat("wq", h, h, k), _mat("wk", kv, h, k), _mat("wv", kv, h, k), _mat("wo", h, h, k),
+            _mat("gate", ffn, h, k), _mat("up", ffn, h, k), _mat("down", h, ffn, k),
+            _vec("attn_norm", h), _vec("mlp_norm", h)]
+
+
+def moe128_layer(k: int, fused_experts: bool = False) -> List[TensorSpec]:
+    """The bench's MoE layer (128 experts of gate_up 5760x2880 and down 2880x2880, a
+    128x2880 router) with k-row blocks: per-expert tensors as the bench stores them, or
+    each projection of all experts fused into one tensor (128*5760 x 2880 and
+    128*2880 x 2880)."""
+    e, h, inter = 128, 2880, 2880
+    if fused_experts:
+        specs = [_mat("experts.gate_up", e * 2 * inter, h, k), _mat("experts.down", e * inter, h, k)]
+    else:
+        specs = []
+        for x in range(e):
+            specs += [_mat(f"e{x}.gate_up", 2 * inter, h, k), _mat(f"e{x}.down", inter, h, k)]
+    return specs + [_mat("router", e, h, k)]
+
+
+STUDY_LAYERS = {
+    "gpt_oss_120b": lambda k: gpt_oss_120b_layer(k, fused_experts=True),
+    "gpt_oss_120b_unfused": lambda k: gpt_oss_120b_layer(k, fused_experts=False),
+    "deepseek_v3": deepseek_v3_layer,
+    "llama3_8b": llama3_8b_layer,
+    "moe128": lambda k: moe128_layer(k, fused_experts=False),
+    "moe128_fused": lambda k: moe128_layer(k, fused_experts=True),
+}
 STUDY_GRANULARITIES = (1, 16, 128)
 STUDY_FSDP_SIZES = (8, 16, 32, 64, 96, 128, 192, 256, 384, 512, 768, 1024)
