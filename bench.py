@@ -41,13 +41,19 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
 FLUSH_BYTES = 1 << 30   # written before every timed launch: 4x the 256 MB MALL
 METRIC = "DBuffer pack/unpack+blockquant GB/s, % HBM peak (Llama-3-8B layer, V=64)"
-# committed counter summaries: (workload, mode, tile-major) -> profiles/traffic_<name>.md
-PROFILE_TRAFFIC = {(1, "step", False): "llama3_8b_v64", (1, "step", True): "llama3_8b_v64_tile_major",
-                   (1, "fp8_gather", False): "llama3_8b_v64_fp8_gather", (4, "adam8", False): "adam8_llama3_8b_v64",
-                   (2, "step", False): "llama3_70b_v1024", (3, "step", False): "moe128_v256",
-                   (4, "step", False): "adam_states_llama3_8b_v64",
-                   (3, "fp8_gather", False): "moe128_v256_fp8_gather",
-                   (1, "fp8_gather", True): "llama3_8b_v64_tile_major_fp8_gather"}
+# committed counter summaries: (workload, mode, tile-major, Adam blocks) -> profiles/traffic_<name>.md
+PROFILE_TRAFFIC = {
+    (1, "step", False, "flat2048"): "llama3_8b_v64",
+    (1, "step", True, "flat2048"): "llama3_8b_v64_tile_major",
+    (1, "fp8_gather", False, "flat2048"): "llama3_8b_v64_fp8_gather",
+    (1, "fp8_gather", True, "flat2048"): "llama3_8b_v64_tile_major_fp8_gather",
+    (2, "step", False, "flat2048"): "llama3_70b_v1024",
+    (3, "step", False, "flat2048"): "moe128_v256",
+    (3, "fp8_gather", False, "flat2048"): "moe128_v256_fp8_gather",
+    (4, "step", False, "flat2048"): "adam_states_llama3_8b_v64",
+    (4, "adam8", False, "flat2048"): "adam8_llama3_8b_v64",
+    (4, "adam8", False, "tile32"): "adam8_tile32_llama3_8b_v64",
+}
 KERNEL_SOURCES = [os.path.join(ROOT, "structure_aware_grouped_amd", "csrc", f)
                   for f in ("device_common.h", "host_common.h", "transform.hip", "quant.hip", "gather.hip",
                             "adam.hip", "rs_internal.h", "plan.cpp")]
@@ -65,6 +71,9 @@ def parse():
                     help="step: the workload's steps; fp8_gather: block quant of the rank slices, then "
                          "the fused unpack-dequant of the codes into the bf16 tensors; adam8 (workload 4): "
                          "one AdamW step on the int8/uint8 block-quantised m and v")
+    ap.add_argument("--adam-blocks", default="flat2048", choices=["flat2048", "tile32"],
+                    help="workload 4's quantisation blocks: 2048-element flat blocks, or the pages' own 8-bit "
+                         "Adam layout, 32x32 tiles of every matrix at 32-row granularity")
     ap.add_argument("--tile-major", action="store_true",
                     help="store the TILE tensors tile by tile (TILEMAJOR): unpack and pack reorder through LDS")
     ap.add_argument("--packed-bf16", action="store_true",
@@ -372,7 +381,7 @@ def main():
     import torch
     import structure_aware_grouped_amd as rs
     from workloads.device import Inputs, garbage, tensor_bits
-    from workloads import Role, tensor_values, tile_major_variant, workload
+    from workloads import Role, adam_tile32_variant, tensor_values, tile_major_variant, workload
 
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
@@ -381,6 +390,11 @@ def main():
     w = workload(args.workload)
     if args.tile_major:
         w = tile_major_variant(w)
+    if args.adam_blocks == "tile32":
+        if args.workload != 4:
+            print("--adam-blocks applies to the Adam-state workload (4)", file=sys.stderr)
+            sys.exit(2)
+        w = adam_tile32_variant(w)
     specs = list(w.specs)
 
     t0 = time.perf_counter()
@@ -673,7 +687,8 @@ def main():
         check = "skipped (the Adam step is checked by tests/test_gpu_adam.py)"
     achieved = nbytes[dominant] / dom_avg_s / 1e9
     # counter summaries exist for the fp32 packed buffer only
-    traffic = None if args.packed_bf16 else read_traffic((args.workload, args.mode, bool(args.tile_major)), dominant)
+    traffic = None if args.packed_bf16 else read_traffic((args.workload, args.mode, bool(args.tile_major),
+                                                          args.adam_blocks), dominant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dominant, "algorithmic_bytes_per_launch": int(nbytes[dominant]),
@@ -701,10 +716,14 @@ def main():
     if args.mode == "adam8":
         names[4] = ("8-bit Adam states on the Llama-3-8B layer shapes, 2048-element blocks, V=64: one fused "
                     "AdamW step (dequant m, v; update fp32 params; requant m int8, v uint8)")
+    if args.adam_blocks == "tile32":
+        names[4] = names[4].replace("2048-element blocks", "32x32 tiles at 32-row granularity (norms: "
+                                                           "2048-element blocks)")
     metric = METRIC if (args.workload == 1 and args.mode == "step" and not args.tile_major
                         and not args.packed_bf16) else \
         f"DBuffer layout transform GB/s (workload {args.workload}, {args.mode}" + \
-        (", tile-major" if args.tile_major else "") + (", bf16 packed" if args.packed_bf16 else "") + ")"
+        (", tile-major" if args.tile_major else "") + (", bf16 packed" if args.packed_bf16 else "") + \
+        (", 32x32 Adam blocks" if args.adam_blocks == "tile32" else "") + ")"
     line = {
         "metric": metric,
         "value": round(value, 1),

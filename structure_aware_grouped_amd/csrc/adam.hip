@@ -156,6 +156,135 @@ __global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restr
   }
 }
 
+// Tiles of at most 1024 elements (the pages' 32x32 blocks): one wave per tile,
+// kAdamWaveTiles tiles per workgroup, the block's absmax a wave reduction
+// only (no LDS, no barrier). Tile jobs b*kAdamWaveTiles + wave.
+constexpr int kAdamWaveTiles = 4;
+
+//
+// Four 32x32 tiles side by side in one band (the usual case: the workgroup's
+// four jobs are consecutive tiles of a band) form a 32 x 128 strip whose rows
+// of 1-byte codes are whole 128-byte runs, while each tile alone has only 32
+// bytes of codes per row, a quarter of a line shared with three other tiles.
+// The workgroup then moves the strip's codes through LDS with 16-byte lane
+// accesses, eight lanes per 128-byte row, and each wave updates its own tile
+// from there; the fp32 parameters and gradients (128 bytes per tile row) go
+// straight to and from memory. Other groups of four jobs take one wave per
+// tile directly.
+constexpr int kStripRows = 32, kStripTileCols = 32, kStripCols = kAdamWaveTiles * kStripTileCols;
+
+// One 32x32 tile of a strip by one wave: codes read from and written back to
+// the strip's LDS copy (cm, cv: kStripRows rows of kStripCols bytes; this
+// tile's columns start at c0). The arithmetic and the order of every
+// operation are adam_block's.
+__device__ void adam_strip_tile(float* __restrict__ param, const float* __restrict__ grad, uint8_t* cm,
+                                uint8_t* cv, float* __restrict__ sm, float* __restrict__ sv, int64_t base,
+                                int64_t stride, int c0, int64_t sidx, int lane, const AdamK& k) {
+  constexpr int VPR = kStripTileCols / 4;           // 4-element vectors per tile row
+  constexpr int NV = kStripRows * VPR / kWave;      // vectors per lane
+  const float sm0 = sm[sidx], sv0 = sv[sidx];
+  f32x4 m1[NV], v1[NV];
+  uint32_t am = 0, av = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = lane + j * kWave, row = i / VPR, col = (i % VPR) * 4;
+    const int64_t e = base + row * stride + col;
+    const f32x4 p = ldg(reinterpret_cast<const f32x4*>(param + e));
+    const f32x4 g = ldg(reinterpret_cast<const f32x4*>(grad + e));
+    const f32x4 dm = decode4<FMT_I8, false>(*reinterpret_cast<const uint32_t*>(cm + row * kStripCols + c0 + col));
+    const f32x4 dv = decode4<FMT_U8, false>(*reinterpret_cast<const uint32_t*>(cv + row * kStripCols + c0 + col));
+    const float pin[4] = {p.x, p.y, p.z, p.w}, gin[4] = {g.x, g.y, g.z, g.w};
+    const float dmi[4] = {dm.x, dm.y, dm.z, dm.w}, dvi[4] = {dv.x, dv.y, dv.z, dv.w};
+    float po[4], mo[4], vo[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      adam_elem(pin[h], gin[h], __fmul_rn(dmi[h], sm0), __fmul_rn(dvi[h], sv0), k, po[h], mo[h], vo[h]);
+    m1[j] = f32x4{mo[0], mo[1], mo[2], mo[3]};
+    v1[j] = f32x4{vo[0], vo[1], vo[2], vo[3]};
+    stg(reinterpret_cast<f32x4*>(param + e), f32x4{po[0], po[1], po[2], po[3]});
+    am = max(am, max(max(__float_as_uint(mo[0]) & 0x7fffffffu, __float_as_uint(mo[1]) & 0x7fffffffu),
+                     max(__float_as_uint(mo[2]) & 0x7fffffffu, __float_as_uint(mo[3]) & 0x7fffffffu)));
+    av = max(av, max(max(__float_as_uint(vo[0]) & 0x7fffffffu, __float_as_uint(vo[1]) & 0x7fffffffu),
+                     max(__float_as_uint(vo[2]) & 0x7fffffffu, __float_as_uint(vo[3]) & 0x7fffffffu)));
+  }
+  const float amax_m = __uint_as_float(wave_max(am));
+  const float amax_v = __uint_as_float(wave_max(av));
+  float scm, rm, scv, rv;
+  block_scale(amax_m, 127.0f, scm, rm);
+  block_scale(amax_v, 255.0f, scv, rv);
+  if (lane == 0) {
+    sm[sidx] = scm;
+    sv[sidx] = scv;
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = lane + j * kWave, row = i / VPR, col = (i % VPR) * 4;
+    *reinterpret_cast<uint32_t*>(cm + row * kStripCols + c0 + col) = amax_m == 0.0f ? 0u
+        : encode4<FMT_I8, false>(__fmul_rn(m1[j].x, rm), __fmul_rn(m1[j].y, rm), __fmul_rn(m1[j].z, rm), __fmul_rn(m1[j].w, rm));
+    *reinterpret_cast<uint32_t*>(cv + row * kStripCols + c0 + col) = amax_v == 0.0f ? 0u
+        : encode4<FMT_U8, false>(__fmul_rn(v1[j].x, rv), __fmul_rn(v1[j].y, rv), __fmul_rn(v1[j].z, rv), __fmul_rn(v1[j].w, rv));
+  }
+}
+
+__global__ __launch_bounds__(kAdamWaveTiles * kWave) void adam_wave_tile_kernel(
+    const QJob* __restrict__ jobs, float* param, const float* grad, uint8_t* qm, float* sm, uint8_t* qv, float* sv,
+    AdamK k, unsigned n_jobs, unsigned n_groups) {
+  __shared__ __align__(16) uint8_t cm[kStripRows * kStripCols];
+  __shared__ __align__(16) uint8_t cv[kStripRows * kStripCols];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  for (unsigned gb = blockIdx.x; gb < n_groups; gb += gridDim.x) {
+    const unsigned t0 = piece_index<kTileXcdGroup>(gb, n_groups) * kAdamWaveTiles;
+    // a strip: four full 32x32 tiles of one tensor side by side, 16-byte aligned
+    // (every thread reads the four jobs, so the choice is the same for all waves)
+    bool strip = t0 + kAdamWaveTiles <= n_jobs;
+    const QJob j0 = jobs[min(t0, n_jobs - 1)];
+    strip = strip && j0.rows == kStripRows && j0.cols == kStripTileCols && j0.base % 16 == 0 && j0.stride % 16 == 0;
+#pragma unroll
+    for (int w = 1; w < kAdamWaveTiles; ++w) {
+      if (!strip) break;
+      const QJob jw = jobs[t0 + w];
+      strip = jw.tensor == j0.tensor && jw.rows == kStripRows && jw.cols == kStripTileCols &&
+              jw.stride == j0.stride && jw.base == j0.base + w * kStripTileCols && jw.scale == j0.scale + w;
+    }
+    if (!strip) {
+      const unsigned t = t0 + wave;
+      if (t < n_jobs) {
+        const QJob j = jobs[t];
+        adam_block<kWave, 4>(param, grad, qm, sm, qv, sv, j.base, j.stride, j.rows, j.cols, j.scale, lane, nullptr, k);
+      }
+      continue;
+    }
+    // codes of the strip in: thread i moves 16 bytes of row i / 8
+    const int row = threadIdx.x / (kStripCols / 16), chunk = threadIdx.x % (kStripCols / 16);
+    const int64_t ge = j0.base + row * j0.stride + chunk * 16;
+    *reinterpret_cast<u32x4*>(cm + row * kStripCols + chunk * 16) = ldg(reinterpret_cast<const u32x4*>(qm + ge));
+    *reinterpret_cast<u32x4*>(cv + row * kStripCols + chunk * 16) = ldg(reinterpret_cast<const u32x4*>(qv + ge));
+    __syncthreads();
+    adam_strip_tile(param, grad, cm, cv, sm, sv, j0.base + wave * kStripTileCols, j0.stride, wave * kStripTileCols,
+                    j0.scale + wave, lane, k);
+    __syncthreads();
+    stg(reinterpret_cast<u32x4*>(qm + ge), *reinterpret_cast<const u32x4*>(cm + row * kStripCols + chunk * 16));
+    stg(reinterpret_cast<u32x4*>(qv + ge), *reinterpret_cast<const u32x4*>(cv + row * kStripCols + chunk * 16));
+    __syncthreads();   // the next group reuses the LDS copy
+  }
+}
+
+// Tiles of up to 16384 elements (128x128): 1024 threads per tile, four
+// 4-element vectors each in registers.
+constexpr int kAdamBigTileThreads = 1024;
+
+__global__ __launch_bounds__(kAdamBigTileThreads) void adam_big_tile_kernel(
+    const QJob* __restrict__ jobs, float* param, const float* grad, uint8_t* qm, float* sm, uint8_t* qv, float* sv,
+    AdamK k, unsigned n_jobs) {
+  __shared__ uint32_t red[2 * kAdamBigTileThreads / kWave];
+  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
+    const QJob j = jobs[piece_index<kTileXcdGroup>(jb, n_jobs)];
+    adam_block<kAdamBigTileThreads, 4>(param, grad, qm, sm, qv, sv, j.base, j.stride, j.rows, j.cols, j.scale,
+                                       threadIdx.x, red, k);
+    __syncthreads();   // the next job reuses this workgroup's LDS
+  }
+}
+
 __device__ __forceinline__ void adam_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, float* param,
                                                              const float* grad, uint8_t* qm, float* sm,
                                                              uint8_t* qv, float* sv, AdamK k) {
@@ -209,9 +338,19 @@ extern "C" int rs_adam8_step(rs_plan* p, float* param, const float* grad, void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* qmb = static_cast<uint8_t*>(q_m);
   uint8_t* qvb = static_cast<uint8_t*>(q_v);
-  if (p->n_qtile)
-    hipLaunchKernelGGL(adam_tile_kernel, grid_of(p, p->n_qtile), dim3(kThreads), 0, s, p->qjobs, param, grad, qmb, s_m,
-                       qvb, s_v, k, static_cast<unsigned>(p->n_qtile));
+  // tiles: the register path sized to the plan's largest tile (16-byte vectors of fp32)
+  const int64_t nt = p->n_qtile;
+  if (nt && p->adam_wave_tiles && p->max_tile_vec16 <= kWave * 4) {
+    const int64_t groups = (nt + kAdamWaveTiles - 1) / kAdamWaveTiles;
+    hipLaunchKernelGGL(adam_wave_tile_kernel, grid_of(p, groups), dim3(kAdamWaveTiles * kWave), 0, s, p->qjobs, param,
+                       grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(nt), static_cast<unsigned>(groups));
+  } else if (nt && p->max_tile_vec16 > kThreads * 4 && p->max_tile_vec16 <= kAdamBigTileThreads * 4) {
+    hipLaunchKernelGGL(adam_big_tile_kernel, grid_of(p, nt), dim3(kAdamBigTileThreads), 0, s, p->qjobs, param, grad,
+                       qmb, s_m, qvb, s_v, k, static_cast<unsigned>(nt));
+  } else if (nt) {
+    hipLaunchKernelGGL(adam_tile_kernel, grid_of(p, nt), dim3(kThreads), 0, s, p->qjobs, param, grad, qmb, s_m,
+                       qvb, s_v, k, static_cast<unsigned>(nt));
+  }
   if (p->n_qflat)
     hipLaunchKernelGGL(adam_flat_kernel, grid_of(p, p->n_qflat), dim3(kFlatThreads), 0, s, p->qjobs + p->n_qtile, param,
                        grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(p->n_qflat));

@@ -395,6 +395,8 @@ void lower_quant(const std::vector<Tensor>& t, int64_t top, QuantList* ql) {
           ql->jobs.push_back(j);
         }
       }
+      const int64_t v16 = br * ((bc * 4 + 15) / 16);
+      ql->max_tile_vec16 = static_cast<int32_t>(std::max<int64_t>(ql->max_tile_vec16, std::min<int64_t>(v16, 1 << 30)));
     } else if (x.kind == RS_FLAT) {
       const int64_t nblk = (x.n + x.p0 - 1) / x.p0;
       for (int64_t b0 = 0; b0 < nblk; b0 += kFlatPerGroup) {
@@ -542,6 +544,9 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
       if (std::strcmp(tmk, "lds") == 0) p->tm_unpack_lds = p->tm_pack_lds = true;
       if (std::strcmp(tmk, "direct") == 0) p->tm_unpack_lds = p->tm_pack_lds = false;
     }
+    // RS_ADAM_TILE_KERNEL=workgroup: the Adam step gives every tile a 256-thread
+    // workgroup even when one wave would hold it (=wave: the default choice)
+    if (const char* ak = std::getenv("RS_ADAM_TILE_KERNEL")) p->adam_wave_tiles = std::strcmp(ak, "workgroup") != 0;
     // RS_MAX_GRID=n caps every launch at n workgroups (rounded down to a
     // multiple of 8, at least 8), so the workgroups loop over work items; the
     // results do not change.

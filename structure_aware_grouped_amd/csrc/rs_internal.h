@@ -308,7 +308,7 @@ struct rs_plan {
   int64_t n_qjobs = 0;
   int64_t n_qtile = 0, n_qflat = 0, n_qzero = 0;
   int64_t n_qblocks = 0;
-  int32_t max_tile_vec16 = 0;  // largest tile, in 16-byte vectors of 4-byte input
+  int32_t max_tile_vec16 = 0;  // largest tile (TILE or TILEMAJOR), in 16-byte vectors of 4-byte input
   bool split_code_lines = false;  // neighbouring tiles share 128-byte lines of codes
   int64_t gather_split8 = 0;      // workgroups per gather run, 8 codes per vector (bf16 out)
   int64_t gather_split4 = 0;      // the same, 4 codes per vector (fp32 out)
@@ -328,4 +328,5 @@ struct rs_plan {
   bool tm_unpack_lds = true;   // tile-major unpack staged through LDS (else the direct kernel)
   bool tm_pack_lds = true;     // tile-major pack staged through LDS (else the direct kernel)
   int64_t max_grid = rs::kMaxGrid;   // workgroups per launch; beyond it workgroups loop over items
+  bool adam_wave_tiles = true;       // Adam step: one wave per tile when every tile fits one wave's registers
 };

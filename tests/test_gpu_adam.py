@@ -100,6 +100,48 @@ def test_steps_on_blocks_beyond_the_register_paths(gpu_lib):
     plan.close()
 
 
+# groups whose largest tile picks each register path of the tile step: 32x32 tiles (one wave a
+# tile, the pages' 8-bit Adam blocks), 64x64 (one 256-thread workgroup a tile), 128x128 (1024
+# threads a tile); each with ragged edge tiles, tiles whose width is not a multiple of 4 (the
+# two-pass path inside the same launch), a tile-major tensor, flat blocks and a row tensor
+TILE_PATHS = {
+    "32x32": [TensorSpec("t32", 256, 320, "TILE", 32, 32), TensorSpec("t32_ragged", 100, 70, "TILE", 32, 32),
+              TensorSpec("t32_odd", 40, 45, "TILE", 32, 32), TensorSpec("tm16", 32, 64, "TILEMAJOR", 16, 16),
+              TensorSpec("flat", 1, 5000, "FLAT", 2048), TensorSpec("norm", 300, 1, "ROWS", 1)],
+    "64x64": [TensorSpec("t64", 256, 320, "TILE", 64, 64), TensorSpec("t32", 64, 96, "TILE", 32, 32),
+              TensorSpec("t64_ragged", 130, 150, "TILE", 64, 64), TensorSpec("flat", 1, 5000, "FLAT", 2048)],
+    "128x128": [TensorSpec("t128", 384, 512, "TILE", 128, 128), TensorSpec("t128_ragged", 300, 400, "TILE", 128, 128),
+                TensorSpec("t128_odd", 130, 131, "TILE", 128, 128), TensorSpec("t32", 64, 96, "TILE", 32, 32),
+                TensorSpec("tm64", 128, 128, "TILEMAJOR", 64, 64), TensorSpec("flat", 1, 3000, "FLAT", 1024)],
+}
+
+
+@pytest.mark.parametrize("max_grid", [None, "8"])
+@pytest.mark.parametrize("paths", sorted(TILE_PATHS))
+def test_chained_steps_on_each_tile_register_path(gpu_lib, paths, max_grid, monkeypatch):
+    import structure_aware_grouped_amd as rs
+    if max_grid:
+        monkeypatch.setenv("RS_MAX_GRID", max_grid)
+    specs, V = TILE_PATHS[paths], 3
+    S, starts, _, _ = rs.rs_plan_build(specs, V)
+    plan = rs.rs_plan_load(specs, V, S, starts, V, 0)
+    rng = np.random.default_rng(len(paths))
+    total = V * S
+    param = rng.standard_normal(total).astype(np.float32)
+    m = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(total) * 1e-3) ** 2).astype(np.float32)
+    qm, sm = OT.block_quant(m, specs, starts, S, V, "i8")
+    qv, sv = OT.block_quant(v, specs, starts, S, V, "u8")
+    for h in HYPERS:
+        grad = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+        want = OA.adam8_step(param, grad, qm, sm, qv, sv, specs, starts, h)
+        got = _run(rs, plan, (param, grad, qm, sm, qv.astype(np.uint8), sv), h)
+        for g, wv, name in zip(got, want, ("param", "q_m", "s_m", "q_v", "s_v")):
+            assert np.array_equal(tensor_bits(g), np.asarray(wv).view(tensor_bits(g).dtype)), (paths, name, h.step)
+        param, qm, sm, qv, sv = want
+    plan.close()
+
+
 def test_zero_state_and_gradient_blocks(gpu_lib):
     import structure_aware_grouped_amd as rs
     specs = [TensorSpec("f", 1, 4096, "FLAT", 1024)]
@@ -119,11 +161,13 @@ def test_zero_state_and_gradient_blocks(gpu_lib):
     plan.close()
 
 
-def test_adam_workload_sampled_blocks(gpu_lib):
-    """One step on the full Adam-state workload; every element of 2000 sampled blocks
-    (and the first and last block of every tensor) against the oracle."""
+@pytest.mark.parametrize("blocks", ["flat2048", "tile32"])
+def test_adam_workload_sampled_blocks(gpu_lib, blocks):
+    """One step on the full Adam-state workload (2048-element flat blocks, or the pages'
+    32x32 tiles at 32-row granularity); every element of 2000 sampled blocks (and the first
+    and last block of every tensor) against the oracle."""
     import structure_aware_grouped_amd as rs
-    w = workload(4)
+    w = workload(4) if blocks == "flat2048" else W.adam_tile32_variant(workload(4))
     specs = list(w.specs)
     S, starts, _, _ = rs.rs_plan_build(specs, w.V)
     R = w.V

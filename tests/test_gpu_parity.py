@@ -525,3 +525,47 @@ def test_plan_reloaded_from_json(gpu_lib):
     assert all(np.array_equal(x, y) for x, y in zip(*res))
     a.close()
     b.close()
+
+
+# Tensors whose tile rows start inside 128-byte lines of codes, so neighbouring tiles (run by
+# different workgroups) write the two halves of a line: 2880-wide rows of 128x128 tiles (the
+# MoE layer's shape, 22 full tiles and a 64-wide edge tile a band, a partial last band), 8.5
+# tiles of 64x128, 256-wide tiles, 64-wide tiles, and a tile-major, a flat and a row tensor in
+# the same plan.
+SPLIT_LINES = [
+    TensorSpec("moe_like", 300, 2880, "TILE", 128, 128),
+    TensorSpec("eight_and_half", 130, 1088, "TILE", 64, 128),
+    TensorSpec("wide_tiles", 200, 1344, "TILE", 128, 256),
+    TensorSpec("narrow_tiles", 70, 200, "TILE", 32, 64),
+    TensorSpec("tm", 64, 128, "TILEMAJOR", 32, 32),
+    TensorSpec("flat", 1, 10000, "FLAT", 2048),
+    TensorSpec("norm", 2880, 1, "ROWS", 1),
+]
+
+
+@pytest.mark.parametrize("max_grid", [None, "16"])
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_quant_of_tiles_that_share_lines_of_codes(gpu_lib, max_grid, pdtype, monkeypatch):
+    """Codes and scales bit for bit against the oracle in every format when neighbouring
+    tiles share 128-byte lines of codes (the MoE-shaped band, the partial last band, the
+    edge tiles); RS_MAX_GRID=16 once, so workgroups loop over tiles."""
+    import structure_aware_grouped_amd as rs
+    if max_grid:
+        monkeypatch.setenv("RS_MAX_GRID", max_grid)
+    V = 5
+    plan = _plan(rs, SPLIT_LINES, V)
+    R, S = plan.R_mat, plan.S
+    total = R * S
+    rng = _rng(300 + (16 if max_grid else 0) + (1 if pdtype == torch.bfloat16 else 0))
+    for fmt in ("e4m3", "i8", "u8"):
+        src_dev, src_h, _ = _flat_input(rng, plan, pdtype, scale=0.3, positive=(fmt == "u8"))
+        qwhole, q = guarded(total, torch.uint8, DEV)
+        q.fill_(0x5A)
+        swhole, scales = guarded(plan.n_qblocks, torch.float32, DEV)
+        rs.rs_block_quant(plan, src_dev, q, fmt, scales)
+        torch.cuda.synchronize()
+        wq, ws = OT.block_quant(src_h, SPLIT_LINES, plan.starts, S, R, fmt)
+        assert np.array_equal(tensor_bits(q), wq), fmt
+        assert np.array_equal(tensor_bits(scales), ws.view(np.uint32)), fmt
+        assert guard_intact(qwhole, total) and guard_intact(swhole, plan.n_qblocks)
+    plan.close()

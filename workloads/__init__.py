@@ -6,7 +6,8 @@ method's arithmetic (no granularities, plans, scaling or quantisation), so
 both the CPU oracle and the HIP path can take their inputs from it without
 sharing any of the computation.
 """
-from .configs import TensorSpec, Workload, WORKLOADS, workload, tiny_variant, tile_major_variant
+from .configs import (TensorSpec, Workload, WORKLOADS, adam_tile32_variant, workload, tiny_variant,
+                      tile_major_variant)
 from .gen import (
     Role,
     seed_key,
@@ -24,7 +25,7 @@ from .gen import (
 )
 
 __all__ = [
-    "TensorSpec", "Workload", "WORKLOADS", "workload", "tiny_variant", "tile_major_variant",
+    "TensorSpec", "Workload", "WORKLOADS", "workload", "tiny_variant", "tile_major_variant", "adam_tile32_variant",
     "Role", "seed_key", "normal_f32", "uniform_f32", "bf16_bits_from_f32",
     "f32_from_bf16_bits", "draw", "tensor_values", "weight_bits", "prev_slice",
     "adam_state", "parallel_map", "worker_count",

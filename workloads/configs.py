@@ -146,6 +146,15 @@ def tiny_variant(base: Workload, **changes) -> Workload:
     return replace(base, **changes)
 
 
+def adam_tile32_variant(w: Workload) -> Workload:
+    """The Adam-state workload with the pages' own 8-bit Adam blocks: every matrix in
+    32x32 tiles (so 32-row rank granularity), 1-D tensors in 2048-element flat blocks."""
+    specs = tuple(TensorSpec(s.name, s.rows, s.cols, "TILE", 32, 32) if s.rows > 1 and s.cols > 1 else s
+                  for s in w.specs)
+    return replace(w, specs=specs, name=w.name.replace("2048-element flat blocks",
+                                                       "32x32 tiles (1-D tensors: 2048-element flat blocks)"))
+
+
 def tile_major_variant(w: Workload) -> Workload:
     """The same workload with every TILE tensor stored tile by tile (TILEMAJOR, same tiles)."""
     specs = tuple(TensorSpec(s.name, s.rows, s.cols, "TILEMAJOR", s.p0, s.p1) if s.kind == "TILE" else s
