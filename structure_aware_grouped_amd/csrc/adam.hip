@@ -40,9 +40,11 @@ __device__ __forceinline__ void block_scale(float amax, float Q, float& scale, f
 // One quantisation block (element (r, c) at base + r*stride + c) handled by
 // NT threads. The old scales are read before the block's max is reduced and
 // the new ones written after it. Fast path: 4-element vectors, every updated
-// m and v kept in registers; otherwise two passes (the second recomputes m1
-// and v1 from the old codes, which it then overwrites).
-template <int NT, int MAXV>
+// m and v kept in registers, the loads issued B vectors at a time; otherwise
+// two passes (the second recomputes m1 and v1 from the old codes, which it
+// then overwrites). B = 1: batches of 4 vectors made the flat-block step 2-3%
+// slower on gfx950 (more registers, fewer waves), so they are not used.
+template <int NT, int MAXV, int B = 1>
 __device__ void adam_block(float* __restrict__ param, const float* __restrict__ grad,
                            uint8_t* __restrict__ qm, float* __restrict__ sm, uint8_t* __restrict__ qv,
                            float* __restrict__ sv, int64_t base, int64_t stride, int rows, int cols,
@@ -54,16 +56,29 @@ __device__ void adam_block(float* __restrict__ param, const float* __restrict__ 
     f32x4 m1[MAXV], v1[MAXV];
     uint32_t am = 0, av = 0;
     GridWalk w(tid, vpr, NT);
+    // vectors in batches of B: every load of a batch is issued before the first is
+    // used (a lane past the block reads the block's first vector and ignores it)
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-      if (tid + j * NT < nvec) {
-        const int64_t e = base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 4;
-        const f32x4 p = ldg(reinterpret_cast<const f32x4*>(param + e));
-        const f32x4 g = ldg(reinterpret_cast<const f32x4*>(grad + e));
-        const uint32_t cm = ldg(reinterpret_cast<const uint32_t*>(qm + e));
-        const uint32_t cv = ldg(reinterpret_cast<const uint32_t*>(qv + e));
-        const f32x4 dm = decode4<FMT_I8, false>(cm), dv = decode4<FMT_U8, false>(cv);
-        const float pin[4] = {p.x, p.y, p.z, p.w}, gin[4] = {g.x, g.y, g.z, g.w};
+    for (int j0 = 0; j0 < MAXV; j0 += B) {
+      f32x4 p[B], g[B];
+      uint32_t cm[B], cv[B];
+      int64_t at[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        at[b] = tid + (j0 + b) * NT < nvec
+                    ? base + static_cast<int64_t>(w.row) * stride + static_cast<int64_t>(w.col) * 4 : base;
+        p[b] = ldg(reinterpret_cast<const f32x4*>(param + at[b]));
+        g[b] = ldg(reinterpret_cast<const f32x4*>(grad + at[b]));
+        cm[b] = ldg(reinterpret_cast<const uint32_t*>(qm + at[b]));
+        cv[b] = ldg(reinterpret_cast<const uint32_t*>(qv + at[b]));
+        w.next();
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int j = j0 + b;
+        if (tid + j * NT >= nvec) continue;
+        const f32x4 dm = decode4<FMT_I8, false>(cm[b]), dv = decode4<FMT_U8, false>(cv[b]);
+        const float pin[4] = {p[b].x, p[b].y, p[b].z, p[b].w}, gin[4] = {g[b].x, g[b].y, g[b].z, g[b].w};
         const float dmi[4] = {dm.x, dm.y, dm.z, dm.w}, dvi[4] = {dv.x, dv.y, dv.z, dv.w};
         float po[4], mo[4], vo[4];
 #pragma unroll
@@ -71,13 +86,12 @@ __device__ void adam_block(float* __restrict__ param, const float* __restrict__ 
           adam_elem(pin[h], gin[h], __fmul_rn(dmi[h], sm0), __fmul_rn(dvi[h], sv0), k, po[h], mo[h], vo[h]);
         m1[j] = f32x4{mo[0], mo[1], mo[2], mo[3]};
         v1[j] = f32x4{vo[0], vo[1], vo[2], vo[3]};
-        stg(reinterpret_cast<f32x4*>(param + e), f32x4{po[0], po[1], po[2], po[3]});
+        stg(reinterpret_cast<f32x4*>(param + at[b]), f32x4{po[0], po[1], po[2], po[3]});
         am = max(am, max(max(__float_as_uint(m1[j].x) & 0x7fffffffu, __float_as_uint(m1[j].y) & 0x7fffffffu),
                          max(__float_as_uint(m1[j].z) & 0x7fffffffu, __float_as_uint(m1[j].w) & 0x7fffffffu)));
         av = max(av, max(max(__float_as_uint(v1[j].x) & 0x7fffffffu, __float_as_uint(v1[j].y) & 0x7fffffffu),
                          max(__float_as_uint(v1[j].z) & 0x7fffffffu, __float_as_uint(v1[j].w) & 0x7fffffffu)));
       }
-      w.next();
     }
     const float amax_m = __uint_as_float(group_max<NT>(am, tid, red));
     const float amax_v = __uint_as_float(group_max<NT>(av, tid, NT > kWave ? red + NT / kWave : nullptr));
@@ -177,11 +191,28 @@ constexpr int kStripRows = 32, kStripTileCols = 32, kStripCols = kAdamWaveTiles 
 // the strip's LDS copy (cm, cv: kStripRows rows of kStripCols bytes; this
 // tile's columns start at c0). The arithmetic and the order of every
 // operation are adam_block's.
-__device__ void adam_strip_tile(float* __restrict__ param, const float* __restrict__ grad, uint8_t* cm,
-                                uint8_t* cv, float* __restrict__ sm, float* __restrict__ sv, int64_t base,
-                                int64_t stride, int c0, int64_t sidx, int lane, const AdamK& k) {
-  constexpr int VPR = kStripTileCols / 4;           // 4-element vectors per tile row
-  constexpr int NV = kStripRows * VPR / kWave;      // vectors per lane
+constexpr int kStripVPR = kStripTileCols / 4;             // 4-element vectors per tile row
+constexpr int kStripNV = kStripRows * kStripVPR / kWave;  // vectors per lane
+
+// Parameters and gradients of one lane's vectors of a strip tile, loaded
+// while the workgroup stages the strip's codes.
+__device__ __forceinline__ void adam_strip_loads(const float* __restrict__ param, const float* __restrict__ grad,
+                                                 int64_t base, int64_t stride, int lane, f32x4 (&p)[kStripNV],
+                                                 f32x4 (&g)[kStripNV]) {
+#pragma unroll
+  for (int j = 0; j < kStripNV; ++j) {
+    const int i = lane + j * kWave, row = i / kStripVPR, col = (i % kStripVPR) * 4;
+    const int64_t e = base + row * stride + col;
+    p[j] = ldg(reinterpret_cast<const f32x4*>(param + e));
+    g[j] = ldg(reinterpret_cast<const f32x4*>(grad + e));
+  }
+}
+
+__device__ void adam_strip_tile(float* __restrict__ param, const f32x4 (&pv)[kStripNV], const f32x4 (&gv)[kStripNV],
+                                uint8_t* cm, uint8_t* cv, float* __restrict__ sm, float* __restrict__ sv,
+                                int64_t base, int64_t stride, int c0, int64_t sidx, int lane, const AdamK& k) {
+  constexpr int VPR = kStripVPR;
+  constexpr int NV = kStripNV;
   const float sm0 = sm[sidx], sv0 = sv[sidx];
   f32x4 m1[NV], v1[NV];
   uint32_t am = 0, av = 0;
@@ -189,8 +220,8 @@ __device__ void adam_strip_tile(float* __restrict__ param, const float* __restri
   for (int j = 0; j < NV; ++j) {
     const int i = lane + j * kWave, row = i / VPR, col = (i % VPR) * 4;
     const int64_t e = base + row * stride + col;
-    const f32x4 p = ldg(reinterpret_cast<const f32x4*>(param + e));
-    const f32x4 g = ldg(reinterpret_cast<const f32x4*>(grad + e));
+    const f32x4 p = pv[j];
+    const f32x4 g = gv[j];
     const f32x4 dm = decode4<FMT_I8, false>(*reinterpret_cast<const uint32_t*>(cm + row * kStripCols + c0 + col));
     const f32x4 dv = decode4<FMT_U8, false>(*reinterpret_cast<const uint32_t*>(cv + row * kStripCols + c0 + col));
     const float pin[4] = {p.x, p.y, p.z, p.w}, gin[4] = {g.x, g.y, g.z, g.w};
@@ -257,11 +288,15 @@ __global__ __launch_bounds__(kAdamWaveTiles * kWave) void adam_wave_tile_kernel(
     // codes of the strip in: thread i moves 16 bytes of row i / 8
     const int row = threadIdx.x / (kStripCols / 16), chunk = threadIdx.x % (kStripCols / 16);
     const int64_t ge = j0.base + row * j0.stride + chunk * 16;
-    *reinterpret_cast<u32x4*>(cm + row * kStripCols + chunk * 16) = ldg(reinterpret_cast<const u32x4*>(qm + ge));
-    *reinterpret_cast<u32x4*>(cv + row * kStripCols + chunk * 16) = ldg(reinterpret_cast<const u32x4*>(qv + ge));
+    const u32x4 codes_m = ldg(reinterpret_cast<const u32x4*>(qm + ge));
+    const u32x4 codes_v = ldg(reinterpret_cast<const u32x4*>(qv + ge));
+    f32x4 pv[kStripNV], gv[kStripNV];
+    const int64_t tb = j0.base + wave * kStripTileCols;
+    adam_strip_loads(param, grad, tb, j0.stride, lane, pv, gv);
+    *reinterpret_cast<u32x4*>(cm + row * kStripCols + chunk * 16) = codes_m;
+    *reinterpret_cast<u32x4*>(cv + row * kStripCols + chunk * 16) = codes_v;
     __syncthreads();
-    adam_strip_tile(param, grad, cm, cv, sm, sv, j0.base + wave * kStripTileCols, j0.stride, wave * kStripTileCols,
-                    j0.scale + wave, lane, k);
+    adam_strip_tile(param, pv, gv, cm, cv, sm, sv, tb, j0.stride, wave * kStripTileCols, j0.scale + wave, lane, k);
     __syncthreads();
     stg(reinterpret_cast<u32x4*>(qm + ge), *reinterpret_cast<const u32x4*>(cm + row * kStripCols + chunk * 16));
     stg(reinterpret_cast<u32x4*>(qv + ge), *reinterpret_cast<const u32x4*>(cv + row * kStripCols + chunk * 16));
