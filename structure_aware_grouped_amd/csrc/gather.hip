@@ -199,15 +199,15 @@ __global__ __launch_bounds__(kFlatThreads) void gather_flat_kernel(const QJob* _
 
 // Gather side of a tile-major tensor, over the same strips: each lane turns
 // VEC codes of one tile row into one 16-byte store of the row-major tensor
-// (8 codes -> 8 bf16, 4 -> 4 fp32), kGatherVec vectors per thread; tile t of
-// the strip uses scale scale0 + t.
+// (8 codes -> 8 bf16, 4 -> 4 fp32), kGatherTmVec vectors per thread; tile t
+// of the strip uses scale scale0 + t.
 template <int FMT, bool HW, bool BF16OUT>
 __device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* __restrict__ jobs,
                                                                   const uint8_t* __restrict__ q,
                                                                   const float* __restrict__ scales,
                                                                   void* const* __restrict__ dst, int split) {
   constexpr int VEC = BF16OUT ? 8 : 4;
-  constexpr int U = kGatherVec;
+  constexpr int U = kGatherTmVec;
   const unsigned ju = b / static_cast<unsigned>(split);
   const int ji = static_cast<int>(ju);
   const int piece = static_cast<int>(b - ju * static_cast<unsigned>(split));
@@ -216,11 +216,11 @@ __device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* 
   const uint32_t mbc = magic_u16(bc);
   const uint8_t* qb = q + j.base;
   void* out = dst[j.tensor];
-  const int pass = split * static_cast<int>(kGatherPiece);
+  const int pass = split * static_cast<int>(kGatherTmPiece);
   if (bc % VEC == 0 && j.cols % VEC == 0) {
     const uint32_t wv = width / VEC, mw = magic_u16(wv);
     const int nvec = j.h * static_cast<int>(wv);
-    for (int i0 = piece * static_cast<int>(kGatherPiece) + static_cast<int>(threadIdx.x); i0 < nvec; i0 += pass) {
+    for (int i0 = piece * static_cast<int>(kGatherTmPiece) + static_cast<int>(threadIdx.x); i0 < nvec; i0 += pass) {
       uint32_t code[U][VEC / 4];
       float sc[U];
       int64_t dpos[U];
@@ -266,10 +266,10 @@ __device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* 
     }
     return;
   }
-  // element path: a piece is kGatherPiece elements, U per thread
+  // element path: a piece is kGatherTmPiece elements, U per thread
   const int n = j.h * static_cast<int>(width);
   const uint32_t mw = magic_u16(width);
-  for (int e0 = piece * static_cast<int>(kGatherPiece) + static_cast<int>(threadIdx.x); e0 < n; e0 += pass) {
+  for (int e0 = piece * static_cast<int>(kGatherTmPiece) + static_cast<int>(threadIdx.x); e0 < n; e0 += pass) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = e0 + u * kGatherThreads;
@@ -322,7 +322,7 @@ void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipS
     hipLaunchKernelGGL((gather_flat_kernel<FMT, HW, BF16OUT>), grid_of(p, p->n_gflat), dim3(kFlatThreads), 0, s, flats, q,
                        scales, p->gdst.dev, static_cast<unsigned>(p->n_gflat));
   if (p->n_tm) {
-    const int64_t split = tm_pieces(p->tm_max_strip, BF16OUT ? 8 : 4, kGatherPiece);
+    const int64_t split = tm_pieces(p->tm_max_strip, BF16OUT ? 8 : 4, kGatherTmPiece);
     const int64_t n = p->n_tm * split;
     hipLaunchKernelGGL((gather_tm_kernel<FMT, HW, BF16OUT>), grid_of(p, n), dim3(kGatherThreads), 0, s, p->tmjobs, q,
                        scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));

@@ -252,6 +252,14 @@ constexpr int64_t kGatherMaxCols = 16384;           // widest TILE tensor handle
 #endif
 constexpr int kGatherThreads = RS_GATHER_THREADS, kGatherVec = RS_GATHER_VEC;
 constexpr int64_t kGatherPiece = int64_t(kGatherThreads) * kGatherVec;
+// The gather side of tile-major strips keeps 4 vectors per thread: against 2,
+// 5.38-5.42 -> 5.62-5.64 TB/s cold on the 8B layer stored tile-major (row runs
+// keep 2: 4 cost the MoE layer's runs 9%).
+#ifndef RS_GATHER_TM_VEC
+#define RS_GATHER_TM_VEC 4
+#endif
+constexpr int kGatherTmVec = RS_GATHER_TM_VEC;
+constexpr int64_t kGatherTmPiece = int64_t(kGatherThreads) * kGatherTmVec;
 // the longest run: kGatherMaxPieces pieces of 8-code vectors, or one row of
 // kGatherMaxCols codes; as 4-code vectors its indices stay under 2^16
 constexpr int64_t kGatherMaxRun = std::max<int64_t>(kGatherMaxPieces * kGatherPiece * 8, kGatherMaxCols);
