@@ -88,9 +88,10 @@ def parse():
                          "(fill) or read (a sum over it, which leaves no dirty lines behind)")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with default HIP events (system-scope fence at every record)")
-    ap.add_argument("--copy-mib", type=int, default=1024,
+    ap.add_argument("--copy-mib", type=int, default=-1,
                     help="size of the streaming copy (rs_bench_copy) timed as the practical ceiling "
-                         "(and used to calibrate HBM byte counters); 0 disables it")
+                         "(and used to calibrate HBM byte counters); -1 (default): the copy moves as many "
+                         "bytes as the dominant kernel (reads + writes), 0 disables it")
     return ap.parse_args()
 
 
@@ -531,7 +532,8 @@ def main():
         # benchmark helper), timed like the kernels; its counter readings calibrate
         # FETCH_SIZE / WRITE_SIZE. torch's own device copy is timed beside it for context.
         blib = bench_lib()
-        nb = args.copy_mib << 20
+        # same size as the dominant kernel: it reads and writes half its bytes each
+        nb = args.copy_mib << 20 if args.copy_mib > 0 else max(1 << 20, int(nbytes[dominant]) // 2 // 1024 * 1024)
         src_c = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
         dst_c = torch.empty_like(src_c)
 
@@ -547,6 +549,8 @@ def main():
         med = float(np.median(ms))
         tms = flushed_launches(lambda: dst_c.copy_(src_c), 5)
         copy = {"kernel": "rs_bench_copy: 16-byte nontemporal loads and stores, 64-thread workgroups of 1 KiB",
+                "size": (f"{nb / 2**20:.0f} MiB copied: the {dominant} kernel's bytes" if args.copy_mib < 0
+                         else f"{nb / 2**20:.0f} MiB copied"),
                 "bytes": 2 * nb, "median_ms": round(med, 5), "GBps": round(2 * nb / (med * 1e-3) / 1e9, 1),
                 "torch_copy_GBps": round(2 * nb / (float(np.median(tms)) * 1e-3) / 1e9, 1),
                 "timing": f"median of {args.steps} flushed launches"}
@@ -700,6 +704,8 @@ def main():
     cpu = None
     if args.cpu_sample and not w.adam_states and args.mode == "step":
         cpu = cpu_baseline(w, plan, tile_major=bool(args.tile_major))
+        cpu["gpu_over_cpu"] = round(value / cpu["value"], 1)
+        cpu["gpu_over_single_core"] = round(value / cpu["single_core"]["value"], 1)
         log(f"CPU oracle: {cpu['sample']}")
 
     names = {0: "tiny group (64x48 1-row blocks, 100x32 16x16 tiles, 7x130 elements; fp32), V=4: unpack + "

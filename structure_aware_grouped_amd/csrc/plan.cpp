@@ -496,7 +496,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     // and piece indices are 32-bit. Under the 2^39-element limit this holds
     // for any plan but one made of tiny tiles.
     const int64_t items = std::max({static_cast<int64_t>(tb.unpack.size()) * unpack_split(4),
-                                    static_cast<int64_t>(tb.pack.size()) * kPackSplit,
+                                    static_cast<int64_t>(tb.pack.size()) * std::max(kPackSplit, kPack1Split),
                                     static_cast<int64_t>(tb.gchunks.size()) * tb.gather_split4,
                                     static_cast<int64_t>(tb.tm.size()) * tm_pieces(tb.tm_max_strip, 4, kTmThreads),
                                     static_cast<int64_t>(tb.qjobs.size()), static_cast<int64_t>(tb.gjobs.size())});

@@ -47,13 +47,26 @@ static_assert(kUnpackChunk % 16 == 0 && kPackChunk % 16 == 0, "work items keep 1
 #ifndef RS_PACK_VEC
 #define RS_PACK_VEC 1
 #endif
+// A pack that does not accumulate (one read and one write stream, the shape
+// of unpack) is fastest with unpack's shape too: 64 threads, plain
+// round-robin over the XCDs. On the Adam-state workload's 1.75 GB packs,
+// interleaved and cold: 5.88-5.94 TB/s with the accumulating pack's 128
+// threads and runs of 256, 6.04-6.09 with 128 threads round-robin, 6.25-6.28
+// with 64 round-robin. The accumulating pack kept its shape: 64 threads
+// round-robin gave it +0.5% cold and -2.5% warm on the 8B layer.
+#ifndef RS_PACK1_THREADS
+#define RS_PACK1_THREADS 64
+#endif
 constexpr int kUnpackThreads = RS_UNPACK_THREADS, kUnpackVec = RS_UNPACK_VEC;
 constexpr int kPackThreads = RS_PACK_THREADS, kPackVec = RS_PACK_VEC;
+constexpr int kPack1Threads = RS_PACK1_THREADS;
 constexpr int64_t kUnpackPiece = int64_t(kUnpackThreads) * kUnpackVec;   // vectors per workgroup
-constexpr int64_t kPackPiece = int64_t(kPackThreads) * kPackVec;         // output vectors per workgroup
-// pieces per unpack item for element size eb; per pack item (fp32 output)
+// pieces per unpack item for element size eb; per pack item (fp32 output) for
+// a pack workgroup of nt threads
 constexpr int64_t unpack_split(int64_t eb) { return (kUnpackChunk * eb / 16 + kUnpackPiece - 1) / kUnpackPiece; }
-constexpr int64_t kPackSplit = (kPackChunk / 4 + kPackPiece - 1) / kPackPiece;
+constexpr int64_t pack_split(int nt) { return (kPackChunk / 4 + int64_t(nt) * kPackVec - 1) / (int64_t(nt) * kPackVec); }
+constexpr int64_t kPackSplit = pack_split(kPackThreads);
+constexpr int64_t kPack1Split = pack_split(kPack1Threads);
 // Consecutive pieces of a split launch kept on one XCD (1: plain round-robin).
 // Pack, with three streams, gains from runs of 256 pieces (512 KiB of output)
 // per XCD: 6.52 -> 6.67 TB/s on the Llama-3-8B layer, 5.97 -> 6.59 TB/s on the
@@ -67,11 +80,15 @@ constexpr int64_t kPackSplit = (kPackChunk / 4 + kPackPiece - 1) / kPackPiece;
 #ifndef RS_PACK_XCD_GROUP
 #define RS_PACK_XCD_GROUP 256
 #endif
+#ifndef RS_PACK1_XCD_GROUP
+#define RS_PACK1_XCD_GROUP 1
+#endif
 #ifndef RS_GATHER_XCD_GROUP
 #define RS_GATHER_XCD_GROUP 128
 #endif
 constexpr unsigned kUnpackXcdGroup = RS_UNPACK_XCD_GROUP;
 constexpr unsigned kPackXcdGroup = RS_PACK_XCD_GROUP;
+constexpr unsigned kPack1XcdGroup = RS_PACK1_XCD_GROUP;   // pack without accumulation
 constexpr unsigned kGatherXcdGroup = RS_GATHER_XCD_GROUP;
 // the same for the per-block kernels (quant, dequant, Adam): consecutive tiles
 // per XCD (4: tile quant 5.98 -> 6.32 TB/s on the 8B layer), consecutive

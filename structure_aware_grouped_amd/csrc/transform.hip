@@ -94,24 +94,26 @@ __device__ __forceinline__ void store_packed1(void* out, int64_t pos, float y) {
 }
 
 // packed = acc ? prev + src*sigma : src*sigma on tensor data, +0.0 on padding.
-// Workgroup b writes piece b % kPackSplit (kPackPiece output vectors) of
-// chunk b / kPackSplit. `prev` may alias `out`: every element is read before
-// it is written, by the same thread (fp32 output only).
-template <bool BF16, bool ACC, bool OB>
+// Workgroup b (NT threads) writes piece b % split (NT * kPackVec output
+// vectors) of chunk b / split, split = pack_split(NT). `prev` may alias `out`:
+// every element is read before it is written, by the same thread (fp32 output
+// only).
+template <bool BF16, bool ACC, bool OB, int NT>
 __device__ __forceinline__ void pack_kernel_piece(unsigned b, const PackChunk* __restrict__ chunks,
                                                              const void* const* __restrict__ src,
                                                              const float* prev, void* out, float sigma) {
-  const unsigned cu = b / static_cast<unsigned>(kPackSplit);
+  constexpr unsigned kSplit = static_cast<unsigned>(pack_split(NT));
+  const unsigned cu = b / kSplit;
   const int ci = static_cast<int>(cu);
-  const int piece = static_cast<int>(b - cu * static_cast<unsigned>(kPackSplit));
+  const int piece = static_cast<int>(b - cu * kSplit);
   const PackChunk c = chunks[ci];
   const int nv = c.n_total >> 2;
-  const int v0 = piece * static_cast<int>(kPackPiece) + static_cast<int>(threadIdx.x);
+  const int v0 = piece * NT * kPackVec + static_cast<int>(threadIdx.x);
   if (c.tensor < 0) {
 #pragma unroll
     for (int u = 0; u < kPackVec; ++u)
-      if (v0 + u * kPackThreads < nv)
-        store_packed4<OB>(out, c.out + 4 * static_cast<int64_t>(v0 + u * kPackThreads), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+      if (v0 + u * NT < nv)
+        store_packed4<OB>(out, c.out + 4 * static_cast<int64_t>(v0 + u * NT), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
     return;
   }
   const void* g = src[c.tensor];
@@ -120,7 +122,7 @@ __device__ __forceinline__ void pack_kernel_piece(unsigned b, const PackChunk* _
   f32x4 gv[kPackVec], pv[kPackVec];
 #pragma unroll
   for (int u = 0; u < kPackVec; ++u) {
-    const int i = v0 + u * kPackThreads;
+    const int i = v0 + u * NT;
     if (i < nv && 4 * i + 4 <= nd) {
       gv[u] = load4<BF16>(g, c.off + 4 * i);
       if constexpr (ACC) pv[u] = ldg(p4 + i);
@@ -128,7 +130,7 @@ __device__ __forceinline__ void pack_kernel_piece(unsigned b, const PackChunk* _
   }
 #pragma unroll
   for (int u = 0; u < kPackVec; ++u) {
-    const int i = v0 + u * kPackThreads;
+    const int i = v0 + u * NT;
     if (i >= nv) continue;
     f32x4 y;
     if (4 * i + 4 <= nd) {
@@ -161,12 +163,23 @@ __device__ __forceinline__ void pack_kernel_piece(unsigned b, const PackChunk* _
   }
 }
 
+// Workgroup shape: the accumulating pack kPackThreads threads, runs of
+// kPackXcdGroup pieces per XCD; without accumulation kPack1Threads, runs of
+// kPack1XcdGroup.
+template <bool ACC>
+struct PackShape {
+  static constexpr int NT = ACC ? kPackThreads : kPack1Threads;
+  static constexpr unsigned XG = ACC ? kPackXcdGroup : kPack1XcdGroup;
+};
+
 template <bool BF16, bool ACC, bool OB>
-__global__ __launch_bounds__(kPackThreads) void pack_kernel(const PackChunk* __restrict__ chunks,
-                                                             const void* const* __restrict__ src,
-                                                             const float* prev, void* out, float sigma, unsigned n_pieces) {
+__global__ __launch_bounds__(PackShape<ACC>::NT) void pack_kernel(const PackChunk* __restrict__ chunks,
+                                                                  const void* const* __restrict__ src,
+                                                                  const float* prev, void* out, float sigma,
+                                                                  unsigned n_pieces) {
+  using Sh = PackShape<ACC>;
   for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
-    pack_kernel_piece<BF16, ACC, OB>(piece_index<kPackXcdGroup>(p, n_pieces), chunks, src, prev, out, sigma);
+    pack_kernel_piece<BF16, ACC, OB, Sh::NT>(piece_index<Sh::XG>(p, n_pieces), chunks, src, prev, out, sigma);
 }
 
 // ------------------------------------------------------------------ tile-major layout
@@ -449,9 +462,9 @@ namespace {
 template <bool BF16, bool ACC, bool OB>
 void launch_pack(const rs_plan* p, void** tab, const float* prev, void* packed, float sigma, hipStream_t s) {
   if (p->n_pack) {
-    const int64_t n_pieces = p->n_pack * kPackSplit;
-    hipLaunchKernelGGL((pack_kernel<BF16, ACC, OB>), grid_of(p, n_pieces), dim3(kPackThreads), 0, s, p->pack, tab,
-                       prev, packed, sigma, static_cast<unsigned>(n_pieces));
+    const int64_t n_pieces = p->n_pack * pack_split(PackShape<ACC>::NT);
+    hipLaunchKernelGGL((pack_kernel<BF16, ACC, OB>), grid_of(p, n_pieces), dim3(PackShape<ACC>::NT), 0, s, p->pack,
+                       tab, prev, packed, sigma, static_cast<unsigned>(n_pieces));
   }
   if (p->n_tm && !p->tm_pack_lds) {
     const int64_t split = tm_pieces(p->tm_max_strip, 4, kTmThreads);
