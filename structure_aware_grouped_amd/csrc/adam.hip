@@ -42,8 +42,8 @@ __device__ __forceinline__ void block_scale(float amax, float Q, float& scale, f
 // the new ones written after it. Fast path: 4-element vectors, every updated
 // m and v kept in registers, the loads issued B vectors at a time; otherwise
 // two passes (the second recomputes m1 and v1 from the old codes, which it
-// then overwrites). B = 1: batches of 4 vectors made the flat-block step 2-3%
-// slower on gfx950 (more registers, fewer waves), so they are not used.
+// then overwrites). The tile kernels load one vector at a time (B = 1); the
+// flat-block kernel, with two vectors per thread, loads both first.
 template <int NT, int MAXV, int B = 1>
 __device__ void adam_block(float* __restrict__ param, const float* __restrict__ grad,
                            uint8_t* __restrict__ qm, float* __restrict__ sm, uint8_t* __restrict__ qv,
@@ -320,23 +320,33 @@ __global__ __launch_bounds__(kAdamBigTileThreads) void adam_big_tile_kernel(
   }
 }
 
-__device__ __forceinline__ void adam_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, float* param,
-                                                             const float* grad, uint8_t* qm, float* sm,
-                                                             uint8_t* qv, float* sv, AdamK k) {
-  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
-  const QJob j = jobs[b];
-  const int wave = threadIdx.x / kWave;
-  if (wave >= j.rows) return;
-  const int len = wave == j.rows - 1 ? j.last : j.cols;
-  adam_block<kWave, 8>(param, grad, qm, sm, qv, sv, j.base + static_cast<int64_t>(wave) * j.cols, len, 1,
-                       len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr, k);
-}
+// Flat blocks, one 256-thread workgroup per block (workgroup b takes block
+// b % kFlatPerGroup of flat group b / kFlatPerGroup): a 2048-element block is
+// two 4-element vectors per thread, both loaded before either is used.
+// Measured on gfx950 against one wave per block (8 vectors per lane, 122
+// VGPRs, 4 waves per SIMD), three interleaved rounds on the Adam-state
+// workload, cold: 5.74-5.82 TB/s one wave, 5.78-5.84 with 128 threads,
+// 5.79-5.85 with 256 threads one vector at a time, 5.85-5.94 with 256 threads
+// and both vectors' loads first (57 VGPRs, 8 waves per SIMD).
+constexpr int kAdamFlatThreads = 256;
+constexpr int kAdamFlatVec = (2048 / 4 + kAdamFlatThreads - 1) / kAdamFlatThreads;
 
-__global__ __launch_bounds__(kFlatThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
-                                                             const float* grad, uint8_t* qm, float* sm,
-                                                             uint8_t* qv, float* sv, AdamK k, unsigned n_jobs) {
-  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
-    adam_flat_kernel_job(jb, n_jobs, jobs, param, grad, qm, sm, qv, sv, k);
+__global__ __launch_bounds__(kAdamFlatThreads) void adam_flat_kernel(const QJob* __restrict__ jobs, float* param,
+                                                                     const float* grad, uint8_t* qm, float* sm,
+                                                                     uint8_t* qv, float* sv, AdamK k,
+                                                                     unsigned n_pieces) {
+  __shared__ uint32_t red[2 * (kAdamFlatThreads / kWave)];
+  for (unsigned pb = blockIdx.x; pb < n_pieces; pb += gridDim.x) {
+    const unsigned b = piece_index<kFlatXcdGroup>(pb, n_pieces);
+    const QJob j = jobs[b / kFlatPerGroup];
+    const int blk = static_cast<int>(b % kFlatPerGroup);
+    if (blk < j.rows) {   // uniform over the workgroup
+      const int len = blk == j.rows - 1 ? j.last : j.cols;
+      adam_block<kAdamFlatThreads, kAdamFlatVec, kAdamFlatVec>(param, grad, qm, sm, qv, sv,
+                                                               j.base + static_cast<int64_t>(blk) * j.cols, len, 1,
+                                                               len, j.scale + blk, threadIdx.x, red, k);
+    }
+    __syncthreads();   // the next block reuses `red`
   }
 }
 
@@ -386,9 +396,11 @@ extern "C" int rs_adam8_step(rs_plan* p, float* param, const float* grad, void* 
     hipLaunchKernelGGL(adam_tile_kernel, grid_of(p, nt), dim3(kThreads), 0, s, p->qjobs, param, grad, qmb, s_m,
                        qvb, s_v, k, static_cast<unsigned>(nt));
   }
-  if (p->n_qflat)
-    hipLaunchKernelGGL(adam_flat_kernel, grid_of(p, p->n_qflat), dim3(kFlatThreads), 0, s, p->qjobs + p->n_qtile, param,
-                       grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(p->n_qflat));
+  if (p->n_qflat) {
+    const int64_t n = p->n_qflat * kFlatPerGroup;   // one workgroup per flat block
+    hipLaunchKernelGGL(adam_flat_kernel, grid_of(p, n), dim3(kAdamFlatThreads), 0, s, p->qjobs + p->n_qtile, param,
+                       grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(n));
+  }
   return launched(who);
 }
 
