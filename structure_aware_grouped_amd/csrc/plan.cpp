@@ -500,7 +500,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
                                     static_cast<int64_t>(tb.gchunks.size()) * tb.gather_split4,
                                     static_cast<int64_t>(tb.tm.size()) * tm_pieces(tb.tm_max_strip, 4, kTmThreads),
                                     static_cast<int64_t>(tb.qjobs.size()), static_cast<int64_t>(tb.gjobs.size()),
-                                    tb.n_qflat * kFlatPerGroup});
+                                    tb.n_qflat * kFlatPerGroup + tb.n_qzero});
     if (items > 0xFFFFFFFFll)
       return fail(RS_ERANGE, "rs_plan_load: the plan needs " + std::to_string(items) +
                                  " work items in one launch; indices are 32-bit");

@@ -6,8 +6,9 @@
 // ("veScale-FSDP: flexible, structure-aware sharding at 10K-GPU scale",
 // feynmanwiki walkthrough, the block-quantisation and 8-bit Adam paragraphs).
 // A tile stays in the registers of one 512-thread workgroup, a flat block in
-// one wave, so each input byte is read once; the absmax is a wave shuffle
-// reduction plus, for tiles, an LDS combine over the waves.
+// those of one 128-thread workgroup (quant) or one wave (dequant), so each
+// input byte is read once; the absmax is a wave shuffle
+// reduction plus, across the waves of a workgroup, an LDS combine.
 #include "host_common.h"
 
 #include <cstdlib>
@@ -194,36 +195,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(const QJob* _
   }
 }
 
-// One wave per flat block, kFlatPerGroup blocks per workgroup; zero-range jobs
-// from n_main on, as in the tile kernel.
-template <bool BF16, int FMT, bool HW>
-__device__ __forceinline__ void quant_flat_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs, int64_t n_main,
-                                                              const void* __restrict__ src,
-                                                              uint8_t* __restrict__ q,
-                                                              float* __restrict__ scales) {
-  const unsigned b = piece_index<kFlatXcdGroup>(jb, n_jobs);
-  const QJob j = jobs[b];
-  if (static_cast<int64_t>(b) >= n_main) {
-    zero_bytes<kFlatThreads>(q, j.base, j.stride, threadIdx.x);
-    return;
-  }
-  const int wave = threadIdx.x / kWave;
-  if (wave >= j.rows) return;
-  const int len = wave == j.rows - 1 ? j.last : j.cols;
-  quant_block<BF16, FMT, HW, kWave, 8, true>(src, q, scales, j.base + static_cast<int64_t>(wave) * j.cols, len,
-                                       1, len, j.scale + wave, threadIdx.x & (kWave - 1), nullptr);
-}
-
-template <bool BF16, int FMT, bool HW>
-__global__ __launch_bounds__(kFlatThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_main,
-                                                              const void* __restrict__ src,
-                                                              uint8_t* __restrict__ q,
-                                                              float* __restrict__ scales, unsigned n_jobs) {
-  for (unsigned jb = blockIdx.x; jb < n_jobs; jb += gridDim.x) {
-    quant_flat_kernel_job<BF16, FMT, HW>(jb, n_jobs, jobs, n_main, src, q, scales);
-  }
-}
-
 // Code bytes of positions outside every block (a plan with no block at all).
 __device__ __forceinline__ void zero_codes_kernel_job(unsigned jb, unsigned n_jobs, const QJob* __restrict__ jobs,
                                                               uint8_t* __restrict__ q) {
@@ -356,6 +327,43 @@ __global__ __launch_bounds__(kThreads) void zero_values_kernel(const QJob* __res
   }
 }
 
+// Flat blocks, one 128-thread workgroup per block: workgroup b < n_flat *
+// kFlatPerGroup takes block b % kFlatPerGroup of flat group b / kFlatPerGroup
+// (a 2048-element fp32 block is 4 vectors per thread, all loaded before the
+// first is used); the rest take the zero-range jobs that follow the flat
+// groups. Measured on gfx950 (Adam-state workload, int8 / uint8 codes, three
+// interleaved rounds, cold): one wave per block (8 vectors per lane, 84
+// VGPRs) 6.04-6.08 TB/s, 128 threads 6.22-6.28, 256 threads 5.80-5.83.
+// Dequant keeps one wave per block: 6.00-6.05 against 5.85-5.92 (128) and
+// 5.65-5.68 (256).
+constexpr int kQuantFlatThreads = 128;
+
+template <bool BF16, int FMT, bool HW>
+__global__ __launch_bounds__(kQuantFlatThreads) void quant_flat_kernel(const QJob* __restrict__ jobs, int64_t n_flat,
+                                                                       const void* __restrict__ src,
+                                                                       uint8_t* __restrict__ q,
+                                                                       float* __restrict__ scales, unsigned n_pieces) {
+  __shared__ uint32_t red[kQuantFlatThreads / kWave];
+  const int64_t n_main = n_flat * kFlatPerGroup;
+  for (unsigned pb = blockIdx.x; pb < n_pieces; pb += gridDim.x) {
+    const unsigned b = piece_index<kFlatXcdGroup>(pb, n_pieces);
+    if (static_cast<int64_t>(b) >= n_main) {
+      const QJob j = jobs[n_flat + (static_cast<int64_t>(b) - n_main)];
+      zero_bytes<kQuantFlatThreads>(q, j.base, j.stride, threadIdx.x);
+    } else {
+      const QJob j = jobs[b / kFlatPerGroup];
+      const int blk = static_cast<int>(b % kFlatPerGroup);
+      if (blk < j.rows) {   // uniform over the workgroup
+        const int len = blk == j.rows - 1 ? j.last : j.cols;
+        // fp32: blocks of up to 2048 elements in registers; bf16: 4096
+        quant_block<BF16, FMT, HW, kQuantFlatThreads, 512 / kQuantFlatThreads, true>(
+            src, q, scales, j.base + static_cast<int64_t>(blk) * j.cols, len, 1, len, j.scale + blk, threadIdx.x, red);
+      }
+    }
+    __syncthreads();   // the next block reuses `red`
+  }
+}
+
 }  // namespace
 }  // namespace rs
 
@@ -393,9 +401,11 @@ void launch_quant_kinds(const QuantLaunch& L, const void* src, uint8_t* q, float
       hipLaunchKernelGGL((quant_tile_kernel<BF16, FMT, HW, kTileXcdGroup>), grid_for(L, n), dim3(kQuantThreads), 0, s,
                          tiles, L.n_tile, src, q, scales, static_cast<unsigned>(n));
   }
-  if (L.n_flat)
-    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), grid_for(L, L.n_flat + nz), dim3(kFlatThreads), 0, s, flats,
-                       L.n_flat, src, q, scales, static_cast<unsigned>(L.n_flat + nz));
+  if (L.n_flat) {
+    const int64_t n = L.n_flat * kFlatPerGroup + nz;   // one workgroup per flat block, then the zero ranges
+    hipLaunchKernelGGL((quant_flat_kernel<BF16, FMT, HW>), grid_for(L, n), dim3(kQuantFlatThreads), 0, s, flats,
+                       L.n_flat, src, q, scales, static_cast<unsigned>(n));
+  }
   if (!L.n_tile && !L.n_flat && nz)
     hipLaunchKernelGGL(zero_codes_kernel, grid_for(L, nz), block, 0, s, flats, q, static_cast<unsigned>(nz));
 }
