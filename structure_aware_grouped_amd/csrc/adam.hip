@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void adam_tile_kernel(const QJob* __restr
 // Tiles of at most 1024 elements (the pages' 32x32 blocks): one wave per tile,
 // kAdamWaveTiles tiles per workgroup, the block's absmax a wave reduction
 // only (no LDS, no barrier). Tile jobs b*kAdamWaveTiles + wave.
-constexpr int kAdamWaveTiles = 4;
+constexpr int kAdamWaveTiles = kAdamStripTiles;
 
 //
 // Four 32x32 tiles side by side in one band (the usual case: the workgroup's
@@ -185,12 +185,14 @@ constexpr int kAdamWaveTiles = 4;
 // from there; the fp32 parameters and gradients (128 bytes per tile row) go
 // straight to and from memory. Other groups of four jobs take one wave per
 // tile directly.
-constexpr int kStripRows = 32, kStripTileCols = 32, kStripCols = kAdamWaveTiles * kStripTileCols;
+constexpr int kStripRows = kAdamStripRows, kStripTileCols = kAdamStripTileCols;
+constexpr int kStripCols = kAdamWaveTiles * kStripTileCols;
 
 // One 32x32 tile of a strip by one wave: codes read from and written back to
 // the strip's LDS copy (cm, cv: kStripRows rows of kStripCols bytes; this
 // tile's columns start at c0). The arithmetic and the order of every
 // operation are adam_block's.
+constexpr int kAdamStripThreads = kAdamWaveTiles * kWave;
 constexpr int kStripVPR = kStripTileCols / 4;             // 4-element vectors per tile row
 constexpr int kStripNV = kStripRows * kStripVPR / kWave;  // vectors per lane
 
@@ -257,7 +259,15 @@ __device__ void adam_strip_tile(float* __restrict__ param, const f32x4 (&pv)[kSt
   }
 }
 
-__global__ __launch_bounds__(kAdamWaveTiles * kWave) void adam_wave_tile_kernel(
+// ALL_STRIPS: the plan's lowering found every group to be a strip, so the
+// kernel neither checks nor carries the one-wave-per-tile path, whose
+// registers would otherwise set the kernel's count (115 VGPRs instead of 124;
+// the 8B layer's states in 32x32 tiles: 5.95-5.99 -> 6.04-6.09 TB/s cold,
+// three interleaved rounds). Two waves per tile (512-thread strips, the
+// tile's maxima combined through LDS; 94 VGPRs, but still 4 waves per SIMD
+// with 8-wave workgroups) ran at 5.09-5.10.
+template <bool ALL_STRIPS>
+__global__ __launch_bounds__(kAdamStripThreads) void adam_wave_tile_kernel(
     const QJob* __restrict__ jobs, float* param, const float* grad, uint8_t* qm, float* sm, uint8_t* qv, float* sv,
     AdamK k, unsigned n_jobs, unsigned n_groups) {
   __shared__ __align__(16) uint8_t cm[kStripRows * kStripCols];
@@ -267,19 +277,22 @@ __global__ __launch_bounds__(kAdamWaveTiles * kWave) void adam_wave_tile_kernel(
     const unsigned t0 = piece_index<kTileXcdGroup>(gb, n_groups) * kAdamWaveTiles;
     // a strip: four full 32x32 tiles of one tensor side by side, 16-byte aligned
     // (every thread reads the four jobs, so the choice is the same for all waves)
-    bool strip = t0 + kAdamWaveTiles <= n_jobs;
     const QJob j0 = jobs[min(t0, n_jobs - 1)];
-    strip = strip && j0.rows == kStripRows && j0.cols == kStripTileCols && j0.base % 16 == 0 && j0.stride % 16 == 0;
+    bool strip = ALL_STRIPS;
+    if constexpr (!ALL_STRIPS) {
+      strip = t0 + kAdamWaveTiles <= n_jobs && j0.rows == kStripRows && j0.cols == kStripTileCols &&
+              j0.base % 16 == 0 && j0.stride % 16 == 0;
 #pragma unroll
-    for (int w = 1; w < kAdamWaveTiles; ++w) {
-      if (!strip) break;
-      const QJob jw = jobs[t0 + w];
-      strip = jw.tensor == j0.tensor && jw.rows == kStripRows && jw.cols == kStripTileCols &&
-              jw.stride == j0.stride && jw.base == j0.base + w * kStripTileCols && jw.scale == j0.scale + w;
+      for (int w = 1; w < kAdamWaveTiles; ++w) {
+        if (!strip) break;
+        const QJob jw = jobs[t0 + w];
+        strip = jw.tensor == j0.tensor && jw.rows == kStripRows && jw.cols == kStripTileCols &&
+                jw.stride == j0.stride && jw.base == j0.base + w * kStripTileCols && jw.scale == j0.scale + w;
+      }
     }
-    if (!strip) {
+    if (!ALL_STRIPS && !strip) {   // one wave per tile
       const unsigned t = t0 + wave;
-      if (t < n_jobs) {
+      if (wave < kAdamWaveTiles && t < n_jobs) {
         const QJob j = jobs[t];
         adam_block<kWave, 4>(param, grad, qm, sm, qv, sv, j.base, j.stride, j.rows, j.cols, j.scale, lane, nullptr, k);
       }
@@ -387,8 +400,12 @@ extern "C" int rs_adam8_step(rs_plan* p, float* param, const float* grad, void* 
   const int64_t nt = p->n_qtile;
   if (nt && p->adam_wave_tiles && p->max_tile_vec16 <= kWave * 4) {
     const int64_t groups = (nt + kAdamWaveTiles - 1) / kAdamWaveTiles;
-    hipLaunchKernelGGL(adam_wave_tile_kernel, grid_of(p, groups), dim3(kAdamWaveTiles * kWave), 0, s, p->qjobs, param,
-                       grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(nt), static_cast<unsigned>(groups));
+    if (p->adam_all_strips)
+      hipLaunchKernelGGL(adam_wave_tile_kernel<true>, grid_of(p, groups), dim3(kAdamStripThreads), 0, s, p->qjobs,
+                         param, grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(nt), static_cast<unsigned>(groups));
+    else
+      hipLaunchKernelGGL(adam_wave_tile_kernel<false>, grid_of(p, groups), dim3(kAdamStripThreads), 0, s, p->qjobs,
+                         param, grad, qmb, s_m, qvb, s_v, k, static_cast<unsigned>(nt), static_cast<unsigned>(groups));
   } else if (nt && p->max_tile_vec16 > kThreads * 4 && p->max_tile_vec16 <= kAdamBigTileThreads * 4) {
     hipLaunchKernelGGL(adam_big_tile_kernel, grid_of(p, nt), dim3(kAdamBigTileThreads), 0, s, p->qjobs, param, grad,
                        qmb, s_m, qvb, s_v, k, static_cast<unsigned>(nt));

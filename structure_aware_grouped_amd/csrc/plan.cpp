@@ -35,6 +35,7 @@ struct Tables {
   int64_t padding = 0;
   int32_t max_tile_vec16 = 0;
   bool split_code_lines = false;
+  bool adam_all_strips = false;
   int64_t gather_split8 = 0, gather_split4 = 0;
 };
 
@@ -171,6 +172,7 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   tb->n_qblocks = ql.n_blocks;
   tb->max_tile_vec16 = ql.max_tile_vec16;
   tb->split_code_lines = ql.split_code_lines;
+  tb->adam_all_strips = ql.all_strips;
   assert(tb->n_qblocks == first_scale[n]);
 
   // gather side: contiguous row runs where every 16-element vector has one
@@ -446,6 +448,19 @@ void lower_quant(const std::vector<Tensor>& t, int64_t top, QuantList* ql) {
     else if (j.kind == QJOB_FLAT) ++ql->n_flat;
     else ++ql->n_zero;
   }
+  // Adam strips: tile jobs 4g .. 4g+3 are four full 32x32 tiles of one tensor
+  // side by side (consecutive in the buffer and in scale order), 16-byte
+  // aligned, for every group g
+  ql->all_strips = ql->n_tile > 0 && ql->n_tile % kAdamStripTiles == 0;
+  for (int64_t g = 0; ql->all_strips && g < ql->n_tile; g += kAdamStripTiles) {
+    const QJob& j0 = ql->jobs[g];
+    for (int w = 0; w < kAdamStripTiles && ql->all_strips; ++w) {
+      const QJob& jw = ql->jobs[g + w];
+      ql->all_strips = jw.tensor == j0.tensor && jw.rows == kAdamStripRows && jw.cols == kAdamStripTileCols &&
+                       jw.stride == j0.stride && jw.stride % 16 == 0 && jw.base % 16 == 0 &&
+                       jw.base == j0.base + w * kAdamStripTileCols && jw.scale == j0.scale + w;
+    }
+  }
 }
 
 
@@ -532,6 +547,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->n_gflat = tb.n_gflat;
     p->max_tile_vec16 = tb.max_tile_vec16;
     p->split_code_lines = tb.split_code_lines;
+    p->adam_all_strips = tb.adam_all_strips;
     p->gather_split8 = tb.gather_split8;
     p->gather_split4 = tb.gather_split4;
     // gfx950's FP8 conversion (OCP E4M3, round to nearest even) by default;

@@ -304,12 +304,18 @@ bool spec_ok(const rs_tensor_spec& s, std::string* why);
 int validate_plan(const char* who, const rs_tensor_spec* specs, int64_t n, int64_t V, int64_t S,
                   const int64_t* starts, int64_t R_mat, std::vector<Tensor>* out, int64_t* R_used);
 
+// The Adam step takes tile jobs in groups of kAdamStripTiles; a group of four
+// 32x32 tiles side by side in one band of one tensor (codes 16-byte aligned)
+// is a 32 x 128 strip whose code rows are whole 128-byte runs.
+constexpr int kAdamStripTiles = 4, kAdamStripRows = 32, kAdamStripTileCols = 32;
+
 // The block quant / dequant work list of a validated plan.
 struct QuantList {
   std::vector<QJob> jobs;   // tiles, then flat groups, then zero ranges
   int64_t n_tile = 0, n_flat = 0, n_zero = 0, n_blocks = 0;
   int32_t max_tile_vec16 = 0;     // largest tile, in 16-byte vectors of 4-byte input
   bool split_code_lines = false;  // neighbouring tiles share 128-byte lines of codes
+  bool all_strips = false;        // the tile jobs are whole Adam strips, group after group
 };
 void lower_quant(const std::vector<Tensor>& t, int64_t top, QuantList* ql);
 
@@ -354,4 +360,5 @@ struct rs_plan {
   bool tm_pack_lds = true;     // tile-major pack staged through LDS (else the direct kernel)
   int64_t max_grid = rs::kMaxGrid;   // workgroups per launch; beyond it workgroups loop over items
   bool adam_wave_tiles = true;       // Adam step: one wave per tile when every tile fits one wave's registers
+  bool adam_all_strips = false;      // Adam step: every group of kAdamStripTiles tile jobs is a strip
 };

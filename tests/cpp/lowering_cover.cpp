@@ -45,6 +45,22 @@ int64_t scale_of(const Tensor& x, int64_t first, int64_t e) {
 }
 
 int64_t g_split8 = 0, g_split4 = 0, g_runs = 0;
+bool g_strips = false;
+
+// The Adam step's whole-strip launch, decided from the tensors rather than
+// the job list: some tensor has tiles, and every tiled tensor is a row-major
+// TILE(32, 32) tensor of whole 32-row bands whose width is a multiple of 128
+// (so each band's tiles fall into groups of four side by side).
+bool strips_from_tensors(const std::vector<Tensor>& t) {
+  bool any = false;
+  for (const Tensor& x : t) {
+    if (x.kind == RS_TILEMAJOR) return false;
+    if (x.kind != RS_TILE) continue;
+    if (x.p0 != 32 || x.p1 != 32 || x.rows % 32 != 0 || x.cols % 128 != 0) return false;
+    any = true;
+  }
+  return any;
+}
 
 bool check(const std::vector<Tensor>& t, int64_t S, int64_t R, int plant) {
   Tables tb;
@@ -52,6 +68,9 @@ bool check(const std::vector<Tensor>& t, int64_t S, int64_t R, int plant) {
   g_split8 = tb.gather_split8;
   g_split4 = tb.gather_split4;
   g_runs = static_cast<int64_t>(tb.gchunks.size());
+  g_strips = tb.adam_all_strips;
+  CHECK(tb.adam_all_strips == strips_from_tensors(t), "Adam strip launch %d, from the tensors %d",
+        int(tb.adam_all_strips), int(strips_from_tensors(t)));
   if (plant == 1 && !tb.pack.empty()) tb.pack.pop_back();
   if (plant == 2 && !tb.qjobs.empty()) tb.qjobs.insert(tb.qjobs.begin(), tb.qjobs.front());
   if (plant == 3 && !tb.gchunks.empty()) tb.gchunks.back().scale0 += 1;
@@ -247,5 +266,6 @@ int main(int argc, char** argv) {
   std::printf("ok\n");
   std::printf("gather runs %lld split8 %lld split4 %lld\n", (long long)g_runs, (long long)g_split8,
               (long long)g_split4);
+  std::printf("adam strips %d\n", int(g_strips));
   return 0;
 }

@@ -100,11 +100,14 @@ def test_steps_on_blocks_beyond_the_register_paths(gpu_lib):
     plan.close()
 
 
-# groups whose largest tile picks each register path of the tile step: 32x32 tiles (one wave a
-# tile, the pages' 8-bit Adam blocks), 64x64 (one 256-thread workgroup a tile), 128x128 (1024
+# groups whose largest tile picks each register path of the tile step: 32x32 tiles (strips of four
+# side by side through LDS, else one wave a tile; the pages' 8-bit Adam blocks), 64x64 (one 256-thread workgroup a tile), 128x128 (1024
 # threads a tile); each with ragged edge tiles, tiles whose width is not a multiple of 4 (the
 # two-pass path inside the same launch), a tile-major tensor, flat blocks and a row tensor
 TILE_PATHS = {
+    # every group of four 32x32 tiles a 32 x 128 strip: the strip-only launch
+    "32x32 strips": [TensorSpec("s256", 64, 256, "TILE", 32, 32), TensorSpec("s128", 96, 128, "TILE", 32, 32),
+                     TensorSpec("flat", 1, 5000, "FLAT", 2048), TensorSpec("norm", 300, 1, "ROWS", 1)],
     "32x32": [TensorSpec("t32", 256, 320, "TILE", 32, 32), TensorSpec("t32_ragged", 100, 70, "TILE", 32, 32),
               TensorSpec("t32_odd", 40, 45, "TILE", 32, 32), TensorSpec("tm16", 32, 64, "TILEMAJOR", 16, 16),
               TensorSpec("flat", 1, 5000, "FLAT", 2048), TensorSpec("norm", 300, 1, "ROWS", 1)],

@@ -14,7 +14,7 @@ import subprocess
 import pytest
 
 from oracle import plan as OP
-from workloads import TensorSpec, tile_major_variant, workload
+from workloads import TensorSpec, adam_tile32_variant, tile_major_variant, workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "structure_aware_grouped_amd", "csrc")
@@ -57,6 +57,30 @@ def _gather_shape(exe, specs, V):
     assert out[0] == "ok", r.stdout
     w = out[1].split()
     return int(w[2]), int(w[4]), int(w[6])
+
+
+def _adam_strips(exe, specs, V):
+    ref = OP.plan(specs, V)
+    lines = [f"{len(specs)} {V} {ref.S} {V}"] + [f"{s.rows} {s.cols} {KINDS[s.kind]} {s.p0} {s.p1} {int(st)}"
+                                                 for s, st in zip(specs, ref.starts)]
+    r = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, timeout=600)
+    out = r.stdout.split("\n")
+    assert out[0] == "ok", r.stdout
+    return out[2] == "adam strips 1"
+
+
+def test_adam_strip_launch_follows_the_tensors(exe):
+    # the check inside compares the lowering's flag with the tensor shapes on every
+    # plan this file runs; here both values it can take on
+    assert _adam_strips(exe, list(adam_tile32_variant(workload(4)).specs), 64)
+    assert not _adam_strips(exe, list(workload(4).specs), 64)          # flat blocks only
+    assert not _adam_strips(exe, list(workload(1).specs), 64)          # 128x128 tiles
+    assert not _adam_strips(exe, [TensorSpec("a", 64, 256, "TILE", 32, 32),
+                                  TensorSpec("b", 64, 96, "TILE", 32, 32)], 2)   # 3 tiles per band
+    assert not _adam_strips(exe, [TensorSpec("a", 64, 256, "TILE", 32, 32),
+                                  TensorSpec("b", 40, 128, "TILE", 32, 32)], 2)  # a partial band
+    assert _adam_strips(exe, [TensorSpec("a", 64, 256, "TILE", 32, 32), TensorSpec("b", 96, 128, "TILE", 32, 32),
+                              TensorSpec("c", 5000, 1, "FLAT", 2048), TensorSpec("d", 300, 1, "ROWS", 1)], 3)
 
 
 @pytest.mark.parametrize("idx,tm", [(0, False), (1, False), (1, True), (2, False), (4, False)])
