@@ -218,8 +218,11 @@ __device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* 
   void* out = dst[j.tensor];
   const int pass = split * static_cast<int>(kGatherTmPiece);
   if (bc % VEC == 0 && j.cols % VEC == 0) {
-    const uint32_t wv = width / VEC, mw = magic_u16(wv);
-    const int nvec = j.h * static_cast<int>(wv);
+    // vectors in buffer order: tile t's run of h rows of bc codes, row by row
+    // (a wave reads contiguous codes; in row order, interleaved on gfx950,
+    // 5.59-5.64 against 5.66-5.67 TB/s cold)
+    const uint32_t rv = static_cast<uint32_t>(j.h) * bc / VEC, mrv = magic_u16(rv);   // vectors per tile run
+    const int nvec = static_cast<int>(j.k * rv);
     for (int i0 = piece * static_cast<int>(kGatherTmPiece) + static_cast<int>(threadIdx.x); i0 < nvec; i0 += pass) {
       uint32_t code[U][VEC / 4];
       float sc[U];
@@ -228,9 +231,9 @@ __device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* 
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u * kGatherThreads;
         if (i < nvec) {
-          const uint32_t r = div_u16(static_cast<uint32_t>(i), wv, mw);
-          const uint32_t col = (static_cast<uint32_t>(i) - r * wv) * VEC;
-          const uint32_t t = div_u16(col, bc, mbc), c = col - t * bc;
+          const uint32_t t = div_u16(static_cast<uint32_t>(i), rv, mrv);
+          const uint32_t e = (static_cast<uint32_t>(i) - t * rv) * VEC;
+          const uint32_t r = div_u16(e, bc, mbc), c = e - r * bc, col = t * bc + c;
           const uint8_t* from = qb + static_cast<int64_t>(t) * j.tile_elems + r * bc + c;
           if constexpr (VEC == 8) {
             const u32x2 w = ldg(reinterpret_cast<const u32x2*>(from));
