@@ -17,7 +17,8 @@ leaves none of its inputs in L2 or the 256 MB MALL, and HIP events on the
 stream the kernels run on bracket each launch; the headline divides one
 step's bytes by the sum of its kernels' median durations over the K steps.
 A warm pass (K steps back to back, wall clock) is reported apart, as is a
-16-byte streaming copy of 1 GiB, the practical ceiling. The CPU baseline
+16-byte streaming copy that moves as many bytes as the dominant kernel, the
+practical ceiling. The CPU baseline
 times the CPU oracle on a bounded sample of the same workload, on one core
 and on all host cores. Prints one JSON line.
 """
