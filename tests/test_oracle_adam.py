@@ -10,7 +10,6 @@
     and zero gradient leave p;
   * a planted mistake (no bias correction) fails the torch comparison.
 """
-import math
 from fractions import Fraction
 
 import numpy as np
