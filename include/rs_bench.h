@@ -1,11 +1,15 @@
 /*
- * rs_bench.h — measurement helper beside the layout library (librs_bench.so).
+ * rs_bench.h — measurement and self-check helpers beside the layout library
+ * (librs_bench.so). Neither is a step of the layout transform.
  *
- * Not a step of the layout transform: a plain streaming copy of known traffic
- * on gfx950, built the way the transform kernels stream (16-byte nontemporal
- * vectors, small short-lived workgroups). The benchmark times it as the
- * practical HBM ceiling next to the 8 TB/s peak, and its counter readings
- * calibrate the HBM byte counters (it reads and writes exactly `bytes`).
+ * rs_bench_copy: a plain streaming copy of known traffic on gfx950, built the
+ * way the transform kernels stream (16-byte nontemporal vectors, small
+ * short-lived workgroups). The benchmark times it as the practical HBM
+ * ceiling next to the 8 TB/s peak, and its counter readings calibrate the HBM
+ * byte counters (it reads and writes exactly `bytes`).
+ *
+ * rs_bench_sqrt_check: checks, value by value, a device building block of the
+ * library against the correctly rounded operation it stands for.
  */
 #ifndef RS_BENCH_H
 #define RS_BENCH_H
@@ -21,6 +25,16 @@ extern "C" {
  * (a hipStream_t passed as void*). Returns 0, -1 (bad argument: nothing is
  * launched) or -6 (launch error). */
 int rs_bench_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/* Self-check of the short correctly rounded square root that the 8-bit Adam
+ * step uses for inputs in [2^-96, FLT_MAX]: every fp32 whose bit pattern lies
+ * in [lo, hi] is compared, bit for bit, with the general correctly rounded
+ * square root. Synchronous on the current device (allocates 16 bytes of
+ * device memory for the counts). *mismatches receives the number of values
+ * that differ and *first_mismatch the lowest such bit pattern (0xFFFFFFFF if
+ * none). Returns 0, -1 (lo > hi or a null pointer: nothing is launched) or -6
+ * (HIP error). */
+int rs_bench_sqrt_check(uint32_t lo, uint32_t hi, uint64_t* mismatches, uint32_t* first_mismatch);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,6 @@
 """Build librs_hip.so (the layout library) and librs_bench.so (the
-benchmark's streaming-copy ceiling) for gfx950 with hipcc, in-tree next to
-this file.
+benchmark's streaming-copy ceiling and the square-root self-check) for gfx950
+with hipcc, in-tree next to this file.
 
     python -m structure_aware_grouped_amd.build
 """
@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librs_hip.so")
 SOURCES = ["planner.cpp", "plan.cpp", "transform.hip", "quant.hip", "gather.hip", "adam.hip"]
 BENCH_LIB = os.path.join(HERE, "librs_bench.so")
-BENCH_SOURCES = ["stream_copy.hip"]
+BENCH_SOURCES = ["stream_copy.hip", "selftest.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

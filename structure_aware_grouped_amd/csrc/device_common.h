@@ -254,6 +254,26 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Square root rounded to nearest even, for x in [kSqrtShortMin, FLT_MAX]:
+// gfx950's v_sqrt_f32 estimate s is within one ulp of the root there, and
+// the rounded root is s or one of its neighbours sd, su, chosen by the signs
+// of the residuals x - sd*s and x - su*s (Tuckerman's rounding test), each
+// from one fma, whose rounding keeps the sign of the exact residual. This
+// skips the scaling of tiny inputs and the zero and infinity cases of the
+// general correctly rounded sequence. Every fp32 of the range gives the same
+// bits as __builtin_sqrtf under -fhip-fp32-correctly-rounded-divide-sqrt
+// (rs_bench_sqrt_check); callers use that one outside the range.
+constexpr float kSqrtShortMin = 0x1p-96f;
+__device__ __forceinline__ float sqrt_rn_short(float x) {
+  const float s = __builtin_amdgcn_sqrtf(x);
+  const float sd = __uint_as_float(__float_as_uint(s) - 1u);
+  const float su = __uint_as_float(__float_as_uint(s) + 1u);
+  const float rd = __builtin_fmaf(-sd, s, x);
+  const float ru = __builtin_fmaf(-su, s, x);
+  const float r = rd <= 0.0f ? sd : s;
+  return ru > 0.0f ? su : r;
+}
+
 // floor(n / d) for n < 2^16 and 1 <= d < 2^16 with m = magic_u16(d) =
 // ceil(2^32 / d): n*m / 2^32 exceeds n/d by less than 2^-16 < 1/d, which
 // never carries past the next integer.

@@ -30,13 +30,13 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(rs_\w+)\s*\(", text, re.M)))
 
 
-def test_bench_helper_library_exports_its_declared_call(rs):
-    """librs_bench.so (the benchmark's streaming-copy ceiling) exports what rs_bench.h declares;
-    bad arguments are refused before any launch."""
+def test_bench_helper_library_exports_its_declared_calls(rs):
+    """librs_bench.so (the benchmark's streaming-copy ceiling and the square-root self-check)
+    exports what rs_bench.h declares; bad arguments are refused before any launch."""
     import ctypes
     text = open(os.path.join(ROOT, "include", "rs_bench.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(rs_\w+)\s*\(", text, re.M)))
-    assert names == ["rs_bench_copy"]
+    assert names == ["rs_bench_copy", "rs_bench_sqrt_check"]
     path = os.path.join(ROOT, "structure_aware_grouped_amd", "librs_bench.so")
     assert os.path.exists(path), "librs_bench.so is not built: run __graft_entry__.build()"
     lib = ctypes.CDLL(path)
@@ -45,6 +45,11 @@ def test_bench_helper_library_exports_its_declared_call(rs):
     assert lib.rs_bench_copy(a, b, 15, None) == -1                      # not a multiple of 16
     assert lib.rs_bench_copy(a, ctypes.c_void_p((1 << 20) + 16), 64, None) == -1   # overlapping
     assert lib.rs_bench_copy(a, b, 0, None) == 0                        # nothing to do
+    lib.rs_bench_sqrt_check.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    n, f = ctypes.c_uint64(7), ctypes.c_uint32(7)
+    assert lib.rs_bench_sqrt_check(2, 1, ctypes.byref(n), ctypes.byref(f)) == -1   # empty range
+    assert lib.rs_bench_sqrt_check(1, 2, None, ctypes.byref(f)) == -1             # null result
+    assert (n.value, f.value) == (7, 7)                                           # untouched
 
 
 def test_library_exports_every_declared_call(rs):
