@@ -145,13 +145,25 @@ def count_quant_blocks(specs) -> int:
     return total
 
 
+# quiet NaN, sign clear, no payload: the scale of a block that holds a NaN
+SCALE_NAN = np.uint32(0x7FC00000).view(np.float32)
+
+
 def quantize_block(x, fmt: str) -> Tuple[np.ndarray, np.float32]:
-    """Codes and scale of one block of fp32 values."""
+    """Codes and scale of one block of fp32 values.
+
+    A block whose values include a NaN or an infinity cannot be scaled (the pages
+    assume finite values; reading): its amax, taken with NaN propagating, is NaN or
+    +inf; its scale is a quiet NaN (0x7FC00000) or +inf; every code is 0x00, so its
+    dequantised values are all NaN (0 x NaN, 0 x inf) and a divergence stays visible."""
     x = np.asarray(x, dtype=np.float32)
     Q = codes.FORMAT_QMAX[fmt]
-    amax = float(np.max(np.abs(x.astype(np.float64)))) if x.size else 0.0
+    with np.errstate(invalid="ignore"):       # a signalling NaN widens quietly
+        amax = float(np.max(np.abs(x.astype(np.float64)))) if x.size else 0.0
     if amax == 0.0:
         return np.zeros(x.shape, dtype=np.uint8), np.float32(1.0)
+    if not np.isfinite(amax):
+        return np.zeros(x.shape, dtype=np.uint8), (SCALE_NAN if np.isnan(amax) else np.float32(np.inf))
     scale = np.float32(amax / Q)
     with np.errstate(over="ignore"):          # Q / amax may overflow fp32: clamp below
         r = min(float(np.float32(Q / amax)), FLT_MAX)
@@ -175,7 +187,8 @@ def block_quant(src: np.ndarray, specs, starts, S: int, R_mat: int, fmt: str):
 
 def dequant_values(c, scale, fmt: str) -> np.ndarray:
     """fl32(decode(code) * scale)."""
-    return f32(codes.decode(c, fmt) * np.float64(np.float32(scale)))
+    with np.errstate(invalid="ignore"):       # 0 x inf of a non-finite block is NaN
+        return f32(codes.decode(c, fmt) * np.float64(np.float32(scale)))
 
 
 def block_dequant(q: np.ndarray, scales, specs, starts, S: int, R_mat: int, fmt: str) -> np.ndarray:

@@ -139,6 +139,37 @@ def test_step_quantises_each_block_and_leaves_the_rest():
     assert np.array_equal(p1[~inside], param[~inside]) and np.array_equal(qm1[~inside], qm[~inside])
 
 
+def test_a_nan_gradient_blanks_its_blocks_only():
+    """Reading (non-finite blocks): a NaN gradient makes that element's m1, v1 and parameter NaN;
+    its m and v blocks get NaN scales and all-zero codes, so the next step reads NaN state for the
+    whole block; every other block steps as without the NaN."""
+    specs = [TensorSpec("f", 1, 2048, "FLAT", 512)]
+    rng = np.random.default_rng(5)
+    param = rng.standard_normal(2048).astype(np.float32)
+    grad = (rng.standard_normal(2048) * 1e-3).astype(np.float32)
+    m = (rng.standard_normal(2048) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(2048) * 1e-3) ** 2).astype(np.float32)
+    qm, sm = T.block_quant(m, specs, [0], 2048, 1, "i8")
+    qv, sv = T.block_quant(v, specs, [0], 2048, 1, "u8")
+    h = HYPERS[0]
+    clean = A.adam8_step(param, grad, qm, sm, qv, sv, specs, [0], h)
+    g2 = grad.copy()
+    g2[700] = np.nan                                            # block 1 (elements 512..1023)
+    with np.errstate(invalid="ignore"):
+        p1, qm1, sm1, qv1, sv1 = A.adam8_step(param, g2, qm, sm, qv, sv, specs, [0], h)
+    blk = slice(512, 1024)
+    assert np.isnan(p1[700]) and np.isnan(p1).sum() == 1
+    assert not qm1[blk].any() and not qv1[blk].any()
+    assert sm1.view(np.uint32)[1] == 0x7FC00000 and sv1.view(np.uint32)[1] == 0x7FC00000
+    for k in (0, 2, 3):
+        rest = slice(512 * k, 512 * (k + 1))
+        assert np.array_equal(p1[rest], clean[0][rest]) and np.array_equal(qm1[rest], clean[1][rest])
+        assert sm1[k] == clean[2][k] and sv1[k] == clean[4][k]
+    with np.errstate(invalid="ignore"):                        # the next step: the whole block is NaN
+        p2 = A.adam8_step(p1, grad, qm1, sm1, qv1, sv1, specs, [0], h)[0]
+    assert np.isnan(p2[blk]).all() and not np.isnan(p2[:512]).any()
+
+
 def test_pin_catches_a_missing_bias_correction(monkeypatch):
     orig = A.host_scalars
 

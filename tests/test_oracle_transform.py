@@ -152,6 +152,41 @@ def test_zero_block_and_tiny_block():
     assert c[1] == 0x00 and c[3] == 0x80
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "i8", "u8"])
+def test_blocks_with_nan_or_infinity(fmt):
+    """Reading: a block holding a NaN or an infinity gets amax NaN (NaN propagates, as
+    torch.amax does) or +inf, scale 0x7FC00000 or +inf, and all-zero codes; it dequantises
+    to NaN everywhere. Finite blocks beside it are untouched."""
+    import torch
+    rng = np.random.default_rng(31)
+    base = rng.standard_normal(64).astype(np.float32)
+    nan_bits = np.uint32([0x7FC00000, 0xFFC00000, 0x7F800001, 0x7FFFFFFF]).view(np.float32)
+    for bad, want_scale in [(nan_bits[0], 0x7FC00000), (nan_bits[1], 0x7FC00000), (nan_bits[2], 0x7FC00000),
+                            (nan_bits[3], 0x7FC00000), (np.float32(np.inf), 0x7F800000),
+                            (np.float32(-np.inf), 0x7F800000)]:
+        for where in (0, 17, 63):
+            x = base.copy()
+            x[where] = bad
+            amax = torch.amax(torch.abs(torch.from_numpy(x))).item()
+            assert (np.isnan(amax) and want_scale == 0x7FC00000) or (amax == np.inf and want_scale == 0x7F800000)
+            c, s = T.quantize_block(x, fmt)
+            assert not c.any() and _bits(s) == want_scale
+            d = T.dequant_values(c, s, fmt)
+            assert np.isnan(d).all()
+    x = base.copy()                      # a NaN wins over an infinity
+    x[3], x[40] = np.inf, np.nan
+    c, s = T.quantize_block(x, fmt)
+    assert not c.any() and _bits(s) == 0x7FC00000
+    # a group: only the block holding the NaN changes
+    specs = [TensorSpec("f", 1, 300, "FLAT", 100)]
+    src = rng.standard_normal(300).astype(np.float32)
+    q0, s0 = T.block_quant(src, specs, [0], 300, 1, fmt)
+    src[150] = np.nan
+    q1, s1 = T.block_quant(src, specs, [0], 300, 1, fmt)
+    assert np.array_equal(q0[:100], q1[:100]) and np.array_equal(q0[200:], q1[200:]) and not q1[100:200].any()
+    assert _bits(s1[1]) == 0x7FC00000 and _bits(s1[0]) == _bits(s0[0]) and _bits(s1[2]) == _bits(s0[2])
+
+
 def test_quant_blocks_cover_each_position_once_and_stay_on_one_rank():
     specs = [TensorSpec("a", 37, 20, "TILE", 8, 6), TensorSpec("b", 3, 5, "ELEM"),
              TensorSpec("c", 1, 4099, "FLAT", 256)]
