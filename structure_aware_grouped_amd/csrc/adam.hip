@@ -38,13 +38,6 @@ __device__ __forceinline__ void adam_elem(float p, float g, float m0, float v0, 
   p1 = __fsub_rn(__fmul_rn(p, k.decay), __fmul_rn(k.step_size, __fdiv_rn(m1, den)));
 }
 
-// Scale and reciprocal of a block with absmax `amax` for code range Q.
-__device__ __forceinline__ void block_scale(float amax, float Q, float& scale, float& r) {
-  const bool zero = amax == 0.0f;
-  scale = zero ? 1.0f : __fdiv_rn(amax, Q);
-  r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
-}
-
 // One quantisation block (element (r, c) at base + r*stride + c) handled by
 // NT threads. The old scales are read before the block's max is reduced and
 // the new ones written after it. Fast path: 4-element vectors, every updated
@@ -115,9 +108,9 @@ __device__ void adam_block(float* __restrict__ param, const float* __restrict__ 
     for (int j = 0; j < MAXV; ++j) {
       if (tid + j * NT < nvec) {
         const int64_t e = base + static_cast<int64_t>(w2.row) * stride + static_cast<int64_t>(w2.col) * 4;
-        const uint32_t cm = amax_m == 0.0f ? 0u
+        const uint32_t cm = rm == 0.0f ? 0u
             : encode4<FMT_I8, false>(__fmul_rn(m1[j].x, rm), __fmul_rn(m1[j].y, rm), __fmul_rn(m1[j].z, rm), __fmul_rn(m1[j].w, rm));
-        const uint32_t cv = amax_v == 0.0f ? 0u
+        const uint32_t cv = rv == 0.0f ? 0u
             : encode4<FMT_U8, false>(__fmul_rn(v1[j].x, rv), __fmul_rn(v1[j].y, rv), __fmul_rn(v1[j].z, rv), __fmul_rn(v1[j].w, rv));
         stg(reinterpret_cast<uint32_t*>(qm + e), cm);
         stg(reinterpret_cast<uint32_t*>(qv + e), cv);
@@ -154,8 +147,8 @@ __device__ void adam_block(float* __restrict__ param, const float* __restrict__ 
     float p1, m1, v1;  // m1 and v1 again, from the old codes (p1 is discarded)
     adam_elem(0.0f, grad[e], __fmul_rn(decode1<FMT_I8, false>(qm[e]), sm0),
               __fmul_rn(decode1<FMT_U8, false>(qv[e]), sv0), k, p1, m1, v1);
-    qm[e] = amax_m == 0.0f ? 0 : static_cast<uint8_t>(encode1<FMT_I8, false>(__fmul_rn(m1, rm)));
-    qv[e] = amax_v == 0.0f ? 0 : static_cast<uint8_t>(encode1<FMT_U8, false>(__fmul_rn(v1, rv)));
+    qm[e] = rm == 0.0f ? 0 : static_cast<uint8_t>(encode1<FMT_I8, false>(__fmul_rn(m1, rm)));
+    qv[e] = rv == 0.0f ? 0 : static_cast<uint8_t>(encode1<FMT_U8, false>(__fmul_rn(v1, rv)));
   }
 }
 
@@ -260,9 +253,9 @@ __device__ void adam_strip_tile(float* __restrict__ param, const f32x4 (&pv)[kSt
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int i = lane + j * kWave, row = i / VPR, col = (i % VPR) * 4;
-    *reinterpret_cast<uint32_t*>(cm + row * kStripCols + c0 + col) = amax_m == 0.0f ? 0u
+    *reinterpret_cast<uint32_t*>(cm + row * kStripCols + c0 + col) = rm == 0.0f ? 0u
         : encode4<FMT_I8, false>(__fmul_rn(m1[j].x, rm), __fmul_rn(m1[j].y, rm), __fmul_rn(m1[j].z, rm), __fmul_rn(m1[j].w, rm));
-    *reinterpret_cast<uint32_t*>(cv + row * kStripCols + c0 + col) = amax_v == 0.0f ? 0u
+    *reinterpret_cast<uint32_t*>(cv + row * kStripCols + c0 + col) = rv == 0.0f ? 0u
         : encode4<FMT_U8, false>(__fmul_rn(v1[j].x, rv), __fmul_rn(v1[j].y, rv), __fmul_rn(v1[j].z, rv), __fmul_rn(v1[j].w, rv));
   }
 }

@@ -254,6 +254,23 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Scale and reciprocal of a quantisation block with absmax amax (>= 0, or
+// NaN) for code range Q. A finite, positive amax gives scale = fl32(amax / Q)
+// and r = min(fl32(Q / amax), FLT_MAX); amax 0 gives scale 1. A block holding
+// a NaN (amax NaN: the max over |x| bits lets a NaN win) or an infinity (amax
+// +inf) cannot be scaled: scale is a quiet NaN 0x7FC00000 or +inf. Every
+// block that is not finite and positive gets r = 0, which marks codes that
+// are all 0x00; such a block dequantises to NaN (0 x NaN, 0 x inf).
+__device__ __forceinline__ void block_scale(float amax, float Q, float& scale, float& r) {
+  if (amax > 0.0f && amax <= FLT_MAX) {
+    scale = __fdiv_rn(amax, Q);
+    r = fminf(__fdiv_rn(Q, amax), FLT_MAX);
+  } else {
+    scale = amax == 0.0f ? 1.0f : (amax != amax ? __uint_as_float(0x7fc00000u) : amax);
+    r = 0.0f;
+  }
+}
+
 // Square root rounded to nearest even, for x in [kSqrtShortMin, FLT_MAX]:
 // gfx950's v_sqrt_f32 estimate s is within one ulp of the root there, and
 // the rounded root is s or one of its neighbours sd, su, chosen by the signs

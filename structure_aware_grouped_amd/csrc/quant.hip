@@ -81,9 +81,10 @@ __device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ 
       }
     }
     const float amax = __uint_as_float(group_max<NT>(m, tid, red));
-    const bool zero = amax == 0.0f;
-    const float r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
-    if (tid == 0) scales[sidx] = zero ? 1.0f : __fdiv_rn(amax, Q);
+    float sc, r;
+    block_scale(amax, Q, sc, r);
+    const bool blank = r == 0.0f;   // a zero or non-finite block: every code 0x00
+    if (tid == 0) scales[sidx] = sc;
     GridWalk w(tid, vpr, NT);
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
@@ -94,7 +95,7 @@ __device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ 
         uint32_t words[VE / 4];
 #pragma unroll
         for (int h = 0; h < VE / 4; ++h) {
-          words[h] = zero ? 0u
+          words[h] = blank ? 0u
                           : encode4<FMT, HW>(__fmul_rn(x[4 * h], r), __fmul_rn(x[4 * h + 1], r),
                                              __fmul_rn(x[4 * h + 2], r), __fmul_rn(x[4 * h + 3], r));
         }
@@ -117,13 +118,14 @@ __device__ void quant_block(const void* __restrict__ src, uint8_t* __restrict__ 
     m = max(m, __float_as_uint(I::elem(src, base + rr * stride + cc)) & 0x7fffffffu);
   }
   const float amax = __uint_as_float(group_max<NT>(m, tid, red));
-  const bool zero = amax == 0.0f;
-  const float r = zero ? 0.0f : fminf(__fdiv_rn(Q, amax), FLT_MAX);
-  if (tid == 0) scales[sidx] = zero ? 1.0f : __fdiv_rn(amax, Q);
+  float sc, r;
+  block_scale(amax, Q, sc, r);
+  const bool blank = r == 0.0f;
+  if (tid == 0) scales[sidx] = sc;
   for (int64_t i = tid; i < total; i += NT) {
     const int64_t rr = i / cols, cc = i - rr * cols;
     const int64_t e = base + rr * stride + cc;
-    q[e] = zero ? 0 : static_cast<uint8_t>(encode1<FMT, HW>(__fmul_rn(I::elem(src, e), r)));
+    q[e] = blank ? 0 : static_cast<uint8_t>(encode1<FMT, HW>(__fmul_rn(I::elem(src, e), r)));
   }
 }
 

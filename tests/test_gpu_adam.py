@@ -145,6 +145,41 @@ def test_chained_steps_on_each_tile_register_path(gpu_lib, paths, max_grid, monk
     plan.close()
 
 
+def test_nan_gradients_blank_their_blocks(gpu_lib):
+    """NaN gradients in flat blocks, 32x32 strips and a ragged 32x32 tensor: two chained steps
+    against the oracle. Codes and scales bit for bit (a blanked block's scale is 0x7FC00000);
+    parameters bit for bit where finite and NaN where the oracle's are NaN."""
+    import structure_aware_grouped_amd as rs
+    specs = [TensorSpec("s", 64, 256, "TILE", 32, 32), TensorSpec("r", 40, 45, "TILE", 32, 32),
+             TensorSpec("f", 1, 5000, "FLAT", 2048)]
+    V = 2
+    S, starts, _, _ = rs.rs_plan_build(specs, V)
+    plan = rs.rs_plan_load(specs, V, S, starts, V, 0)
+    rng = np.random.default_rng(77)
+    total = V * S
+    param = rng.standard_normal(total).astype(np.float32)
+    m = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+    v = ((rng.standard_normal(total) * 1e-3) ** 2).astype(np.float32)
+    qm, sm = OT.block_quant(m, specs, starts, S, V, "i8")
+    qv, sv = OT.block_quant(v, specs, starts, S, V, "u8")
+    for step, h in enumerate(HYPERS[:2]):
+        grad = (rng.standard_normal(total) * 1e-3).astype(np.float32)
+        if step == 0:
+            for i, e in ((0, 5), (0, 300 * 1 + 70), (1, 1000), (2, 4100)):
+                grad[int(starts[i]) + e] = np.nan
+        with np.errstate(invalid="ignore"):
+            want = OA.adam8_step(param, grad, qm, sm, qv, sv, specs, starts, h)
+        got = _run(rs, plan, (param, grad, qm, sm, qv.astype(np.uint8), sv), h)
+        gp = got[0].cpu().numpy()
+        nan = np.isnan(want[0])
+        assert nan.any() and np.array_equal(np.isnan(gp), nan), step
+        assert np.array_equal(gp[~nan].view(np.uint32), want[0][~nan].view(np.uint32)), step
+        for g, wv, name in zip(got[1:], want[1:], ("q_m", "s_m", "q_v", "s_v")):
+            assert np.array_equal(tensor_bits(g), np.asarray(wv).view(tensor_bits(g).dtype)), (name, step)
+        param, qm, sm, qv, sv = want
+    plan.close()
+
+
 def test_zero_state_and_gradient_blocks(gpu_lib):
     import structure_aware_grouped_amd as rs
     specs = [TensorSpec("f", 1, 4096, "FLAT", 1024)]

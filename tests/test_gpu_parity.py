@@ -386,7 +386,10 @@ def test_e4m3_encoder_every_mantissa(gpu_lib, encoder, monkeypatch):
 
 @pytest.mark.parametrize("fmt,encoder", [("e4m3", "sw"), ("e4m3", "hw"), ("i8", "sw"), ("u8", "sw")])
 def test_special_blocks(gpu_lib, fmt, encoder, monkeypatch):
-    """All-zero, subnormal-amax, constant, single-outlier and signed-zero blocks."""
+    """All-zero, subnormal-amax, constant, single-outlier and signed-zero blocks, and blocks that
+    hold a NaN (quiet, signalling, negative) or an infinity: codes and scales bit for bit; the
+    dequantised values bit for bit, NaN where the oracle has NaN (a NaN's sign and payload carry
+    no meaning: 0 x inf gives the platform's default NaN)."""
     import structure_aware_grouped_amd as rs
     monkeypatch.setenv("RS_E4M3_ENCODER", encoder)
     b = 256
@@ -399,6 +402,13 @@ def test_special_blocks(gpu_lib, fmt, encoder, monkeypatch):
         (np.random.default_rng(1).standard_normal(b) * 1e-30).astype(np.float32),
         np.float32(np.random.default_rng(2).standard_normal(b) * 1e30),
     ]
+    for k, bad in enumerate([0x7FC00000, 0x7F800001, 0xFFC00000, 0x7F800000, 0xFF800000]):
+        x = np.random.default_rng(10 + k).standard_normal(b).astype(np.float32)
+        x[(37 * k) % b] = np.uint32(bad).view(np.float32)
+        blocks.append(x)
+    x = np.random.default_rng(20).standard_normal(b).astype(np.float32)   # a NaN and an infinity
+    x[5], x[200] = np.inf, np.nan
+    blocks.append(x)
     data = np.concatenate(blocks)
     if fmt == "u8":
         data = np.abs(data)
@@ -412,7 +422,15 @@ def test_special_blocks(gpu_lib, fmt, encoder, monkeypatch):
     assert np.array_equal(tensor_bits(sc), ws.view(np.uint32))
     out = torch.empty(data.size, dtype=torch.float32, device=DEV)
     rs.rs_block_dequant(plan, q, fmt, sc, out)
-    assert np.array_equal(tensor_bits(out), OT.block_dequant(wq, ws, spec, [0], data.size, 1, fmt).view(np.uint32))
+    want = OT.block_dequant(wq, ws, spec, [0], data.size, 1, fmt)
+    got = out.cpu().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 6 * b
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    full = torch.empty(1, data.size, dtype=torch.float32, device=DEV)      # the gather side
+    rs.rs_unpack_dequant(plan, q, fmt, sc, [full])
+    got = full.cpu().numpy().ravel()
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
     plan.close()
 
 
