@@ -117,6 +117,22 @@ def test_random_group_lists(exe, seed):
     assert _run(exe, specs, V, R) == "ok"
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_groups_of_32x32_tiles(exe, seed):
+    # the pages' 8-bit Adam blocks: whole strips or not, by width and band; the coverage check and
+    # the strip-launch check (against the tensor shapes) run on every one
+    rng = random.Random(7000 + seed)
+    specs = []
+    for i in range(rng.randint(1, 5)):
+        rows = 32 * rng.randint(1, 6) - (rng.choice([0, 0, 0, 7]))
+        cols = rng.choice([128, 256, 384, 96, 160, 32 * rng.randint(1, 12)])
+        specs.append(TensorSpec(f"t{i}", rows, cols, "TILE", 32, 32))
+    if rng.random() < 0.5:
+        specs.append(TensorSpec("norm", 300, 1, rng.choice(["ROWS", "FLAT"]), rng.choice([1, 2048])))
+    V = rng.choice([1, 2, 3, 8])
+    assert _run(exe, specs, V) == "ok"
+
+
 def test_gather_runs_and_strips_of_a_mid_size_group(exe):
     specs = [TensorSpec("a", 1024, 2048, "TILE", 128, 128), TensorSpec("b", 300, 1000, "TILE", 64, 64),
              TensorSpec("c", 300001, 1, "FLAT", 2048), TensorSpec("d", 256, 512, "TILEMAJOR", 32, 32),
