@@ -166,6 +166,18 @@ def test_param_and_grad_workloads(gpu_lib, idx, tile_major):
     pads = OP.padding_ranges(specs, plan.starts, S, R)
     _zero_everywhere(packed, pads)
     print(f"  unpack and pack match on tensors {sample}; padding zero", flush=True)
+    if not tile_major:
+        # every tensor, on the device: unpack is a copy of the tensor's slice of the gathered buffer,
+        # and pack equals fl32(prev + fl32(g * sigma)) from torch's elementwise fp32 multiply and add
+        sig = torch.tensor(sigma, dtype=torch.float32, device=DEV)
+        for i in range(len(specs)):
+            s, n = int(plan.starts[i]), int(plan.numels[i])
+            assert torch.equal(params[i].reshape(-1).view(torch.int16 if params[i].element_size() == 2 else torch.int32),
+                               G[s: s + n].view(torch.int16 if G.element_size() == 2 else torch.int32)), f"unpack {i}"
+            y = torch.mul(grads[i].reshape(-1), sig)
+            want = torch.add(prev[s: s + n], y)
+            assert torch.equal(packed[s: s + n].view(torch.int32), want.view(torch.int32)), f"pack {i}"
+        print(f"  unpack and pack of all {len(specs)} tensors match their slices and torch's fp32 ops", flush=True)
     if idx == 1 and not tile_major:
         # the same pack into a bf16 buffer (bf16 ReduceScatter): each fp32 result rounded once
         del packed
