@@ -228,6 +228,9 @@ int rs_pack_scatter(rs_plan* plan, const void* const* src, int32_t src_dt,
  * block of a FLAT tensor):
  *   amax = max |x| over B;  Q = 448 (RS_E4M3), 127 (RS_I8), 255 (RS_U8);
  *   amax == 0: scale[B] = 1.0 and every code is 0;
+ *   amax NaN (a NaN in B; NaN wins the max) or +inf (an infinity in B):
+ *   scale[B] = quiet NaN 0x7FC00000 or +inf and every code is 0, so the
+ *   block dequantises to NaN everywhere (the pages assume finite values);
  *   otherwise scale[B] = fl32(amax / Q), r = min(fl32(Q / amax), FLT_MAX),
  *   code = enc(fl32(x * r)), enc being round-to-nearest-even with saturation
  *   (E4M3: to +-448, sign kept, -0 -> 0x80; I8: to [-127,127]; U8: [0,255]).
