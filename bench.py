@@ -549,7 +549,7 @@ def main():
         ms = flushed_launches(own_copy, args.steps)
         med = float(np.median(ms))
         tms = flushed_launches(lambda: dst_c.copy_(src_c), 5)
-        copy = {"kernel": "rs_bench_copy: 16-byte nontemporal loads and stores, 64-thread workgroups of 1 KiB",
+        copy = {"kernel": "rs_bench_copy: 16-byte nontemporal loads, nt-sc1 buffer stores, 64-thread workgroups of 1 KiB",
                 "size": (f"{nb / 2**20:.0f} MiB copied: the {dominant} kernel's bytes" if args.copy_mib < 0
                          else f"{nb / 2**20:.0f} MiB copied"),
                 "bytes": 2 * nb, "median_ms": round(med, 5), "GBps": round(2 * nb / (med * 1e-3) / 1e9, 1),

@@ -3,8 +3,9 @@
  * (librs_bench.so). Neither is a step of the layout transform.
  *
  * rs_bench_copy: a plain streaming copy of known traffic on gfx950, built the
- * way the transform kernels stream (16-byte nontemporal vectors, small
- * short-lived workgroups). The benchmark times it as the practical HBM
+ * way the transform kernels stream (16-byte vectors, nontemporal loads,
+ * stores with nt and sc1 set, small short-lived workgroups). The benchmark
+ * times it as the practical HBM
  * ceiling next to the 8 TB/s peak, and its counter readings calibrate the HBM
  * byte counters (it reads and writes exactly `bytes`).
  *

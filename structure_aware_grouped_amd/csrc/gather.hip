@@ -75,7 +75,8 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
 // again split pieces further on while the run lasts. A run of several rows
 // holds at most kGatherMaxPieces * kGatherPiece * 8 = 65536 elements, fewer
 // than 2^16 vectors, so its row and tile-column indices come from div_u16; a
-// one-row run needs no division.
+// one-row run needs no division. Nontemporal stores: nt-sc1 ones ran 1-7%
+// slower here.
 template <int FMT, bool HW, bool BF16OUT>
 __device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const GatherChunk* __restrict__ chunks,
                                                                     const uint8_t* __restrict__ q,
@@ -200,7 +201,8 @@ __global__ __launch_bounds__(kFlatThreads) void gather_flat_kernel(const QJob* _
 // Gather side of a tile-major tensor, over the same strips: each lane turns
 // VEC codes of one tile row into one 16-byte store of the row-major tensor
 // (8 codes -> 8 bf16, 4 -> 4 fp32), kGatherTmVec vectors per thread; tile t
-// of the strip uses scale scale0 + t.
+// of the strip uses scale scale0 + t. Stores with nt and sc1 set: 2-3% faster
+// cold than nontemporal ones.
 template <int FMT, bool HW, bool BF16OUT>
 __device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* __restrict__ jobs,
                                                                   const uint8_t* __restrict__ q,
@@ -259,11 +261,11 @@ __device__ __forceinline__ void gather_tm_kernel_piece(unsigned b, const TmJob* 
           v[4 * h + 3] = __fmul_rn(d.w, sc[u]);
         }
         if constexpr (BF16OUT) {
-          stg(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + dpos[u]),
+          sts<kStoreNtSc1>(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + dpos[u]),
               u32x4{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
                     bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)});
         } else {
-          stg(reinterpret_cast<f32x4*>(static_cast<float*>(out) + dpos[u]), f32x4{v[0], v[1], v[2], v[3]});
+          sts<kStoreNtSc1>(reinterpret_cast<f32x4*>(static_cast<float*>(out) + dpos[u]), f32x4{v[0], v[1], v[2], v[3]});
         }
       }
     }

@@ -1,9 +1,12 @@
 // rs_bench_copy: a 16-byte streaming copy for gfx950, the practical HBM
 // ceiling next to which the layout kernels are measured. Each 64-thread
-// workgroup moves 1 KiB (one nontemporal 16-byte load and store per lane)
-// and exits, which keeps many independent streams in flight across the HBM
-// channels, as the unpack and pack kernels do. Launches use at most 2^24
-// workgroups; beyond that each workgroup loops.
+// workgroup moves 1 KiB (one 16-byte load and store per lane) and exits,
+// which keeps many independent streams in flight across the HBM channels, as
+// the unpack and pack kernels do. Loads are nontemporal; stores are buffer
+// stores with nt and sc1 set (cache-policy immediate 18), the fastest store
+// measured for a cold streamed copy on gfx950: 6.70 TB/s against 6.62 with
+// nontemporal global stores. Launches use at most 2^24 workgroups; beyond
+// that each workgroup loops.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -21,7 +24,11 @@ __global__ __launch_bounds__(kThreads) void copy16_kernel(const u32x4* __restric
                                                            int64_t nvec) {
   for (int64_t b = blockIdx.x; b * kThreads < nvec; b += gridDim.x) {
     const int64_t i = b * kThreads + threadIdx.x;
-    if (i < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    // the workgroup's 1 KiB of dst is the buffer; lane t writes 16 bytes at 16t
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(dst + b * kThreads, 0, -1, 0x00020000);
+    if (i < nvec)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_nontemporal_load(src + i), r,
+                                             static_cast<int>(threadIdx.x) * 16, 0, 18);
   }
 }
 

@@ -18,6 +18,8 @@ namespace {
 // ------------------------------------------------------------------ unpack
 
 // Workgroup b copies piece b % split (kUnpackPiece vectors) of chunk b / split.
+// Stores with nt and sc1 set: 3% faster cold than nontemporal ones (8B and
+// MoE layers), the same warm.
 __device__ __forceinline__ void unpack_kernel_piece(unsigned b, const CopyChunk* __restrict__ chunks,
                                                                const uint8_t* __restrict__ gathered,
                                                                void* const* __restrict__ dst, int eb,
@@ -39,7 +41,7 @@ __device__ __forceinline__ void unpack_kernel_piece(unsigned b, const CopyChunk*
     if (v0 + u * kUnpackThreads < nvec) r[u] = ldg(s4 + v0 + u * kUnpackThreads);
 #pragma unroll
   for (int u = 0; u < kUnpackVec; ++u)
-    if (v0 + u * kUnpackThreads < nvec) stg(d4 + v0 + u * kUnpackThreads, r[u]);
+    if (v0 + u * kUnpackThreads < nvec) sts<kStoreNtSc1>(d4 + v0 + u * kUnpackThreads, r[u]);
   const int tail = nbytes & 15;
   if (piece == 0 && static_cast<int>(threadIdx.x) < tail) d[(nvec << 4) + threadIdx.x] = s[(nvec << 4) + threadIdx.x];
 }
@@ -75,14 +77,16 @@ __device__ __forceinline__ float load1(const void* p, int64_t e) {
 
 // Four (or one) packed values at element `pos` of the packed buffer: fp32, or,
 // for a bf16 buffer (OB), each fp32 result rounded once to the nearest bf16
-// (ties to even).
+// (ties to even). Stores with nt and sc1 set: 2-3% faster cold than
+// nontemporal ones for every pack measured (fp32, with and without
+// accumulation; row-major and tile-major).
 template <bool OB>
 __device__ __forceinline__ void store_packed4(void* out, int64_t pos, const f32x4& y) {
   if constexpr (OB)
-    stg(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + pos),
+    sts<kStoreNtSc1>(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + pos),
         u32x2{bf16_rne(y.x) | (bf16_rne(y.y) << 16), bf16_rne(y.z) | (bf16_rne(y.w) << 16)});
   else
-    stg(reinterpret_cast<f32x4*>(static_cast<float*>(out) + pos), y);
+    sts<kStoreNtSc1>(reinterpret_cast<f32x4*>(static_cast<float*>(out) + pos), y);
 }
 
 template <bool OB>
@@ -212,7 +216,7 @@ __device__ __forceinline__ void unpack_tm_kernel_job(unsigned jb, unsigned n_job
     const int wv = width / VE, total2 = h * wv;
     for (int v = tid; v < total2; v += kTmLdsThreads) {
       const int r = v / wv, w = v - r * wv;
-      stg(reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(r) * j.cols + w * VE) * EB),
+      sts<kStoreNtSc1>(reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(r) * j.cols + w * VE) * EB),
           *reinterpret_cast<const u32x4*>(stage + (r * width + w * VE) * EB));
     }
     return;
@@ -331,7 +335,7 @@ __device__ __forceinline__ void unpack_tm_direct_kernel_piece(unsigned b, const 
       const uint32_t col = (static_cast<uint32_t>(v) - r * wv) * VE;
       const uint32_t t = div_u16(col, bc, mbc), c = col - t * bc;
       const u32x4 x = ldg(reinterpret_cast<const u32x4*>(src + (static_cast<int64_t>(t) * j.tile_elems + r * bc + c) * EB));
-      stg(reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(r) * j.cols + col) * EB), x);
+      sts<kStoreNtSc1>(reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(r) * j.cols + col) * EB), x);
     }
     return;
   }
