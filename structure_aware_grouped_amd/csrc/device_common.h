@@ -49,6 +49,18 @@ __device__ __forceinline__ void stg(T* p, T v) {
   else *p = v;
 }
 
+// stg for a pointer read from a table: the compiler cannot tell that it
+// addresses global memory and would issue a flat store, which also counts
+// against the LDS/scalar-load counter; the cast makes it a global store.
+// Every buffer the library writes is device memory.
+template <typename T>
+__device__ __forceinline__ void stg_global(T* p, T v) {
+  typedef __attribute__((address_space(1))) T* GT;
+  const GT g = (GT)p;
+  if constexpr (kNT) __builtin_nontemporal_store(v, g);
+  else *g = v;
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -91,7 +103,7 @@ __device__ __forceinline__ void sts(T* p, T v) {
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, o, 0, SC);
       }
     } else {
-      stg(p, v);
+      stg_global(p, v);
     }
   }
 }

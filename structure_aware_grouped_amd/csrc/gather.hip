@@ -45,11 +45,11 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
         if constexpr (BF16OUT) {
           const u32x4 o{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
                         bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)};
-          stg(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + dbase + off[u]), o);
+          stg_global(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + dbase + off[u]), o);
         } else {
           f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(dst) + dbase + off[u]);
-          stg(o, f32x4{v[0], v[1], v[2], v[3]});
-          stg(o + 1, f32x4{v[4], v[5], v[6], v[7]});
+          stg_global(o, f32x4{v[0], v[1], v[2], v[3]});
+          stg_global(o + 1, f32x4{v[4], v[5], v[6], v[7]});
         }
       }
     }
@@ -75,8 +75,9 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
 // again split pieces further on while the run lasts. A run of several rows
 // holds at most kGatherMaxPieces * kGatherPiece * 8 = 65536 elements, fewer
 // than 2^16 vectors, so its row and tile-column indices come from div_u16; a
-// one-row run needs no division. Nontemporal stores: nt-sc1 ones ran 1-7%
-// slower here.
+// one-row run needs no division. Nontemporal global stores: nt-sc1 ones ran
+// 1-7% slower here, and the flat stores that the table's pointer gave before
+// the cast 2-5% slower (8B layer, cold).
 template <int FMT, bool HW, bool BF16OUT>
 __device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const GatherChunk* __restrict__ chunks,
                                                                     const uint8_t* __restrict__ q,
@@ -135,11 +136,11 @@ __device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const Gathe
         v[4 * h + 3] = __fmul_rn(d.w, sc[u]);
       }
       if constexpr (BF16OUT) {
-        stg(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e),
+        stg_global(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e),
             u32x4{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
                   bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)});
       } else {
-        stg(reinterpret_cast<f32x4*>(static_cast<float*>(out) + e), f32x4{v[0], v[1], v[2], v[3]});
+        stg_global(reinterpret_cast<f32x4*>(static_cast<float*>(out) + e), f32x4{v[0], v[1], v[2], v[3]});
       }
     }
   }
