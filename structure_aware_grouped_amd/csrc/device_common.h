@@ -74,6 +74,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStoreNT = 0;
 constexpr int kStoreNtSc1 = 18;
 
+// Store of a 4-, 8- or 16-byte value at byte offset off from base with cache
+// policy SC, as a buffer store. The caller guarantees that base is the same
+// in every lane of the wave and that 0 <= off < 2^31. Where a kernel has such
+// a base (a block's or a run's start) this is the cheaper form: no per-store
+// vote.
+template <int SC, typename T>
+__device__ __forceinline__ void sts_at(const void* base, int off, T v) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu)));
+  const uint64_t a0 = (static_cast<uint64_t>(hi) << 32) | lo;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a0), 0, -1, 0x00020000);
+  if constexpr (sizeof(T) == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, SC);
+  } else if constexpr (sizeof(T) == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, SC);
+  } else {
+    static_assert(sizeof(T) == 4, "4-, 8- or 16-byte stores");
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, SC);
+  }
+}
+
 // Store of a 4-, 8- or 16-byte value with cache policy SC. A buffer store
 // addresses base + 32-bit offset, with the base the same in every lane: here
 // the first active lane's address. When some active lane's address is below
