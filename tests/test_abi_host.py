@@ -31,12 +31,12 @@ def _declared():
 
 
 def test_bench_helper_library_exports_its_declared_calls(rs):
-    """librs_bench.so (the benchmark's streaming-copy ceiling and the square-root self-check)
-    exports what rs_bench.h declares; bad arguments are refused before any launch."""
+    """librs_bench.so (the benchmark's streaming-copy ceiling, the square-root and store
+    self-checks) exports what rs_bench.h declares; bad arguments are refused before any launch."""
     import ctypes
     text = open(os.path.join(ROOT, "include", "rs_bench.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(rs_\w+)\s*\(", text, re.M)))
-    assert names == ["rs_bench_copy", "rs_bench_sqrt_check"]
+    assert names == ["rs_bench_copy", "rs_bench_sqrt_check", "rs_bench_store_check"]
     path = os.path.join(ROOT, "structure_aware_grouped_amd", "librs_bench.so")
     assert os.path.exists(path), "librs_bench.so is not built: run __graft_entry__.build()"
     lib = ctypes.CDLL(path)
@@ -50,6 +50,12 @@ def test_bench_helper_library_exports_its_declared_calls(rs):
     assert lib.rs_bench_sqrt_check(2, 1, ctypes.byref(n), ctypes.byref(f)) == -1   # empty range
     assert lib.rs_bench_sqrt_check(1, 2, None, ctypes.byref(f)) == -1             # null result
     assert (n.value, f.value) == (7, 7)                                           # untouched
+    lib.rs_bench_store_check.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    assert lib.rs_bench_store_check(None, 128, 0, None) == -1                      # null
+    assert lib.rs_bench_store_check(a, 100, 0, None) == -1                         # not a multiple of 128
+    assert lib.rs_bench_store_check(a, 128, 4, None) == -1                         # no such mode
+    assert lib.rs_bench_store_check(ctypes.c_void_p((1 << 20) + 8), 128, 0, None) == -1   # not 16-byte aligned
+    assert lib.rs_bench_store_check(a, (1 << 30) + 128, 0, None) == -1             # too many vectors
 
 
 def test_library_exports_every_declared_call(rs):
