@@ -1,11 +1,12 @@
 // Device-side building blocks shared by the kernel files of the RaggedShard /
-// DBuffer layout library (gfx950): vector types, nontemporal loads and
-// stores, the 8-bit code formats, wavefront reductions, the division-free
+// DBuffer layout library (gfx950): vector types, nontemporal loads, the
+// stores and their cache policies, the 8-bit code formats, wavefront reductions, the division-free
 // index walks and the XCD-aware renumbering of work items. Everything here is
 // in an anonymous namespace: each kernel file gets its own copy.
 //
 // Every kernel is HBM-bound streaming work over plan-indexed work lists made
-// once by rs_plan_load, with 16-byte nontemporal vector loads and stores. The
+// once by rs_plan_load, with 16-byte vector loads (nontemporal) and stores
+// (nontemporal, or with nt and sc1 set where that measured faster). The
 // streaming transforms split each work item over small, short-lived
 // workgroups (64-128 threads, one or two vectors each), which keep more
 // independent streams in flight on gfx950 than one large workgroup per item;
