@@ -257,7 +257,11 @@ struct GatherChunk {
 // [kGatherMinPieces, kGatherMaxPieces], that launches the fewest workgroups:
 // on the MoE layer (2880-wide rows, 128-row bands) 16-row runs of exactly 45
 // pieces ran the gather at 6.28 TB/s, against 5.79 for runs of about 16K codes.
-constexpr int64_t kGatherMinPieces = 8;
+// Runs of at least 48 pieces (P from 48 instead of 8) were faster again, in
+// eight interleaved pairs: the MoE layer 6.59 -> 6.68 TB/s (22-row runs), the
+// 8B layer 5.86 -> 5.94 (14-row runs, 4-row runs of the 14336-wide tensor,
+// 56 pieces each, where P from 8 gave 28-piece runs).
+constexpr int64_t kGatherMinPieces = 48;
 constexpr int64_t kGatherMaxPieces = 64;
 constexpr int64_t kGatherMaxCols = 16384;           // widest TILE tensor handled as row runs
 // Gather runs are split like unpack items: kGatherThreads * kGatherVec vectors per workgroup.

@@ -149,11 +149,13 @@ def test_planted_mistakes_are_reported(exe, plant):
 
 
 def test_gather_runs_fill_their_workgroups(exe):
-    # MoE-shaped experts (2880-wide rows, 128-row bands): 16-row runs of exactly 45 pieces of 1024 codes
+    # MoE-shaped experts (2880-wide rows, 128-row bands), runs of 48 to 64 pieces of 1024 codes:
+    # the fewest workgroups come from 22-row runs (63,360 codes, 62 pieces), five per band and
+    # one of the band's last 18 rows (the last 64-row band of `down`: 22 + 22 + 20)
     specs = []
     for e in range(4):
         specs += [TensorSpec(f"e{e}.gate_up", 5760, 2880, "TILE", 128, 128),
                   TensorSpec(f"e{e}.down", 2880, 2880, "TILE", 128, 128)]
     runs, split8, split4 = _gather_shape(exe, specs, 8)
-    assert (split8, split4) == (45, 90)
-    assert runs == 4 * (5760 // 16 + (22 * 128 // 16 + 64 // 16))
+    assert (split8, split4) == (62, 124)
+    assert runs == 4 * (5760 // 128 * 6 + (2880 // 128 * 6 + 3))
