@@ -1,8 +1,9 @@
 // Device-side building blocks shared by the kernel files of the RaggedShard /
 // DBuffer layout library (gfx950): vector types, nontemporal loads, the
-// stores and their cache policies, the 8-bit code formats, wavefront reductions, the division-free
-// index walks and the XCD-aware renumbering of work items. Everything here is
-// in an anonymous namespace: each kernel file gets its own copy.
+// stores and their cache policies, the 8-bit code formats, wavefront
+// reductions, the division-free index walks and the XCD-aware renumbering of
+// work items. Everything here is in an anonymous namespace: each kernel file
+// gets its own copy.
 //
 // Every kernel is HBM-bound streaming work over plan-indexed work lists made
 // once by rs_plan_load, with 16-byte vector loads (nontemporal) and stores
@@ -75,6 +76,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStoreNT = 0;
 constexpr int kStoreNtSc1 = 18;
 
+// Word 3 of a raw (byte-addressed, stride 0) buffer descriptor on gfx9-family
+// parts: data format 32 bits, no swizzle. The range is 2^32 - 1 bytes; every
+// caller keeps its offsets under 2^31.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// The first active lane's value of a 64-bit address, in scalar registers.
+// readfirstlane is int -> int: each half is widened through uint32_t, so a
+// low word with bit 31 set does not spill into the high word.
+__device__ __forceinline__ uint64_t first_lane(uint64_t a) {
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu)));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Store of a 4-, 8- or 16-byte value at byte offset off from base with cache
 // policy SC, as a buffer store. The caller guarantees that base is the same
 // in every lane of the wave and that 0 <= off < 2^31. Where a kernel has such
@@ -82,11 +97,8 @@ constexpr int kStoreNtSc1 = 18;
 // vote.
 template <int SC, typename T>
 __device__ __forceinline__ void sts_at(const void* base, int off, T v) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu)));
-  const uint64_t a0 = (static_cast<uint64_t>(hi) << 32) | lo;
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a0), 0, -1, 0x00020000);
+  const uint64_t a0 = first_lane(reinterpret_cast<uint64_t>(base));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a0), 0, -1, kRawBufferWord3);
   if constexpr (sizeof(T) == 16) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, SC);
   } else if constexpr (sizeof(T) == 8) {
@@ -107,27 +119,13 @@ __device__ __forceinline__ void sts(T* p, T v) {
   if constexpr (SC == 0) {
     stg(p, v);
   } else {
-    // readfirstlane is int -> int: each half is widened through uint32_t,
-    // so a low word with bit 31 set does not spill into the high word.
     const uint64_t a = reinterpret_cast<uint64_t>(p);
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu)));
-    const uint64_t a0 = (static_cast<uint64_t>(hi) << 32) | lo;
+    const uint64_t a0 = first_lane(a);
     const uint64_t off = a - a0;
-    if (__all(off < 0x80000000ull)) {
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a0), 0, -1, 0x00020000);
-      const int o = static_cast<int>(off);
-      if constexpr (sizeof(T) == 16) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, o, 0, SC);
-      } else if constexpr (sizeof(T) == 8) {
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, o, 0, SC);
-      } else {
-        static_assert(sizeof(T) == 4, "4-, 8- or 16-byte stores");
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, o, 0, SC);
-      }
-    } else {
+    if (__all(off < 0x80000000ull))
+      sts_at<SC>(reinterpret_cast<const void*>(a0), static_cast<int>(off), v);
+    else
       stg_global(p, v);
-    }
   }
 }
 

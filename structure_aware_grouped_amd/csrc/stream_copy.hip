@@ -24,7 +24,8 @@ __global__ __launch_bounds__(kThreads) void copy16_kernel(const u32x4* __restric
                                                            int64_t nvec) {
   for (int64_t b = blockIdx.x; b * kThreads < nvec; b += gridDim.x) {
     const int64_t i = b * kThreads + threadIdx.x;
-    // the workgroup's 1 KiB of dst is the buffer; lane t writes 16 bytes at 16t
+    // the workgroup's 1 KiB of dst is the buffer (a raw descriptor: word 3
+    // 0x00020000, 32-bit data format); lane t writes 16 bytes at 16t
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(dst + b * kThreads, 0, -1, 0x00020000);
     if (i < nvec)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_nontemporal_load(src + i), r,
