@@ -71,23 +71,23 @@ __device__ void gather_block(const uint8_t* __restrict__ q, void* __restrict__ d
 // Contiguous row runs of a quantised tensor (see GatherChunk). Each lane turns
 // VEC codes into one 16-byte store (8 codes -> 8 bf16, 4 codes -> 4 fp32), so
 // the lanes of a wave read and write one contiguous range each. Workgroup b
-// takes piece b % split of run b / split: kGatherVec vectors per thread, and
-// again split pieces further on while the run lasts. A run of several rows
-// holds at most kGatherMaxPieces * kGatherPiece * 8 = 65536 elements, fewer
-// than 2^16 vectors, so its row and tile-column indices come from div_u16; a
-// one-row run needs no division. Stores have nt and sc1 set and are addressed
+// takes piece b % split of run b / split: U vectors per thread (the plan's
+// gather_vec, 2 or 4), and again split pieces further on while the run lasts.
+// A run of several rows holds at most kGatherMaxRun elements, fewer than 2^16
+// vectors, so its row and tile-column indices come from div_u16; a one-row
+// run needs no division. Stores have nt and sc1 set and are addressed
 // from the run's start (sts_at, when the run spans under 2 GiB of the tensor,
 // as every run of a TILE tensor does; otherwise nontemporal global stores):
 // 1-2% faster cold than nontemporal global stores, where the per-lane-address
 // form (sts) was 1-7% slower and the flat stores that the table's pointer
 // gave before a global cast 2-5% slower.
-template <int FMT, bool HW, bool BF16OUT>
+template <int FMT, bool HW, bool BF16OUT, int U>
 __device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const GatherChunk* __restrict__ chunks,
                                                                     const uint8_t* __restrict__ q,
                                                                     const float* __restrict__ scales,
                                                                     void* const* __restrict__ dst, int split) {
   constexpr int VEC = BF16OUT ? 8 : 4;
-  constexpr int U = kGatherVec;
+  constexpr int kPiece = static_cast<int>(gather_piece(U));
   const unsigned cu = b / static_cast<unsigned>(split);
   const int ci = static_cast<int>(cu);
   const int piece = static_cast<int>(b - cu * static_cast<unsigned>(split));
@@ -101,8 +101,8 @@ __device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const Gathe
   const uint32_t mv = magic_u16(vpr);
   const uint32_t cpt = band ? static_cast<uint32_t>(c.bc / VEC) : 1u;   // vectors per tile column
   const uint32_t mc = magic_u16(cpt);
-  const int pass = split * static_cast<int>(kGatherPiece);
-  for (int i0 = piece * static_cast<int>(kGatherPiece) + static_cast<int>(threadIdx.x); i0 < nvec; i0 += pass) {
+  const int pass = split * kPiece;
+  for (int i0 = piece * kPiece + static_cast<int>(threadIdx.x); i0 < nvec; i0 += pass) {
     uint32_t code[U][VEC / 4];
     float sc[U];
 #pragma unroll
@@ -158,13 +158,13 @@ __device__ __forceinline__ void gather_rows_kernel_piece(unsigned b, const Gathe
   }
 }
 
-template <int FMT, bool HW, bool BF16OUT>
+template <int FMT, bool HW, bool BF16OUT, int U>
 __global__ __launch_bounds__(kGatherThreads) void gather_rows_kernel(const GatherChunk* __restrict__ chunks,
                                                                     const uint8_t* __restrict__ q,
                                                                     const float* __restrict__ scales,
                                                                     void* const* __restrict__ dst, int split, unsigned n_pieces) {
   for (unsigned p = blockIdx.x; p < n_pieces; p += gridDim.x)
-    gather_rows_kernel_piece<FMT, HW, BF16OUT>(piece_index<kGatherXcdGroup>(p, n_pieces), chunks, q, scales, dst, split);
+    gather_rows_kernel_piece<FMT, HW, BF16OUT, U>(piece_index<kGatherXcdGroup>(p, n_pieces), chunks, q, scales, dst, split);
 }
 
 template <int FMT, bool HW, bool BF16OUT>
@@ -330,8 +330,12 @@ void launch_gather(const rs_plan* p, const uint8_t* q, const float* scales, hipS
   if (p->n_gchunks) {
     const int64_t split = BF16OUT ? p->gather_split8 : p->gather_split4;
     const int64_t n = p->n_gchunks * split;
-    hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT>), grid_of(p, n), dim3(kGatherThreads), 0, s, p->gchunks, q,
-                       scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));
+    if (p->gather_vec == kGatherVecShort)
+      hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT, kGatherVecShort>), grid_of(p, n), dim3(kGatherThreads), 0,
+                         s, p->gchunks, q, scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));
+    else
+      hipLaunchKernelGGL((gather_rows_kernel<FMT, HW, BF16OUT, kGatherVecLong>), grid_of(p, n), dim3(kGatherThreads), 0,
+                         s, p->gchunks, q, scales, p->gdst.dev, static_cast<int>(split), static_cast<unsigned>(n));
   }
   if (p->n_gtile)
     hipLaunchKernelGGL((gather_tile_kernel<FMT, HW, BF16OUT>), grid_of(p, p->n_gtile), block, 0, s, tiles, q, scales,

@@ -36,6 +36,7 @@ struct Tables {
   int32_t max_tile_vec16 = 0;
   bool split_code_lines = false;
   bool adam_all_strips = false;
+  int gather_vec = kGatherVecLong;
   int64_t gather_split8 = 0, gather_split4 = 0;
 };
 
@@ -184,8 +185,21 @@ void lower(const std::vector<Tensor>& t, int64_t S, int64_t R_mat, Tables* tb) {
   for (const QJob& j : tb->qjobs)
     if (j.kind == QJOB_TILE && !tile_vec[j.tensor] && t[j.tensor].kind != RS_TILEMAJOR)
       tb->gjobs.push_back(j);   // TILEMAJOR tensors use the tile-major strips
-  // one run length for the plan (8-code pieces: kGatherPiece vectors of 8 codes)
-  const int64_t pc8 = kGatherPiece * 8;
+  // vectors per thread, from the length of the launch (rs_internal.h) unless
+  // RS_GATHER_VEC=2|4 forces it; then one run length for the plan (8-code
+  // pieces: gather_piece(vec) vectors of 8 codes)
+  int64_t run_elems = 0;
+  for (int64_t ti = 0; ti < n; ++ti) {
+    const Tensor& x = t[ti];
+    if (x.kind == RS_TILE && tile_vec[ti]) run_elems += x.n;
+    else if (x.kind == RS_FLAT && x.p0 % 16 == 0) run_elems += (x.n / x.p0) * x.p0;
+  }
+  tb->gather_vec = run_elems < kGatherShortElems ? kGatherVecShort : kGatherVecLong;
+  if (const char* gv = std::getenv("RS_GATHER_VEC")) {
+    const int f = std::atoi(gv);
+    if (f == kGatherVecShort || f == kGatherVecLong) tb->gather_vec = f;
+  }
+  const int64_t pc8 = gather_piece(tb->gather_vec) * 8;
   std::vector<RunGroups> groups(n, RunGroups{0, 0, 0, 0});
   std::vector<RunGroups> used;
   for (int64_t ti = 0; ti < n; ++ti) {
@@ -548,6 +562,7 @@ extern "C" int rs_plan_load(const rs_tensor_spec* specs, int64_t n, int64_t V, i
     p->max_tile_vec16 = tb.max_tile_vec16;
     p->split_code_lines = tb.split_code_lines;
     p->adam_all_strips = tb.adam_all_strips;
+    p->gather_vec = tb.gather_vec;
     p->gather_split8 = tb.gather_split8;
     p->gather_split4 = tb.gather_split4;
     // gfx950's FP8 conversion (OCP E4M3, round to nearest even) by default;

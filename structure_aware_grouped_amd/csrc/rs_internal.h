@@ -250,10 +250,10 @@ struct GatherChunk {
   int32_t unused;
 };
 
-// A gather run is split over `split` workgroups of kGatherPiece vectors, the
+// A gather run is split over `split` workgroups of gather_piece(vec) vectors, the
 // same number for every run of a launch, so a run shorter than the longest
 // leaves workgroups idle. The lowering therefore picks one target length for
-// the whole plan, P pieces of kGatherPiece * 8 codes with P in
+// the whole plan, P pieces of gather_piece(vec) * 8 codes with P in
 // [kGatherMinPieces, kGatherMaxPieces], that launches the fewest workgroups:
 // on the MoE layer (2880-wide rows, 128-row bands) 16-row runs of exactly 45
 // pieces ran the gather at 6.28 TB/s, against 5.79 for runs of about 16K codes.
@@ -264,15 +264,22 @@ struct GatherChunk {
 constexpr int64_t kGatherMinPieces = 48;
 constexpr int64_t kGatherMaxPieces = 64;
 constexpr int64_t kGatherMaxCols = 16384;           // widest TILE tensor handled as row runs
-// Gather runs are split like unpack items: kGatherThreads * kGatherVec vectors per workgroup.
+// Gather runs are split like unpack items: kGatherThreads threads of `vec`
+// vectors each per workgroup, vec chosen per plan. A short launch (a row-run
+// gather of fewer than kGatherShortElems elements, a few hundred µs) takes 4
+// vectors per thread, half the workgroups; a longer one 2. Measured cold,
+// three interleaved rounds: 4 against 2 vectors gave +2.3% on 0.2G elements
+// of 2880-wide rows and +1-5% on 0.18G of 4096-wide rows (and +3-7% on the
+// 8B layer's 0.22G), the same on 0.8G of 2880-wide rows, -2% on 2.8G of
+// 4096-wide rows and -8% on the MoE layer's 3.2G: what decides is the
+// length of the launch, not the row width. RS_GATHER_VEC=2|4 forces one.
 #ifndef RS_GATHER_THREADS
 #define RS_GATHER_THREADS 64
 #endif
-#ifndef RS_GATHER_VEC
-#define RS_GATHER_VEC 2
-#endif
-constexpr int kGatherThreads = RS_GATHER_THREADS, kGatherVec = RS_GATHER_VEC;
-constexpr int64_t kGatherPiece = int64_t(kGatherThreads) * kGatherVec;
+constexpr int kGatherThreads = RS_GATHER_THREADS;
+constexpr int kGatherVecShort = 4, kGatherVecLong = 2;
+constexpr int64_t kGatherShortElems = int64_t(1) << 29;
+constexpr int64_t gather_piece(int vec) { return int64_t(kGatherThreads) * vec; }   // vectors per workgroup
 // The gather side of tile-major strips keeps 4 vectors per thread: against 2,
 // 5.38-5.42 -> 5.62-5.64 TB/s cold on the 8B layer stored tile-major (row runs
 // keep 2: 4 cost the MoE layer's runs 9%).
@@ -281,9 +288,11 @@ constexpr int64_t kGatherPiece = int64_t(kGatherThreads) * kGatherVec;
 #endif
 constexpr int kGatherTmVec = RS_GATHER_TM_VEC;
 constexpr int64_t kGatherTmPiece = int64_t(kGatherThreads) * kGatherTmVec;
-// the longest run: kGatherMaxPieces pieces of 8-code vectors, or one row of
-// kGatherMaxCols codes; as 4-code vectors its indices stay under 2^16
-constexpr int64_t kGatherMaxRun = std::max<int64_t>(kGatherMaxPieces * kGatherPiece * 8, kGatherMaxCols);
+// the longest run: kGatherMaxPieces pieces of 8-code vectors (of the larger
+// piece), or one row of kGatherMaxCols codes; as 4-code vectors its indices
+// stay under 2^16
+constexpr int64_t kGatherMaxRun =
+    std::max<int64_t>(kGatherMaxPieces * gather_piece(kGatherVecShort) * 8, kGatherMaxCols);
 static_assert(kGatherMaxRun / 4 < 65536, "a run of several rows keeps its vector indices under 2^16");
 
 
@@ -345,6 +354,7 @@ struct rs_plan {
   int64_t n_qblocks = 0;
   int32_t max_tile_vec16 = 0;  // largest tile (TILE or TILEMAJOR), in 16-byte vectors of 4-byte input
   bool split_code_lines = false;  // neighbouring tiles share 128-byte lines of codes
+  int gather_vec = rs::kGatherVecLong;   // vectors per thread of the row-run gather
   int64_t gather_split8 = 0;      // workgroups per gather run, 8 codes per vector (bf16 out)
   int64_t gather_split4 = 0;      // the same, 4 codes per vector (fp32 out)
 

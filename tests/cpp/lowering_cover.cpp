@@ -6,7 +6,9 @@
 // Reads "n V S R_mat" and n lines "rows cols kind p0 p1 start" on stdin;
 // prints "ok" or the first violation. With an argument 1-4 it first plants
 // one mistake in the lists (a pack chunk dropped, a quant job doubled, a
-// gather scale shifted, an unpack source shifted), which must be reported. This file includes plan.cpp so that it
+// gather scale shifted, an unpack source shifted), which must be reported.
+// With the argument "shape" it only lowers the plan and prints the gather
+// side's shape (for plans too large to check element by element). This file includes plan.cpp so that it
 // can call validate_plan() and the file-local lower(); link it with planner.cpp.
 #include "plan.cpp"
 
@@ -44,7 +46,7 @@ int64_t scale_of(const Tensor& x, int64_t first, int64_t e) {
   return first + (R / x.p0) * ntc + C / x.p1;
 }
 
-int64_t g_split8 = 0, g_split4 = 0, g_runs = 0;
+int64_t g_split8 = 0, g_split4 = 0, g_runs = 0, g_vec = 0;
 bool g_strips = false;
 
 // The Adam step's whole-strip launch, decided from the tensors rather than
@@ -68,6 +70,7 @@ bool check(const std::vector<Tensor>& t, int64_t S, int64_t R, int plant) {
   g_split8 = tb.gather_split8;
   g_split4 = tb.gather_split4;
   g_runs = static_cast<int64_t>(tb.gchunks.size());
+  g_vec = tb.gather_vec;
   g_strips = tb.adam_all_strips;
   CHECK(tb.adam_all_strips == strips_from_tensors(t), "Adam strip launch %d, from the tensors %d",
         int(tb.adam_all_strips), int(strips_from_tensors(t)));
@@ -201,8 +204,8 @@ bool check(const std::vector<Tensor>& t, int64_t S, int64_t R, int plant) {
   reset();
   for (const GatherChunk& c : tb.gchunks) {
     const Tensor& x = t[c.tensor];
-    CHECK(ceil_div(int64_t(c.rows) * c.cols, kGatherPiece * 8) <= tb.gather_split8 &&
-              ceil_div(int64_t(c.rows) * c.cols, kGatherPiece * 4) <= tb.gather_split4,
+    CHECK(ceil_div(int64_t(c.rows) * c.cols, gather_piece(tb.gather_vec) * 8) <= tb.gather_split8 &&
+              ceil_div(int64_t(c.rows) * c.cols, gather_piece(tb.gather_vec) * 4) <= tb.gather_split4,
           "gather run of %lld codes longer than the split", (long long)c.rows * c.cols);
     CHECK(c.qbase == x.start + c.toff && c.cols % 8 == 0, "gather run of tensor %d", c.tensor);
     for (int64_t r = 0; r < c.rows; ++r)
@@ -237,7 +240,8 @@ bool check(const std::vector<Tensor>& t, int64_t S, int64_t R, int plant) {
 }  // namespace
 
 int main(int argc, char** argv) {
-  const int plant = argc > 1 ? std::atoi(argv[1]) : 0;
+  const bool shape_only = argc > 1 && std::strcmp(argv[1], "shape") == 0;
+  const int plant = argc > 1 && !shape_only ? std::atoi(argv[1]) : 0;
   long long n, V, S, R;
   if (std::scanf("%lld %lld %lld %lld", &n, &V, &S, &R) != 4 || n < 1) return 2;
   std::vector<rs_tensor_spec> specs(n);
@@ -259,13 +263,20 @@ int main(int argc, char** argv) {
     std::printf("invalid plan: %s\n", rs_last_error());
     return 0;
   }
+  if (shape_only) {
+    Tables tb;
+    lower(t, S, R, &tb);
+    std::printf("ok\ngather runs %lld split8 %lld split4 %lld vec %d\n", (long long)tb.gchunks.size(),
+                (long long)tb.gather_split8, (long long)tb.gather_split4, tb.gather_vec);
+    return 0;
+  }
   if (!check(t, S, R, plant)) {
     std::printf("FAIL %s\n", fail_msg.c_str());
     return 0;
   }
   std::printf("ok\n");
-  std::printf("gather runs %lld split8 %lld split4 %lld\n", (long long)g_runs, (long long)g_split8,
-              (long long)g_split4);
+  std::printf("gather runs %lld split8 %lld split4 %lld vec %lld\n", (long long)g_runs, (long long)g_split8,
+              (long long)g_split4, (long long)g_vec);
   std::printf("adam strips %d\n", int(g_strips));
   return 0;
 }

@@ -289,6 +289,21 @@ def test_launches_that_loop_over_work_items(gpu_lib, tm_kernel, monkeypatch):
     _full_check(rs, TILE_MAJOR, 3, torch.float32, 79)
 
 
+@pytest.mark.parametrize("max_grid", [None, "24"])
+@pytest.mark.parametrize("vec", ["2", "4"])
+@pytest.mark.parametrize("pdtype", [torch.float32, torch.bfloat16])
+def test_row_run_gather_at_both_vector_counts(gpu_lib, vec, pdtype, max_grid, monkeypatch):
+    """The row-run gather with 2 and 4 vectors per thread (RS_GATHER_VEC forces the count; a
+    plan takes 4 below 2^29 row-run elements, so every small group here would take 4), on the
+    ragged and mid-size groups, with and without launches that loop over their runs."""
+    import structure_aware_grouped_amd as rs
+    monkeypatch.setenv("RS_GATHER_VEC", vec)
+    if max_grid:
+        monkeypatch.setenv("RS_MAX_GRID", max_grid)
+    _full_check(rs, RAGGED, 6, pdtype, 41)
+    _full_check(rs, MID, 7, pdtype, 42)
+
+
 def test_trailing_padding_ranks(gpu_lib):
     """R_mat > R_used: ranks holding only padding come out zero."""
     import structure_aware_grouped_amd as rs

@@ -48,15 +48,22 @@ def _run(exe, specs, V, R=None, plant=0):
     return r.stdout.strip().split("\n")[0]
 
 
-def _gather_shape(exe, specs, V):
+def _gather_shape(exe, specs, V, vec=None, shape_only=False):
+    """(runs, split8, split4, vectors per thread) of the gather side; vec forces the vector
+    count through RS_GATHER_VEC; shape_only skips the element-by-element check."""
     ref = OP.plan(specs, V)
     lines = [f"{len(specs)} {V} {ref.S} {V}"] + [f"{s.rows} {s.cols} {KINDS[s.kind]} {s.p0} {s.p1} {int(st)}"
                                                  for s, st in zip(specs, ref.starts)]
-    r = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, timeout=600)
+    env = dict(os.environ)
+    env.pop("RS_GATHER_VEC", None)
+    if vec is not None:
+        env["RS_GATHER_VEC"] = str(vec)
+    r = subprocess.run([exe] + (["shape"] if shape_only else []), input="\n".join(lines) + "\n",
+                       capture_output=True, text=True, timeout=600, env=env)
     out = r.stdout.split("\n")
     assert out[0] == "ok", r.stdout
     w = out[1].split()
-    return int(w[2]), int(w[4]), int(w[6])
+    return int(w[2]), int(w[4]), int(w[6]), int(w[8])
 
 
 def _adam_strips(exe, specs, V):
@@ -149,13 +156,30 @@ def test_planted_mistakes_are_reported(exe, plant):
 
 
 def test_gather_runs_fill_their_workgroups(exe):
-    # MoE-shaped experts (2880-wide rows, 128-row bands), runs of 48 to 64 pieces of 1024 codes:
-    # the fewest workgroups come from 22-row runs (63,360 codes, 62 pieces), five per band and
-    # one of the band's last 18 rows (the last 64-row band of `down`: 22 + 22 + 20)
+    # MoE-shaped experts (2880-wide rows, 128-row bands) with 2 vectors per thread (the long-launch
+    # choice, forced), runs of 48 to 64 pieces of 1024 codes: the fewest workgroups come from 22-row
+    # runs (63,360 codes, 62 pieces), five per band and one of the band's last 18 rows (the last
+    # 64-row band of `down`: 22 + 22 + 20)
     specs = []
     for e in range(4):
         specs += [TensorSpec(f"e{e}.gate_up", 5760, 2880, "TILE", 128, 128),
                   TensorSpec(f"e{e}.down", 2880, 2880, "TILE", 128, 128)]
-    runs, split8, split4 = _gather_shape(exe, specs, 8)
-    assert (split8, split4) == (62, 124)
+    runs, split8, split4, vec = _gather_shape(exe, specs, 8, vec=2)
+    assert (split8, split4, vec) == (62, 124, 2)
     assert runs == 4 * (5760 // 128 * 6 + (2880 // 128 * 6 + 3))
+    # 4 vectors per thread (pieces of 2048 codes): 43-row runs (123,840 codes, 61 pieces), three per
+    # band (43 + 43 + 42; the last 64-row band of `down`: 43 + 21)
+    runs, split8, split4, vec = _gather_shape(exe, specs, 8, vec=4)
+    assert (split8, split4, vec) == (61, 121, 4)
+    assert runs == 4 * (5760 // 128 * 3 + (2880 // 128 * 3 + 2))
+
+
+def test_gather_vectors_per_thread_follow_the_launch_length(exe):
+    # fewer than 2^29 elements in row runs: 4 vectors per thread; from 2^29 on: 2
+    small = [TensorSpec(f"t{i}", 14336, 1024, "TILE", 128, 128) for i in range(4)]
+    large = [TensorSpec(f"t{i}", 14336, 1024, "TILE", 128, 128) for i in range(37)]   # 543M elements
+    assert sum(s.rows * s.cols for s in large) >= 1 << 29 > sum(s.rows * s.cols for s in large[:36])
+    assert _gather_shape(exe, small, 8)[3] == 4
+    assert _gather_shape(exe, large, 64, shape_only=True)[3] == 2
+    assert _gather_shape(exe, large[:36], 64, shape_only=True)[3] == 4
+    assert _gather_shape(exe, small, 8, vec=2)[3] == 2
