@@ -280,11 +280,13 @@ constexpr int kGatherThreads = RS_GATHER_THREADS;
 constexpr int kGatherVecShort = 4, kGatherVecLong = 2;
 constexpr int64_t kGatherShortElems = int64_t(1) << 29;
 constexpr int64_t gather_piece(int vec) { return int64_t(kGatherThreads) * vec; }   // vectors per workgroup
-// The gather side of tile-major strips keeps 4 vectors per thread: against 2,
-// 5.38-5.42 -> 5.62-5.64 TB/s cold on the 8B layer stored tile-major (row runs
-// keep 2: 4 cost the MoE layer's runs 9%).
+// The gather side of tile-major strips takes 8 vectors per thread: on the 8B
+// layer stored tile-major, cold, 4 against 2 gave 5.38-5.42 -> 5.62-5.64 TB/s
+// and, with nt-sc1 stores, 8 against 4 5.74-5.79 -> 5.85-6.05 in three
+// interleaved rounds (warm 2-3% slower). With 128x128 tiles a bf16 strip is
+// 256 vectors, one workgroup either way; an fp32 strip takes one instead of two.
 #ifndef RS_GATHER_TM_VEC
-#define RS_GATHER_TM_VEC 4
+#define RS_GATHER_TM_VEC 8
 #endif
 constexpr int kGatherTmVec = RS_GATHER_TM_VEC;
 constexpr int64_t kGatherTmPiece = int64_t(kGatherThreads) * kGatherTmVec;
